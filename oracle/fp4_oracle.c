@@ -1,0 +1,479 @@
+/*
+ * fp4_oracle.c -- scalar CPU oracle.  TEST INFRASTRUCTURE ONLY (see the
+ * header for who may load it and for the page tags used in citations).
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -fopenmp -ffp-contract=off
+ *        -fno-fast-math fp4_oracle.c -o libfp4_oracle.so -lm
+ */
+#include "fp4_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------
+ * Element grids.
+ * E2M1: sign, 2 exponent bits, 1 mantissa bit; magnitudes 0, .5, 1, 1.5, 2,
+ * 3, 4, 6 ([UFP4] "Declaracion del Problema" and Metodologia 1 name E2M1;
+ * [TJ2] Riepilogo 1 has 0 and 0.5 as neighbouring bins; [MXFP4] 2.A gives
+ * the FP4 limit 6.0).  Uniform grid: equal spacing l_i = r_i ([UFP4]
+ * Metodologia 2, "Rejilla Uniforme"), read as the integers 0..7 times the
+ * block scale (E1M2 with bias 1 is k/4; the factor 4 lives in the scale).
+ * ---------------------------------------------------------------------- */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+static const double kUniform[8] = {0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0};
+
+static const double* grid_levels(int grid) {
+  return grid == FP4R_GRID_UNIFORM ? kUniform : kE2M1;
+}
+
+float fp4r_level(int grid, int k) { return (float)grid_levels(grid)[k & 7]; }
+
+/* ------------------------------------------------------------------------
+ * Philox4x32-10 (Salmon et al., SC'11).  One round maps counter c under key
+ * k: the two 32x32 -> 64-bit products M0*c0 and M1*c2 are split into high
+ * and low words, and the new counter is
+ *   (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0));
+ * the key is bumped by the Weyl constants between rounds.
+ * ---------------------------------------------------------------------- */
+#define PHILOX_M0 0xD2511F53u
+#define PHILOX_M1 0xCD9E8D57u
+#define PHILOX_W0 0x9E3779B9u
+#define PHILOX_W1 0xBB67AE85u
+
+void fp4r_philox4x32_10(uint32_t k0, uint32_t k1, const uint32_t ctr[4],
+                        uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += PHILOX_W0;
+      k1 += PHILOX_W1;
+    }
+    uint64_t p0 = (uint64_t)PHILOX_M0 * (uint64_t)c0;
+    uint64_t p1 = (uint64_t)PHILOX_M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+uint16_t fp4r_rht_signs(uint64_t seed) {
+  uint32_t ctr[4] = {0u, 0u, 1u, 0u};
+  uint32_t out[4];
+  fp4r_philox4x32_10((uint32_t)seed, (uint32_t)(seed >> 32), ctr, out);
+  return (uint16_t)(out[0] & 0xFFFFu);
+}
+
+/* Draw for logical element n: one Philox call per 8 consecutive elements,
+ * counter (g_lo, g_hi, 0, 0) with g = n / 8; element l = n % 8 takes the
+ * 16-bit half (l % 2) of word (l / 2). */
+uint32_t fp4r_sr_u16(uint64_t seed, uint64_t n) {
+  uint64_t g = n >> 3;
+  unsigned l = (unsigned)(n & 7u);
+  uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
+  uint32_t out[4];
+  fp4r_philox4x32_10((uint32_t)seed, (uint32_t)(seed >> 32), ctr, out);
+  return (out[l >> 1] >> (16u * (l & 1u))) & 0xFFFFu;
+}
+
+/* ------------------------------------------------------------------------
+ * Random Hadamard transform on one group of 16 ([UFP4] Metodologia 1-2 and
+ * "Eficiencia"; [TJ2] 2.C): a random +-1 diagonal D followed by the
+ * Sylvester-ordered Hadamard matrix, scaled by 1/4 so that it is orthogonal.
+ * The butterfly runs the stages h = 1, 2, 4, 8; at each stage every pair
+ * (j, j+h) with j & h == 0 becomes (t_j + t_{j+h}, t_j - t_{j+h}).
+ * ---------------------------------------------------------------------- */
+static void fwht16(float t[16]) {
+  for (int h = 1; h < 16; h <<= 1) {
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      float u = t[j], v = t[j + h];
+      t[j] = u + v;
+      t[j + h] = u - v;
+    }
+  }
+}
+
+void fp4r_rht16(const float in[16], uint16_t signs, int inverse,
+                float out[16]) {
+  float t[16];
+  if (!inverse) {
+    for (int j = 0; j < 16; ++j) t[j] = ((signs >> j) & 1u) ? -in[j] : in[j];
+    fwht16(t);
+    for (int j = 0; j < 16; ++j) out[j] = t[j] * 0.25f;
+  } else {
+    for (int j = 0; j < 16; ++j) t[j] = in[j];
+    fwht16(t);
+    for (int j = 0; j < 16; ++j) {
+      float s = t[j] * 0.25f;
+      out[j] = ((signs >> j) & 1u) ? -s : s;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * E4M3 scale byte (NVFP4's 8-bit block scale, [TJ2] 2.A; named E4M3 in
+ * [MXFP4] 2): bias 7, 3 mantissa bits, subnormal step 2^-9, largest finite
+ * 448 (byte 0x7E; 0x7F is NaN).  Values are listed by byte, which orders
+ * them by magnitude; encoding picks the nearest, ties to the even byte.
+ * ---------------------------------------------------------------------- */
+static double e4m3_value_def(unsigned b) {
+  unsigned e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0) return ldexp((double)m, -9);
+  return ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+}
+
+/* The 127 non-negative finite values, filled from the definition above
+ * when the library is loaded. */
+static double kE4M3[127];
+
+__attribute__((constructor)) static void e4m3_table_init(void) {
+  for (unsigned b = 0; b < 127u; ++b) kE4M3[b] = e4m3_value_def(b);
+}
+
+float fp4r_e4m3_decode(uint8_t b) {
+  if ((b & 0x7Fu) == 0x7Fu) return NAN;
+  double v = kE4M3[b & 0x7Fu];
+  return (float)((b & 0x80u) ? -v : v);
+}
+
+uint8_t fp4r_e4m3_encode(float r) {
+  double x = (double)r;
+  if (x >= 448.0) return 0x7E; /* saturating: 448 is the largest finite */
+  if (!(x > 0.0)) return 0x00; /* zero (and negative zero) */
+  unsigned c = 0;
+  while (c + 1 <= 0x7Eu && kE4M3[c + 1] <= x) ++c;
+  double lo = kE4M3[c];
+  if (lo == x) return (uint8_t)c;
+  double hi = kE4M3[c + 1];
+  double dl = x - lo, dh = hi - x; /* both exact in binary64 */
+  if (dl < dh) return (uint8_t)c;
+  if (dh < dl) return (uint8_t)(c + 1);
+  return (uint8_t)((c & 1u) ? c + 1 : c);
+}
+
+/* ------------------------------------------------------------------------
+ * MX (E8M0) scale exponent ([MXFP4] 2: a power-of-two scale; 2.A: the
+ * block amax lands near the top of the E2M1 range and saturates at 6).
+ * e = floor(log2 amax) - 2, where 2 is E2M1's largest exponent.
+ * ---------------------------------------------------------------------- */
+int fp4r_e8m0_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int ex;
+  (void)frexp((double)amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+  int e = (ex - 1) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+/* ------------------------------------------------------------------------
+ * Rounding a magnitude m >= 0 to a grid.  k is the bin with
+ * L[k] <= m < L[k+1]; m >= L[7] saturates at 7 ([MXFP4] 2.A: saturation at
+ * the FP4 limit).  RTNE compares m with the exact midpoint, ties to the even
+ * code ([UFP4] Metodologia 1: RTNE bins).  SR rounds up with probability
+ * (m - L[k]) / (L[k+1] - L[k]) using a 16-bit draw ([TJ2] 2.A: stochastic
+ * rounding so that E[round(x)] = x; [UFP4] Metodologia 2: SR on dY).
+ * ---------------------------------------------------------------------- */
+static int bin_below(double m, const double* L) {
+  int k = 0;
+  while (k < 7 && L[k + 1] <= m) ++k;
+  return k;
+}
+
+int fp4r_round_rtne(float mf, int grid) {
+  const double* L = grid_levels(grid);
+  double m = (double)mf;
+  if (m >= L[7]) return 7;
+  int k = bin_below(m, L);
+  double mid = 0.5 * (L[k] + L[k + 1]);
+  if (m < mid) return k;
+  if (m > mid) return k + 1;
+  return (k & 1) ? k + 1 : k;
+}
+
+int fp4r_round_sr(float mf, int grid, uint32_t u16) {
+  const double* L = grid_levels(grid);
+  double m = (double)mf;
+  if (m >= L[7]) return 7;
+  int k = bin_below(m, L);
+  double p = (m - L[k]) / (L[k + 1] - L[k]);
+  return ((double)(u16 & 0xFFFFu) < p * 65536.0) ? k + 1 : k;
+}
+
+/* ------------------------------------------------------------------------
+ * Tensor helpers.
+ * ---------------------------------------------------------------------- */
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+    return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+  uint32_t bias = 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)((u + bias) >> 16);
+}
+
+static float load_elem(const void* x, int dt, int64_t idx) {
+  if (dt == FP4R_BF16) return bf16_to_f32(((const uint16_t*)x)[idx]);
+  return ((const float*)x)[idx];
+}
+
+/* A[i][j] of the logical operand: x[i][j] for ROW, x[j][i] for COL. */
+static int64_t a_index(int axis, int64_t i, int64_t j, int64_t ld) {
+  return axis == FP4R_ROW ? i * ld + j : j * ld + i;
+}
+
+static int grid_of(int format) {
+  return format == FP4R_UFP4 ? FP4R_GRID_UNIFORM : FP4R_GRID_E2M1;
+}
+
+/* G, the largest grid level, used by the two-level tensor scale. */
+static float grid_max(int format) {
+  return format == FP4R_UFP4 ? 7.0f : 6.0f;
+}
+
+static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
+                        int64_t ld) {
+  if (!p) return -1;
+  if (p->format < 0 || p->format > 2) return -1;
+  if (p->format == FP4R_MXFP4 ? p->block != 32 : p->block != 16) return -1;
+  if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;
+  if (p->rounding != FP4R_RTNE && p->rounding != FP4R_SR) return -1;
+  if (rows < 0 || cols < 0 || ld < cols) return -1;
+  int64_t W = p->axis == FP4R_ROW ? cols : rows;
+  if (W % p->block) return -1;
+  if (p->rht && (W % 16)) return -1;
+  return 0;
+}
+
+/* One row of the logical operand, widened and (optionally) rotated. */
+static void load_row(const void* x, int dt, int axis, int64_t ld, int64_t i,
+                     int64_t W, int rht, uint16_t signs, float* y) {
+  for (int64_t j = 0; j < W; ++j) y[j] = load_elem(x, dt, a_index(axis, i, j, ld));
+  if (rht)
+    for (int64_t j = 0; j < W; j += 16) fp4r_rht16(y + j, signs, 0, y + j);
+}
+
+/* ------------------------------------------------------------------------
+ * Block scale and element quantization.
+ *
+ * NVFP4 / uniform grid (two-level scaling: FP32 tensor scale, E4M3 block
+ * scale per 16 elements; [TJ2] 2.A, [NGPT] "Enunciato del Problema" on
+ * per-tensor dynamic scaling):
+ *   s_t = amax_t / (G * 448);  r_b = amax_b / (s_t * G);  S_b = E4M3(r_b);
+ *   d_b = s_t * decode(S_b);  v = y * (1 / d_b).
+ * MXFP4 ([MXFP4] 2): d_b = 2^e with e = floor(log2 amax_b) - 2.
+ * A block whose scale decodes to zero codes every element as a signed zero.
+ * ---------------------------------------------------------------------- */
+static float block_decode_scale(const fp4r_params* p, uint8_t sbyte, float s_t) {
+  if (p->format == FP4R_MXFP4) return ldexpf(1.0f, (int)sbyte - 127);
+  if (sbyte == 0) return 0.0f;
+  return s_t * fp4r_e4m3_decode(sbyte);
+}
+
+static uint8_t block_scale_byte(const fp4r_params* p, float amax_b, float s_t) {
+  if (p->format == FP4R_MXFP4) return (uint8_t)(fp4r_e8m0_exponent(amax_b) + 127);
+  if (s_t == 0.0f || amax_b == 0.0f) return 0x00;
+  float den = s_t * grid_max(p->format);
+  float r = amax_b / den;
+  return fp4r_e4m3_encode(r);
+}
+
+void fp4r_quantize_block(const float* y, const fp4r_params* p,
+                         uint8_t scale_byte, float tensor_scale,
+                         int64_t row_a, int64_t col_a0, int64_t W,
+                         uint8_t* codes_out) {
+  int grid = grid_of(p->format);
+  float d = block_decode_scale(p, scale_byte, tensor_scale);
+  float inv = d != 0.0f ? 1.0f / d : 0.0f;
+  for (int i = 0; i < p->block; ++i) {
+    float yi = y[i];
+    unsigned s = signbit(yi) ? 1u : 0u;
+    int k = 0;
+    if (d != 0.0f && yi != 0.0f) {
+      float v = yi * inv;
+      float m = fabsf(v);
+      if (p->rounding == FP4R_SR) {
+        uint64_t n = (uint64_t)row_a * (uint64_t)W + (uint64_t)(col_a0 + i);
+        k = fp4r_round_sr(m, grid, fp4r_sr_u16(p->sr_seed, n));
+      } else {
+        k = fp4r_round_rtne(m, grid);
+      }
+    }
+    codes_out[i] = (uint8_t)((s << 3) | (unsigned)k);
+  }
+}
+
+int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
+                  int64_t ld, const fp4r_params* p, uint8_t* codes,
+                  uint8_t* scales, float* tensor_scale) {
+  if (check_params(p, rows, cols, ld)) return -1;
+  if (in_dtype != FP4R_BF16 && in_dtype != FP4R_F32) return -1;
+  const int axis = p->axis, B = p->block;
+  const int64_t RA = axis == FP4R_ROW ? rows : cols;
+  const int64_t W = axis == FP4R_ROW ? cols : rows;
+  const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
+  const int two_level = p->format != FP4R_MXFP4;
+
+  /* tensor scale: amax over the whole (rotated) operand */
+  float s_t = 0.0f;
+  if (two_level) {
+    if (!tensor_scale) return -1;
+    if (p->ts_mode == FP4R_TS_GIVEN) {
+      s_t = *tensor_scale;
+    } else {
+      float amax = 0.0f;
+#pragma omp parallel
+      {
+        float* y = (float*)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
+        float local = 0.0f;
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < RA; ++i) {
+          load_row(x, in_dtype, axis, ld, i, W, p->rht, signs, y);
+          for (int64_t j = 0; j < W; ++j)
+            if (fabsf(y[j]) > local) local = fabsf(y[j]);
+        }
+#pragma omp critical
+        if (local > amax) amax = local;
+        free(y);
+      }
+      s_t = amax / (grid_max(p->format) * 448.0f);
+      *tensor_scale = s_t;
+    }
+  }
+
+  const int64_t nblk = W / B;
+#pragma omp parallel
+  {
+    float* y = (float*)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
+    uint8_t kb[32];
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < RA; ++i) {
+      load_row(x, in_dtype, axis, ld, i, W, p->rht, signs, y);
+      for (int64_t b = 0; b < nblk; ++b) {
+        const float* yb = y + b * B;
+        float amax_b = 0.0f;
+        for (int e = 0; e < B; ++e)
+          if (fabsf(yb[e]) > amax_b) amax_b = fabsf(yb[e]);
+        uint8_t sbyte = block_scale_byte(p, amax_b, s_t);
+        scales[i * nblk + b] = sbyte;
+        fp4r_quantize_block(yb, p, sbyte, s_t, i, b * B, W, kb);
+        for (int e = 0; e < B; e += 2) {
+          int64_t c = b * B + e; /* even column: low nibble */
+          codes[i * (W / 2) + c / 2] = (uint8_t)(kb[e] | (kb[e + 1] << 4));
+        }
+      }
+    }
+    free(y);
+  }
+  return 0;
+}
+
+int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
+                    const float* tensor_scale, int64_t rows, int64_t cols,
+                    const fp4r_params* p, int inverse_rht, void* out,
+                    int out_dtype, int64_t ld_out) {
+  if (check_params(p, rows, cols, ld_out)) return -1;
+  if (out_dtype != FP4R_BF16 && out_dtype != FP4R_F32) return -1;
+  if (inverse_rht && !p->rht) return -1;
+  const int axis = p->axis, B = p->block, grid = grid_of(p->format);
+  const int64_t RA = axis == FP4R_ROW ? rows : cols;
+  const int64_t W = axis == FP4R_ROW ? cols : rows;
+  const int64_t nblk = W / B;
+  const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
+  float s_t = 0.0f;
+  if (p->format != FP4R_MXFP4) {
+    if (!tensor_scale) return -1;
+    s_t = *tensor_scale;
+  }
+#pragma omp parallel
+  {
+    float* v = (float*)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < RA; ++i) {
+      for (int64_t b = 0; b < nblk; ++b) {
+        float d = block_decode_scale(p, scales[i * nblk + b], s_t);
+        for (int e = 0; e < B; ++e) {
+          int64_t c = b * B + e;
+          uint8_t byte = codes[i * (W / 2) + c / 2];
+          unsigned code = (c & 1) ? (byte >> 4) : (byte & 15u);
+          float mag = fp4r_level(grid, (int)(code & 7u)) * d;
+          v[c] = (code & 8u) ? -mag : mag;
+        }
+      }
+      if (inverse_rht)
+        for (int64_t j = 0; j < W; j += 16) fp4r_rht16(v + j, signs, 1, v + j);
+      for (int64_t j = 0; j < W; ++j) {
+        int64_t o = a_index(axis, i, j, ld_out);
+        if (out_dtype == FP4R_F32) ((float*)out)[o] = v[j];
+        else ((uint16_t*)out)[o] = f32_to_bf16_rne(v[j]);
+      }
+    }
+    free(v);
+  }
+  return 0;
+}
+
+int fp4r_rht(const void* x, int in_dtype, int64_t rows, int64_t cols,
+             int64_t ld, int axis, uint64_t seed, int inverse, float* y) {
+  if (in_dtype != FP4R_BF16 && in_dtype != FP4R_F32) return -1;
+  if (axis != FP4R_ROW && axis != FP4R_COL) return -1;
+  if (rows < 0 || cols < 0 || ld < cols) return -1;
+  const int64_t RA = axis == FP4R_ROW ? rows : cols;
+  const int64_t W = axis == FP4R_ROW ? cols : rows;
+  if (W % 16) return -1;
+  const uint16_t signs = fp4r_rht_signs(seed);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < RA; ++i) {
+    for (int64_t j = 0; j < W; j += 16) {
+      float a[16], t[16];
+      for (int e = 0; e < 16; ++e) a[e] = load_elem(x, in_dtype, a_index(axis, i, j + e, ld));
+      fp4r_rht16(a, signs, inverse, t);
+      for (int e = 0; e < 16; ++e) y[a_index(axis, i, j + e, cols)] = t[e];
+    }
+  }
+  return 0;
+}
+
+/* ---- array forms ------------------------------------------------------- */
+void fp4r_e4m3_encode_n(const float* r, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = fp4r_e4m3_encode(r[i]);
+}
+
+void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
+                  const uint32_t* u16, uint8_t* k_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i)
+    k_out[i] = (uint8_t)(rounding == FP4R_SR ? fp4r_round_sr(m[i], grid, u16[i])
+                                             : fp4r_round_rtne(m[i], grid));
+}
+
+void fp4r_sr_u16_n(uint64_t seed, const uint64_t* idx, int64_t n,
+                   uint32_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = fp4r_sr_u16(seed, idx[i]);
+}
+
+int fp4r_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

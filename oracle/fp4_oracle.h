@@ -1,0 +1,139 @@
+/*
+ * fp4_oracle.h -- scalar CPU oracle for block-scaled 4-bit quantization with
+ * an optional 16-point random Hadamard transform (RHT).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no source,
+ * header, table or helper with the HIP library; the two meet only through
+ * the seeded input generators and the comparison in the tests.
+ *
+ * The oracle is deliberately plain: one element at a time, in the order the
+ * method is described, with linear scans instead of bit tricks.  Rows of the
+ * logical operand are independent, so an OpenMP "parallel for" over rows is
+ * the only concession to speed; it does not change any result.
+ *
+ * Pages cited (each is a summary of one paper):
+ *   [UFP4]  gist.science/es/paper/2606.20381, "Replanteamiento del Sesgo de
+ *           Contraccion en el Preentrenamiento de LLM en FP4"
+ *   [NGPT]  gist.science/it/paper/2605.06067, "Le Architetture Normalizzate
+ *           sono Nativamente a 4 Bit"
+ *   [TJ2]   gist.science/it/paper/2510.27527, "TetraJet-v2: Accurate NVFP4
+ *           Training for Large Language Models ..."
+ *   [MXFP4] gist.science/fr/paper/2603.08713, "Unveiling the Potential of
+ *           Quantization with MXFP4 ..."
+ *   [HIF]   gist.science/es/paper/2602.12635, "Unleashing Low-Bit Inference
+ *           on Ascend NPUs ..."
+ * Published definitions used where the pages name a thing without defining
+ * it: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+ * as easy as 1, 2, 3", SC'11); OCP FP8 E4M3 and OCP Microscaling (MX) v1.0
+ * for the E4M3 and E8M0 scale bytes; the Sylvester-ordered Hadamard matrix.
+ *
+ * Arithmetic model: every float operation that feeds a decision is an IEEE
+ * binary32 operation with round-to-nearest-even, in the order written
+ * (built with -ffp-contract=off, no fast-math, denormals kept).  Rounding
+ * decisions that are exact in binary64 are taken in binary64.
+ */
+#ifndef FP4_ORACLE_H
+#define FP4_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* enumerations (values mirror the product's C-ABI by convention only) */
+enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2 };
+enum { FP4R_ROW = 0, FP4R_COL = 1 };
+enum { FP4R_RTNE = 0, FP4R_SR = 1 };
+enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
+enum { FP4R_TS_COMPUTE = 0, FP4R_TS_GIVEN = 1 };
+enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1 };
+
+typedef struct {
+  int32_t format;   /* FP4R_NVFP4 / FP4R_MXFP4 / FP4R_UFP4 */
+  int32_t block;    /* 16 (NVFP4, UFP4) or 32 (MXFP4) */
+  int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
+  int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
+  int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */
+  int32_t ts_mode;  /* FP4R_TS_COMPUTE or FP4R_TS_GIVEN (NVFP4/UFP4) */
+  uint64_t rht_seed;
+  uint64_t sr_seed;
+} fp4r_params;
+
+/* ---- primitives -------------------------------------------------------- */
+
+/* Philox4x32-10 block function (SC'11): 10 rounds of the 4x32 Philox
+ * bijection of counter ctr under key (k0, k1). */
+void fp4r_philox4x32_10(uint32_t k0, uint32_t k1, const uint32_t ctr[4],
+                        uint32_t out[4]);
+
+/* The 16 RHT signs of a seed: low 16 bits of Philox(key = seed,
+ * counter = (0, 0, 1, 0)) word 0.  Bit j set means d_j = -1. */
+uint16_t fp4r_rht_signs(uint64_t seed);
+
+/* The 16-bit stochastic-rounding draw of logical element n = row*W + col. */
+uint32_t fp4r_sr_u16(uint64_t seed, uint64_t n);
+
+/* Forward: y = (1/4) H16 D a.  Inverse: a = D (1/4) H16 y.  Butterfly
+ * stages h = 1, 2, 4, 8 in binary32, then the exact scaling by 1/4. */
+void fp4r_rht16(const float in[16], uint16_t signs, int inverse, float out[16]);
+
+/* OCP E4M3 (FN: bias 7, max 448, no infinities), round to nearest even,
+ * saturating to 448 for r >= 448.  r must be >= 0. */
+uint8_t fp4r_e4m3_encode(float r);
+float fp4r_e4m3_decode(uint8_t b);
+
+/* MX scale exponent for a block amax: floor(log2 amax) - 2 clamped to
+ * [-127, 127]; amax == 0 gives -127. */
+int fp4r_e8m0_exponent(float amax);
+
+/* Magnitude code k (0..7) of m >= 0 on a grid, RTNE or SR with draw u16. */
+int fp4r_round_rtne(float m, int grid);
+int fp4r_round_sr(float m, int grid, uint32_t u16);
+float fp4r_level(int grid, int k);
+
+/* ---- tensor entry points (host pointers) ------------------------------- */
+
+/* Quantize x (rows x cols, leading dimension ld, BF16 bits or FP32).
+ * codes: rows_A * W / 2 bytes, scales: rows_A * W / block bytes, where the
+ * logical operand A is x (ROW) or x^T (COL) and W its row length.
+ * tensor_scale: written (COMPUTE) or read (GIVEN) for NVFP4/UFP4.
+ * Returns 0 on success, -1 on invalid arguments. */
+int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
+                  int64_t ld, const fp4r_params* p, uint8_t* codes,
+                  uint8_t* scales, float* tensor_scale);
+
+/* Dequantize back into x's layout (rows x cols, leading dimension ld_out),
+ * optionally undoing the RHT.  out_dtype FP4R_F32 or FP4R_BF16 (RNE). */
+int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
+                    const float* tensor_scale, int64_t rows, int64_t cols,
+                    const fp4r_params* p, int inverse_rht, void* out,
+                    int out_dtype, int64_t ld_out);
+
+/* Standalone RHT along the axis; y is rows x cols FP32, contiguous. */
+int fp4r_rht(const void* x, int in_dtype, int64_t rows, int64_t cols,
+             int64_t ld, int axis, uint64_t seed, int inverse, float* y);
+
+/* Quantize one block of already-transformed values y[0..block) with a
+ * given scale byte and tensor scale; element (row_a, col_a0 + i) of a
+ * logical operand with row length W supplies the SR draw.  codes_out gets
+ * one 4-bit code per byte.  Used by the tests' boundary rule. */
+void fp4r_quantize_block(const float* y, const fp4r_params* p,
+                         uint8_t scale_byte, float tensor_scale,
+                         int64_t row_a, int64_t col_a0, int64_t W,
+                         uint8_t* codes_out);
+
+/* ---- array forms of the primitives, for the tests' pins ---------------- */
+void fp4r_e4m3_encode_n(const float* r, int64_t n, uint8_t* out);
+void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
+                  const uint32_t* u16, uint8_t* k_out);
+void fp4r_sr_u16_n(uint64_t seed, const uint64_t* idx, int64_t n,
+                   uint32_t* out);
+int fp4r_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_ORACLE_H */

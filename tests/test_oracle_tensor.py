@@ -1,0 +1,294 @@
+"""Tensor-level pins for the oracle (CPU only).
+
+Closed-form worked examples of RHT + quantization, exact round trips of
+on-grid blocks, the transpose invariant, a brute-force quantizer for tiny
+tensors (argmin over candidate sets built from torch's E4M3 table), the
+nearest-level property, and the pages' directional claims.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+from scipy.linalg import hadamard
+
+import oracle
+import workloads
+
+H16 = hadamard(16).astype(np.float64)
+E2M1 = np.array(oracle.E2M1_LEVELS)
+UNI = np.array(oracle.UNIFORM_LEVELS)
+
+
+def _signs_vec(seed):
+    s = oracle.rht_signs(seed)
+    return np.array([-1.0 if (s >> j) & 1 else 1.0 for j in range(16)])
+
+
+# ---------------------------------------------------------------- worked examples
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4"])
+@pytest.mark.parametrize("k", [0, 5, 15])
+def test_single_spike_group_saturates_every_code(fmt, k):
+    """One nonzero a at index k of a 16-group: after the RHT every entry is
+    +-a/4, so the block amax is a/4, every code has the top magnitude, and the
+    signs follow column k of H16 times d_k.  With a/4 = G*448*2^j everything
+    is exact and dequantize + inverse RHT returns a e_k."""
+    seed = 3
+    G = 6 if fmt == "nvfp4" else 7
+    a = 4.0 * G * 448 * 2.0 ** -5
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, k] = a
+    codes, scales, ts = oracle.quantize(x, fmt, rht=True, rht_seed=seed)
+    assert ts == a / 4 / (G * 448)
+    assert scales[0, 0] == 0x7E
+    c = oracle.unpack_codes(codes)[0]
+    assert (c & 7 == 7).all()
+    sign = 0.25 * H16[:, k] * _signs_vec(seed)[k] < 0
+    assert np.array_equal((c >> 3).astype(bool), sign)
+    back = oracle.dequantize(codes, scales, ts, 1, 16, fmt, rht=True, rht_seed=seed,
+                             inverse_rht=True)
+    assert np.array_equal(back, x)
+
+
+@pytest.mark.parametrize("seed", [0, 4])
+def test_sign_matched_constant_group_concentrates(seed):
+    """x_j = c d_j: the RHT gives (4c, 0, ..., 0), one top code and fifteen
+    zero codes; with 4c = 6*448*2^j the round trip is exact."""
+    c = 6 * 448 * 2.0 ** -3 / 4
+    d = _signs_vec(seed)
+    x = (c * d).astype(np.float32)[None, :]
+    codes, scales, ts = oracle.quantize(x, "nvfp4", rht=True, rht_seed=seed)
+    cc = oracle.unpack_codes(codes)[0]
+    assert cc[0] == 7 and (cc[1:] == 0).all()
+    back = oracle.dequantize(codes, scales, ts, 1, 16, "nvfp4", rht=True, rht_seed=seed,
+                             inverse_rht=True)
+    assert np.array_equal(back, x)
+
+
+def test_tensor_scale_definition_and_top_block():
+    """s_t = amax / (6 * 448) in fp32; the block holding the tensor amax gets
+    the largest E4M3 scale (448)."""
+    x = workloads.small_case("normal", 64, 64, 1)
+    codes, scales, ts = oracle.quantize(x, "nvfp4")
+    amax = np.float32(np.abs(x).max())
+    assert ts == np.float32(amax / np.float32(2688.0))
+    r, c = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert scales[r, c // 16] == 0x7E
+
+
+# ------------------------------------------------------------------ round trips
+def test_on_grid_blocks_round_trip_exactly():
+    rng = np.random.default_rng(8)
+    e4 = np.arange(0x08, 0x7F)  # normal E4M3 bytes
+    for fmt, levels in (("nvfp4", E2M1), ("ufp4", UNI)):
+        G = levels[-1]
+        s_t = np.float32(2.0 ** -10)
+        rows = []
+        for _ in range(64):
+            S = int(rng.choice(e4))
+            d = np.float32(s_t * np.float32(oracle.e4m3_decode(S)))
+            k = rng.integers(0, 8, 16)
+            k[rng.integers(0, 16)] = 7  # the block amax is G * d
+            sgn = rng.choice([-1.0, 1.0], 16)
+            rows.append((sgn * levels[k] * np.float64(d)).astype(np.float32))
+        x = np.stack(rows)
+        codes, scales, ts = oracle.quantize(x, fmt, tensor_scale=float(s_t))
+        back = oracle.dequantize(codes, scales, ts, x.shape[0], 16, fmt)
+        assert np.array_equal(back, x), fmt
+    # MXFP4: d = 2^e and amax in [4 d, 8 d)
+    rows = []
+    for _ in range(64):
+        e = int(rng.integers(-100, 100))
+        k = rng.integers(0, 8, 32)
+        k[rng.integers(0, 32)] = 7
+        rows.append((rng.choice([-1.0, 1.0], 32) * E2M1[k] * 2.0 ** e).astype(np.float32))
+    x = np.stack(rows)
+    codes, scales, _ = oracle.quantize(x, "mxfp4")
+    assert np.array_equal(oracle.dequantize(codes, scales, None, 64, 32, "mxfp4"), x)
+
+
+# ------------------------------------------------------------ transpose invariant
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+@pytest.mark.parametrize("rht", [False, True])
+def test_col_equals_row_of_transpose(fmt, rounding, rht):
+    x = workloads.to_bf16_bits(workloads.small_case("t3", 96, 64, 2))
+    col = oracle.quantize(x, fmt, "col", rounding, rht, 5, 77)
+    row = oracle.quantize(np.ascontiguousarray(x.T), fmt, "row", rounding, rht, 5, 77)
+    assert np.array_equal(col[0], row[0]) and np.array_equal(col[1], row[1])
+    assert col[2] == row[2]
+    back_c = oracle.dequantize(*col, 96, 64, fmt, "col", rht, 5, inverse_rht=rht)
+    back_r = oracle.dequantize(*row, 64, 96, fmt, "row", rht, 5, inverse_rht=rht)
+    assert np.array_equal(back_c, back_r.T)
+
+
+# ------------------------------------------------------------- brute force, tiny
+def _e4m3_table():
+    return torch.from_numpy(np.arange(0, 0x7F, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _nearest_tie_even(value: float, cands: np.ndarray) -> int:
+    d = np.abs(cands.astype(np.float64) - value)
+    idx = np.nonzero(d == d.min())[0]
+    even = [i for i in idx if i % 2 == 0]
+    return int(even[0] if even else idx[0])
+
+
+def _brute_quantize(x: np.ndarray, fmt: str):
+    """Independent scalar quantizer (no RHT, RTNE, row axis) for tiny inputs."""
+    R, C = x.shape
+    levels = UNI if fmt == "ufp4" else E2M1
+    B = 32 if fmt == "mxfp4" else 16
+    table = _e4m3_table()
+    G = np.float32(levels[-1])
+    s_t = np.float32(np.float32(np.abs(x).max()) / np.float32(G * np.float32(448)))
+    codes = np.zeros((R, C), dtype=np.uint8)
+    scales = np.zeros((R, C // B), dtype=np.uint8)
+    for i in range(R):
+        for b in range(C // B):
+            y = x[i, b * B:(b + 1) * B]
+            amax = np.float32(np.abs(y).max())
+            if fmt == "mxfp4":
+                e = -127 if amax == 0 else max(-127, int(np.floor(np.log2(np.float64(amax)))) - 2)
+                S, d = e + 127, np.float32(2.0 ** e)
+            else:
+                if s_t == 0 or amax == 0:
+                    S = 0
+                else:
+                    r = np.float32(amax / np.float32(s_t * G))
+                    S = 0x7E if r >= 448 else _nearest_tie_even(float(r), table)
+                d = np.float32(s_t * table[S]) if S else np.float32(0)
+            scales[i, b] = S
+            for j in range(B):
+                yj = y[j]
+                k = 0
+                if d != 0 and yj != 0:
+                    v = np.float32(yj * np.float32(np.float32(1) / d))
+                    k = 7 if abs(v) >= levels[-1] else _nearest_tie_even(abs(float(v)), levels)
+                codes[i, b * B + j] = (8 if np.signbit(yj) else 0) | k
+    return codes, scales, s_t
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("kind", ["normal", "wide_range", "tiny", "zeros_mixed", "grid_ties"])
+def test_brute_force_tiny(fmt, kind):
+    x = workloads.small_case(kind, 3, 64, 21)
+    codes, scales, ts = oracle.quantize(x, fmt)
+    bc, bs, bts = _brute_quantize(x, fmt)
+    assert np.array_equal(oracle.unpack_codes(codes), bc)
+    assert np.array_equal(scales, bs)
+    if fmt != "mxfp4":
+        assert ts == bts
+
+
+# --------------------------------------------------------------------- properties
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4"])
+def test_each_code_is_a_nearest_level(fmt):
+    x = workloads.to_bf16_bits(workloads.small_case("t3", 128, 256, 4))
+    codes, scales, ts = oracle.quantize(x, fmt, rht=True, rht_seed=2)
+    y = oracle.rht(x, "row", 2)
+    xhat = oracle.dequantize(codes, scales, ts, 128, 256, fmt, rht=True, rht_seed=2)
+    B = 32 if fmt == "mxfp4" else 16
+    levels = UNI if fmt == "ufp4" else E2M1
+    if fmt == "mxfp4":
+        d = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    else:
+        d = np.float32(ts) * _e4m3_table()[np.minimum(scales, 0x7E)].astype(np.float32)
+        d = np.where(scales == 0, 0, d)
+    d = np.repeat(d.astype(np.float64), B, axis=1)
+    ok = d > 0
+    err = np.abs(y - xhat)
+    # no other level of the block is strictly closer (saturation aside)
+    for lev in levels:
+        alt = np.abs(np.abs(y) - lev * d)
+        sat = np.abs(y) > levels[-1] * d
+        slack = 2.0 ** -22 * np.maximum(np.abs(y), lev * d)  # fp32 rounding of L[k] * d_b
+        assert ((err <= alt + slack) | ~ok | sat).all()
+
+
+def test_empty_and_leading_dimension():
+    L = oracle.lib()
+    p = oracle.make_params("nvfp4")
+    ts = np.zeros(1, dtype=np.float32)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    dummy = np.zeros(1, dtype=np.uint8)
+    rc = L.fp4r_quantize(dummy.ctypes.data, 1, 0, 0, 0, ctypes.byref(p),
+                         dummy.ctypes.data_as(u8), dummy.ctypes.data_as(u8),
+                         ts.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    assert rc == 0 and ts[0] == 0.0
+    # a strided view (ld > cols) gives the same result as the dense copy
+    big = workloads.small_case("normal", 8, 80, 3)
+    dense = np.ascontiguousarray(big[:, :64])
+    codes = np.zeros((8, 32), dtype=np.uint8)
+    scales = np.zeros((8, 4), dtype=np.uint8)
+    rc = L.fp4r_quantize(big.ctypes.data, 1, 8, 64, 80, ctypes.byref(p),
+                         codes.ctypes.data_as(u8), scales.ctypes.data_as(u8),
+                         ts.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    assert rc == 0
+    c2, s2, t2 = oracle.quantize(dense, "nvfp4")
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2) and ts[0] == t2
+
+
+def test_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((4, 24), dtype=np.float32), "nvfp4")
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((4, 48), dtype=np.float32), "mxfp4")
+    with pytest.raises(ValueError):
+        oracle.quantize(np.zeros((24, 32), dtype=np.float32), "nvfp4", "col")
+
+
+def test_all_zero_tensor():
+    x = np.zeros((4, 32), dtype=np.float32)
+    x[1, 3] = -0.0
+    for fmt in ("nvfp4", "ufp4", "mxfp4"):
+        codes, scales, ts = oracle.quantize(x, fmt, rht=True)
+        assert (scales == 0).all()
+        assert ts in (0.0, None)
+        assert set(np.unique(oracle.unpack_codes(codes))) <= {0, 8}
+
+
+# ------------------------------------------------------------- page directions
+def test_sr_mean_tends_to_input():
+    """Averaged over seeds, SR dequantization approaches the input
+    (TetraJet-v2 page, 2.A: E[round(x)] = x)."""
+    x = workloads.small_case("normal", 16, 64, 9)
+    acc = np.zeros_like(x, dtype=np.float64)
+    n = 400
+    for s in range(n):
+        c, sc, ts = oracle.quantize(x, "nvfp4", rounding="sr", sr_seed=s)
+        acc += oracle.dequantize(c, sc, ts, 16, 64, "nvfp4")
+    c, sc, ts = oracle.quantize(x, "nvfp4")
+    rtne_err = np.abs(oracle.dequantize(c, sc, ts, 16, 64, "nvfp4") - x).mean()
+    sr_mean_err = np.abs(acc / n - x).mean()
+    assert sr_mean_err < 0.25 * rtne_err
+
+
+def _normalized_bias(x, fmt, rht):
+    """Mean of q - v in normalized magnitude space (v = |y| / d_b, q its
+    level), over elements of blocks with a nonzero scale: the quantity whose
+    per-bin expectation the shrinkage-bias page gives as (l - r)/2."""
+    codes, scales, ts = oracle.quantize(x, fmt, rht=rht, rht_seed=0)
+    y = oracle.rht(x, "row", 0) if rht else workloads.bf16_bits_to_f32(x)
+    d = np.float32(ts) * _e4m3_table()[np.minimum(scales, 0x7E)].astype(np.float32)
+    d = np.repeat(np.where(scales == 0, 0, d).astype(np.float64), 16, axis=1)
+    levels = UNI if fmt == "ufp4" else E2M1
+    q = levels[oracle.unpack_codes(codes) & 7]
+    ok = d > 0
+    return float((q[ok] - np.abs(y)[ok] / d[ok]).mean())
+
+
+def test_shrinkage_direction_under_rht():
+    """Shrinkage-bias page (Metodologia 1 and Resultados): under the RHT the
+    E2M1 grid shrinks magnitudes (negative normalized bias) more than the
+    uniform grid; on an outlier-heavy tensor the RHT makes E2M1's bias worse
+    and the uniform grid's better."""
+    w = workloads.weight_with_spikes(256, 1024, 0)
+    b_e2m1 = _normalized_bias(w, "nvfp4", True)
+    b_uni = _normalized_bias(w, "ufp4", True)
+    assert b_e2m1 < 0
+    assert abs(b_uni) < abs(b_e2m1)
+    a = workloads.activation_with_outlier_channels(256, 1024, 0)
+    assert _normalized_bias(a, "nvfp4", True) < _normalized_bias(a, "nvfp4", False)
+    assert abs(_normalized_bias(a, "ufp4", True)) < abs(_normalized_bias(a, "ufp4", False))
