@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RHT + FP4 quantize path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input: every
+quantize call of the workload (default: the 4096x4096 BF16 Student-t
+activation with outlier channels, 16-point RHT + NVFP4, row axis, once with
+RTNE and once with stochastic rounding).  Inputs are resident in device
+memory before timing starts.  W untimed warmup steps, then exactly K steps
+between device synchronizations, timed with HIP events on the stream the
+kernels run on.  Prints one JSON line.
+
+`value` is input GB/s over the whole step (bytes of BF16 input of every call
+/ step time).  `roofline` covers the dominant call: its algorithmic bytes
+(input + codes + scale bytes + 4-byte tensor scale) over its mean duration,
+against the 8 TB/s HBM peak.  `cpu_baseline` times the scalar oracle on the
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
+KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_kernels.hip",
+                  "block_scaled_bit_fp4_amd/csrc/fp4_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int) -> int:
+    """Bytes the method must move once: the input, the packed codes, one
+    scale byte per block, and the FP32 tensor scale for two-level formats."""
+    n = rows * cols
+    block = 32 if fmt == "mxfp4" else 16
+    return n * in_bytes + n // 2 + n // block + (0 if fmt == "mxfp4" else 4)
+
+
+def traffic_for(workload: str, call_index: int):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    per = t.get("per_call_bytes")
+    if not per or call_index >= len(per):
+        return None
+    return per[call_index]
+
+
+def cpu_baseline(w, tensors, budget_s=12.0):
+    """The oracle, as it is, on the host: whole workload steps repeated until
+    ~budget_s of CPU time has passed (at least one step)."""
+    import oracle
+    reps, t0, nbytes = 0, time.perf_counter(), 0
+    while True:
+        for call in w.calls:
+            x = tensors[call.tensor]
+            oracle.quantize(x, call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
+                            call.sr_seed)
+            nbytes += x.size * x.itemsize
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d full step(s) of the workload (%d calls each) in %.1f s" % (
+                reps, len(w.calls), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="activation")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the hot path is single-GPU in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_bit_fp4_amd as fp4
+    import workloads
+
+    w = workloads.workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tensors = {}
+    for call in w.calls:
+        if call.tensor not in tensors:
+            tensors[call.tensor] = w.make(call.tensor)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    dtensors = {k: to_dev(v) for k, v in tensors.items()}
+    # preallocated outputs and workspaces, so the timed loop only launches
+    plans = []
+    for call in w.calls:
+        x = dtensors[call.tensor]
+        rows, cols = x.shape
+        cs, ss = fp4.output_shapes(rows, cols, call.fmt, call.axis)
+        p = fp4.make_params(call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
+                            call.sr_seed)
+        nws = fp4.workspace_bytes(rows, cols, p)
+        plans.append(dict(
+            call=call, x=x,
+            codes=torch.empty(cs, dtype=torch.uint8, device=dev),
+            scales=torch.empty(ss, dtype=torch.uint8, device=dev),
+            ts=torch.empty(1, dtype=torch.float32, device=dev),
+            ws=torch.empty(max(nws, 16), dtype=torch.uint8, device=dev) if nws else None,
+            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size()),
+            in_bytes=x.numel() * x.element_size()))
+    stream = torch.cuda.current_stream()
+
+    def run(pl):
+        c = pl["call"]
+        fp4.quantize(pl["x"], c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed,
+                     codes=pl["codes"], scales=pl["scales"], ts_out=pl["ts"],
+                     workspace=pl["ws"], stream=stream)
+
+    def step():
+        for pl in plans:
+            run(pl)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t_wall = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    in_bytes = sum(pl["in_bytes"] for pl in plans)
+    value = in_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-call durations (events on the launch stream around each call)
+    reps = max(20, args.steps // 2)
+    per_call = []
+    for i, pl in enumerate(plans):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            run(pl)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        per_call.append(ms)
+    dom = max(range(len(plans)), key=lambda i: per_call[i])
+    pl = plans[dom]
+    achieved = pl["alg"] / (per_call[dom] * 1e-3) / 1e9
+    c = pl["call"]
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload, dom),
+        "kernel": "fp4_quantize call %d (%s %s %s rht=%s): tensor-amax + quantize kernels"
+                  % (dom, c.fmt, c.axis, c.rounding, c.rht),
+        "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, tensors)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description,
+                   "tensors": {k: list(v.shape) for k, v in tensors.items()},
+                   "calls": ["%s %s %s %s rht=%s" % (c.tensor, c.fmt, c.axis, c.rounding, c.rht)
+                             for c in w.calls],
+                   "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+                   "per_call_us": [round(m * 1e3, 2) for m in per_call],
+                   "wall_ms_per_step": round(wall_ms, 4)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""MI355X (gfx950) fused RHT + block-scaled FP4 quantize / dequantize.
+
+A thin ctypes binding over ``libfp4.so`` (the C ABI in ``include/fp4.h``).
+This module only marshals arguments: it allocates outputs as torch device
+tensors, passes raw pointers, sizes and the current HIP stream, and raises on
+a non-zero status.  Every step of the computation runs in the HIP kernels;
+there is no CPU fallback, and importing the library fails loudly when
+``libfp4.so`` has not been built (``python -m block_scaled_bit_fp4_amd.build``).
+
+Formats: ``"nvfp4"`` (E2M1, 16-element blocks, E4M3 scale, FP32 tensor
+scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
+(uniform 0..7 grid, 16-element blocks, E4M3 scale, FP32 tensor scale).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp4.so")
+
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16}
+AXES = {"row": 0, "col": 1}
+ROUNDINGS = {"rtne": 0, "sr": 1}
+DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+
+FP4_OK = 0
+STATUS = {0: "FP4_OK", -1: "FP4_ERR_NULL", -2: "FP4_ERR_FORMAT", -3: "FP4_ERR_SHAPE",
+          -4: "FP4_ERR_ALIGN", -5: "FP4_ERR_DTYPE", -6: "FP4_ERR_WORKSPACE",
+          -7: "FP4_ERR_DEVICE"}
+
+# every symbol include/fp4.h declares
+EXPORTS = ("fp4_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_rht",
+           "fp4_rht_signs", "fp4_status_str")
+
+
+class FP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = load().fp4_status_str(status).decode()
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status), msg))
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("axis", ctypes.c_int32),
+        ("rounding", ctypes.c_int32),
+        ("rht", ctypes.c_int32),
+        ("ts_mode", ctypes.c_int32),
+        ("rht_seed", ctypes.c_uint64),
+        ("sr_seed", ctypes.c_uint64),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """The ctypes handle of libfp4.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp4.so is not built: run python -m block_scaled_bit_fp4_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER(Params)
+        L.fp4_workspace_bytes.argtypes = [i64, i64, P]
+        L.fp4_workspace_bytes.restype = sz
+        L.fp4_quantize.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, sz, vp]
+        L.fp4_quantize.restype = i32
+        L.fp4_dequantize.argtypes = [vp, vp, vp, i64, i64, P, i32, vp, i32, i64, vp]
+        L.fp4_dequantize.restype = i32
+        L.fp4_rht.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_uint64, i32, vp, vp]
+        L.fp4_rht.restype = i32
+        L.fp4_rht_signs.argtypes = [ctypes.c_uint64]
+        L.fp4_rht_signs.restype = ctypes.c_uint16
+        L.fp4_status_str.argtypes = [i32]
+        L.fp4_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_params(fmt="nvfp4", axis="row", rounding="rtne", rht=False, rht_seed=0, sr_seed=0,
+                ts_given=False) -> Params:
+    return Params(FORMATS[fmt], BLOCK[fmt], AXES[axis], ROUNDINGS[rounding], int(bool(rht)),
+                  1 if ts_given else 0, int(rht_seed) & (2**64 - 1), int(sr_seed) & (2**64 - 1))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_2d(x: torch.Tensor, name: str):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("%s must be a 2-D tensor with unit column stride" % name)
+    if not x.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def rht_signs(seed: int) -> int:
+    return int(load().fp4_rht_signs(int(seed) & (2**64 - 1)))
+
+
+def workspace_bytes(rows: int, cols: int, params: Params) -> int:
+    return int(load().fp4_workspace_bytes(rows, cols, ctypes.byref(params)))
+
+
+def output_shapes(rows: int, cols: int, fmt: str, axis: str):
+    ra, w = (rows, cols) if axis == "row" else (cols, rows)
+    return (ra, w // 2), (ra, w // BLOCK[fmt])
+
+
+def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: str = "rtne",
+             rht: bool = False, rht_seed: int = 0, sr_seed: int = 0,
+             tensor_scale=None, codes: Optional[torch.Tensor] = None,
+             scales: Optional[torch.Tensor] = None, ts_out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Quantize a BF16/FP32 device matrix.  Returns (codes, scales, tensor_scale).
+
+    ``tensor_scale``: None computes the NVFP4/UFP4 tensor scale from the data;
+    a float or one-element float32 device tensor supplies it.  The returned
+    tensor scale is a one-element float32 device tensor (None for MXFP4)."""
+    _check_2d(x, "x")
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    given = tensor_scale is not None
+    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given)
+    cshape, sshape = output_shapes(rows, cols, fmt, axis)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
+    ts = None
+    if fmt != "mxfp4":
+        if given:
+            ts = tensor_scale if torch.is_tensor(tensor_scale) else torch.tensor(
+                [float(tensor_scale)], dtype=torch.float32, device=dev)
+        else:
+            ts = ts_out if ts_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    nws = workspace_bytes(rows, cols, p)
+    if nws and workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    st = load().fp4_quantize(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
+                             ctypes.byref(p), codes.data_ptr(), scales.data_ptr(), _ptr(ts),
+                             _ptr(workspace), nws if workspace is not None else 0,
+                             _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_quantize")
+    return codes, scales, ts
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: int, cols: int,
+               fmt: str = "nvfp4", axis: str = "row", rht: bool = False, rht_seed: int = 0,
+               inverse_rht: bool = False, out_dtype=torch.float32,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rebuild a rows x cols matrix (x's layout) from codes and scales."""
+    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, True)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    if out.dtype not in DTYPES:
+        raise TypeError("out must be bfloat16 or float32")
+    st = load().fp4_dequantize(codes.data_ptr(), scales.data_ptr(), _ptr(tensor_scale), rows,
+                               cols, ctypes.byref(p), int(bool(inverse_rht)), out.data_ptr(),
+                               DTYPES[out.dtype], out.stride(0), _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_dequantize")
+    return out
+
+
+def rht(x: torch.Tensor, axis: str = "row", seed: int = 0, inverse: bool = False,
+        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Standalone 16-point RHT (or its inverse) along an axis; FP32 output."""
+    _check_2d(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    st = load().fp4_rht(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0), AXES[axis],
+                        int(seed) & (2**64 - 1), int(bool(inverse)), out.data_ptr(),
+                        _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_rht")
+    return out

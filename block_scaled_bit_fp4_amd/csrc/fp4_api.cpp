@@ -1,0 +1,213 @@
+// fp4_api.cpp -- the C ABI declared in include/fp4.h: host-side validation
+// (no HIP call happens before every argument has been checked) and dispatch
+// to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "fp4.h"
+#include "fp4_launch.h"
+
+namespace {
+
+// Host Philox4x32-10 (Salmon et al., SC'11) for the RHT sign mask.
+void philox10_host(uint32_t k0, uint32_t k1, uint32_t c[4]) {
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = (uint32_t)p1;
+    c[2] = n2;
+    c[3] = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("FP4_DEBUG_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+fp4_status finish(hipError_t e, hipStream_t s) {
+  if (e != hipSuccess) return FP4_ERR_DEVICE;
+  if (debug_sync()) {
+    if (hipStreamSynchronize(s) != hipSuccess) return FP4_ERR_DEVICE;
+    if (hipGetLastError() != hipSuccess) return FP4_ERR_DEVICE;
+  }
+  return FP4_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int32_t dt) { return dt == FP4_BF16 ? 2 : 4; }
+
+fp4_status check_params(const fp4_params* p) {
+  if (!p) return FP4_ERR_NULL;
+  if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4)
+    return FP4_ERR_FORMAT;
+  if (p->block != (p->format == FP4_MXFP4 ? 32 : 16)) return FP4_ERR_FORMAT;
+  if (p->axis != FP4_AXIS_ROW && p->axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
+  if (p->rounding != FP4_RTNE && p->rounding != FP4_SR) return FP4_ERR_FORMAT;
+  if (p->rht != 0 && p->rht != 1) return FP4_ERR_FORMAT;
+  if (p->format != FP4_MXFP4 && p->ts_mode != FP4_TS_COMPUTE && p->ts_mode != FP4_TS_GIVEN)
+    return FP4_ERR_FORMAT;
+  return FP4_OK;
+}
+
+fp4_status check_shape(const fp4_params* p, int64_t rows, int64_t cols, int64_t ld) {
+  if (rows < 0 || cols < 0 || ld < cols || ld < 0) return FP4_ERR_SHAPE;
+  const int64_t W = p->axis == FP4_AXIS_ROW ? cols : rows;
+  if (W % p->block) return FP4_ERR_SHAPE;
+  if (p->rht && (W % 16)) return FP4_ERR_SHAPE;
+  return FP4_OK;
+}
+
+bool two_level(const fp4_params* p) { return p->format != FP4_MXFP4; }
+
+bool needs_workspace(const fp4_params* p) {
+  return two_level(p) && p->ts_mode == FP4_TS_COMPUTE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p) {
+  (void)rows;
+  (void)cols;
+  if (check_params(p) != FP4_OK) return 0;
+  return needs_workspace(p) ? sizeof(float) * (size_t)kAmaxPartials : 0;
+}
+
+uint16_t fp4_rht_signs(uint64_t rht_seed) {
+  uint32_t c[4] = {0u, 0u, 1u, 0u};
+  philox10_host((uint32_t)rht_seed, (uint32_t)(rht_seed >> 32), c);
+  return (uint16_t)(c[0] & 0xFFFFu);
+}
+
+fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                        int64_t ld, const fp4_params* p, uint8_t* codes, uint8_t* scales,
+                        float* tensor_scale, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  fp4_status st = check_params(p);
+  if (st != FP4_OK) return st;
+  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if ((st = check_shape(p, rows, cols, ld)) != FP4_OK) return st;
+  const bool empty = rows == 0 || cols == 0;
+  if (two_level(p) && !tensor_scale) return FP4_ERR_NULL;
+  if (!empty) {
+    if (!x || !codes || !scales) return FP4_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FP4_ERR_ALIGN;
+    if ((ld * (int64_t)elem_size(in_dtype)) % 16) return FP4_ERR_ALIGN;
+  }
+  if (needs_workspace(p)) {
+    if (!workspace) return FP4_ERR_WORKSPACE;
+    if (ws_bytes < sizeof(float) * (size_t)kAmaxPartials) return FP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (empty) {
+    if (needs_workspace(p)) return finish(fp4_launch_write_scalar(tensor_scale, 0.0f, s), s);
+    return FP4_OK;
+  }
+  QuantLaunch q{};
+  q.x = x;
+  q.in_dtype = in_dtype;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld = ld;
+  q.format = p->format;
+  q.axis = p->axis;
+  q.sr = p->rounding == FP4_SR;
+  q.rht = p->rht;
+  q.ts_given = two_level(p) && p->ts_mode == FP4_TS_GIVEN;
+  q.signs = p->rht ? fp4_rht_signs(p->rht_seed) : 0u;
+  q.sr_k0 = (uint32_t)p->sr_seed;
+  q.sr_k1 = (uint32_t)(p->sr_seed >> 32);
+  q.codes = codes;
+  q.scales = scales;
+  q.tensor_scale = tensor_scale;
+  q.workspace = static_cast<float*>(workspace);
+  return finish(fp4_launch_quantize(q, s), s);
+}
+
+fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, int64_t rows, int64_t cols,
+                          const fp4_params* p, int32_t inverse_rht, void* out,
+                          int32_t out_dtype, int64_t ld_out, void* stream) {
+  fp4_status st = check_params(p);
+  if (st != FP4_OK) return st;
+  if (out_dtype != FP4_BF16 && out_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if (inverse_rht != 0 && inverse_rht != 1) return FP4_ERR_FORMAT;
+  if (inverse_rht && !p->rht) return FP4_ERR_FORMAT;
+  if ((st = check_shape(p, rows, cols, ld_out)) != FP4_OK) return st;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !out) return FP4_ERR_NULL;
+  if (two_level(p) && !tensor_scale) return FP4_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(out)) return FP4_ERR_ALIGN;
+  if ((ld_out * (int64_t)elem_size(out_dtype)) % 16) return FP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DequantLaunch q{};
+  q.codes = codes;
+  q.scales = scales;
+  q.tensor_scale = tensor_scale;
+  q.rows = rows;
+  q.cols = cols;
+  q.format = p->format;
+  q.axis = p->axis;
+  q.inverse_rht = inverse_rht;
+  q.signs = p->rht ? fp4_rht_signs(p->rht_seed) : 0u;
+  q.out = out;
+  q.out_dtype = out_dtype;
+  q.ld_out = ld_out;
+  return finish(fp4_launch_dequantize(q, s), s);
+}
+
+fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                   int32_t axis, uint64_t rht_seed, int32_t inverse, float* y, void* stream) {
+  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if (axis != FP4_AXIS_ROW && axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
+  if (inverse != 0 && inverse != 1) return FP4_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || ld < cols) return FP4_ERR_SHAPE;
+  const int64_t W = axis == FP4_AXIS_ROW ? cols : rows;
+  if (W % 16) return FP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !y) return FP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return FP4_ERR_ALIGN;
+  if ((ld * (int64_t)elem_size(in_dtype)) % 16 || (cols * 4) % 16) return FP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RhtLaunch q{};
+  q.x = x;
+  q.in_dtype = in_dtype;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld = ld;
+  q.axis = axis;
+  q.inverse = inverse;
+  q.signs = fp4_rht_signs(rht_seed);
+  q.y = y;
+  return finish(fp4_launch_rht(q, s), s);
+}
+
+const char* fp4_status_str(fp4_status s) {
+  switch (s) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_NULL: return "a required pointer is NULL";
+    case FP4_ERR_FORMAT: return "invalid format, block, axis, rounding or mode";
+    case FP4_ERR_SHAPE: return "invalid shape or leading dimension";
+    case FP4_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case FP4_ERR_DTYPE: return "unknown element type";
+    case FP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP4_ERR_DEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

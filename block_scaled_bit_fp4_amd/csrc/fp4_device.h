@@ -1,0 +1,192 @@
+// fp4_device.h -- device-side building blocks of the gfx950 FP4 codec.
+//
+// Everything here runs per lane in registers.  The arithmetic is binary32
+// with round-to-nearest-even in the order of the method's description (the
+// library is built with -ffp-contract=off and correctly rounded division),
+// so codes and scales are reproducible bit for bit on any launch geometry.
+//
+// Pages cited (summaries on gist.science):
+//   [UFP4]  es/paper/2606.20381  shrinkage bias and the uniform E1M2 grid
+//   [NGPT]  it/paper/2605.06067  normalized transformers under NVFP4
+//   [TJ2]   it/paper/2510.27527  TetraJet-v2 NVFP4 training
+//   [MXFP4] fr/paper/2603.08713  MXFP4 error reduction (OAS, MBS)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2 };
+
+// ---------------------------------------------------------------- widening
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------ Philox4x32-10
+// Counter-based generator of Salmon et al. (SC'11): ten rounds of
+// 32x32->64-bit products of counter words with the two round multipliers,
+// high halves xor-ed with the other counter words and the key, key bumped
+// by the Weyl constants between rounds.  One 64-bit product per multiplier
+// maps to a single v_mad_u64_u32.
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t k0, uint32_t k1, uint32_t c0,
+                                               uint32_t c1, uint32_t c2, uint32_t c3) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// ------------------------------------------------------------ RHT butterfly
+// 16-point Walsh-Hadamard butterfly in natural (Sylvester) order, stages
+// h = 1, 2, 4, 8 ([UFP4] Metodologia 1-2, "Eficiencia"; [TJ2] 2.C).  The
+// stage order is fixed so that the binary32 result does not depend on the
+// launch geometry.
+__device__ __forceinline__ void fwht16(float (&t)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      const float u = t[j], v = t[j + h];
+      t[j] = u + v;
+      t[j + h] = u - v;
+    }
+  }
+}
+
+// Sign flip d_j a_j for a group (bit j of `signs` set: d_j = -1).
+__device__ __forceinline__ void apply_signs(float (&t)[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    t[j] = __uint_as_float(__float_as_uint(t[j]) ^ (((signs >> j) & 1u) << 31));
+}
+
+// Forward RHT of one group: y = (1/4) H16 D a.
+__device__ __forceinline__ void rht16_forward(float (&t)[16], uint32_t signs) {
+  apply_signs(t, signs);
+  fwht16(t);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = t[j] * 0.25f;
+}
+
+// Inverse: a = D (1/4) H16 y.
+__device__ __forceinline__ void rht16_inverse(float (&t)[16], uint32_t signs) {
+  fwht16(t);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = t[j] * 0.25f;
+  apply_signs(t, signs);
+}
+
+// -------------------------------------------------------------- scale bytes
+// E4M3 (OCP FN variant: bias 7, max 448, no infinities) of r >= 0, round to
+// nearest even, saturating at 448.  Below 2^-6 the format is subnormal with
+// step 2^-9, so the code is rint(r * 512); above, the binary32 mantissa is
+// rounded to 3 bits and rebiased.  Branch-free.
+__device__ __forceinline__ uint32_t e4m3_encode(float r) {
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(r, 0.015625f) * 512.0f);
+  uint32_t b = __float_as_uint(r);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  const uint32_t nor = (b >> 20) - (120u << 3);
+  const uint32_t s = r < 0.015625f ? sub : nor;
+  return r < 448.0f ? s : 0x7Eu;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  const float nor = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nor;
+}
+
+// MX scale exponent ([MXFP4] 2: power-of-two E8M0 scale): floor(log2 amax)
+// minus E2M1's top exponent 2, clamped to [-127, 127]; zero or subnormal
+// amax lands on -127.  amax >= 0.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const int ex = (int)(__float_as_uint(amax) >> 23);
+  const int e = ex - 129;
+  return (ex == 0 || e < -127) ? -127 : e;
+}
+
+// ---------------------------------------------------------- element grids
+// E2M1 levels 0, .5, 1, 1.5, 2, 3, 4, 6 ([UFP4] Problema; [TJ2] Riepilogo 1;
+// [MXFP4] 2.A limit 6).  Uniform levels 0..7 ([UFP4] Metodologia 2).
+__device__ __forceinline__ float e2m1_level(uint32_t k) {
+  const float big = __uint_as_float((((k >> 1) + 126u) << 23) | ((k & 1u) << 22));
+  return k < 2u ? (k ? 0.5f : 0.0f) : big;
+}
+
+template <int FMT>
+__device__ __forceinline__ float grid_level(uint32_t k) {
+  if constexpr (FMT == kUFP4) return (float)k;
+  else return e2m1_level(k);
+}
+
+// Magnitude code of m >= 0 (or +inf), round to nearest even code.
+// E2M1: inside each binade the levels are equally spaced (0.5 below 2, 1 in
+// [2,4), 2 above 4) and the even code is the even multiple of the spacing,
+// so rint(m / spacing) decides; values past 6 saturate.
+// Uniform: rint(m), saturating at 7.
+template <int FMT>
+__device__ __forceinline__ uint32_t round_rtne_sw(float m) {
+  if constexpr (FMT == kUFP4) {
+    return (uint32_t)fminf(__builtin_rintf(m), 7.0f);
+  } else {
+    const bool lo = m < 2.0f, mid = m < 4.0f;
+    const float q = lo ? m * 2.0f : (mid ? m : m * 0.5f);
+    const float off = lo ? 0.0f : (mid ? 2.0f : 4.0f);
+    return (uint32_t)fminf(__builtin_rintf(q) + off, 7.0f);
+  }
+}
+
+// Stochastic rounding ([TJ2] 2.A; [UFP4] Metodologia 2): with L[k] <= m <
+// L[k+1], round up iff u16 < p * 2^16, p = (m - L[k]) / (L[k+1] - L[k]),
+// which is the (exact) fractional part of m / spacing.
+template <int FMT>
+__device__ __forceinline__ uint32_t round_sr_sw(float m, uint32_t u16) {
+  float q, off;
+  if constexpr (FMT == kUFP4) {
+    q = m;
+    off = 0.0f;
+  } else {
+    const bool lo = m < 2.0f, mid = m < 4.0f;
+    q = lo ? m * 2.0f : (mid ? m : m * 0.5f);
+    off = lo ? 0.0f : (mid ? 2.0f : 4.0f);
+  }
+  const float fl = __builtin_floorf(q);
+  const float up = (float)u16 < (q - fl) * 65536.0f ? 1.0f : 0.0f;
+  return (uint32_t)fminf(fl + off + up, 7.0f);
+}
+
+// G, the largest level, in the two-level tensor scale amax / (G * 448).
+template <int FMT>
+__device__ __forceinline__ float grid_max() { return FMT == kUFP4 ? 7.0f : 6.0f; }
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Block-wide max over a 256-thread workgroup; every thread gets the result.
+__device__ __forceinline__ float block_max_256(float v) {
+  __shared__ float red[4];
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+}  // namespace fp4dev

@@ -1,0 +1,50 @@
+// fp4_launch.h -- internal interface between the C-ABI layer and the kernels.
+// Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Number of per-workgroup partial maxima of the tensor-amax pass; the
+// workspace of a two-level quantize in computed-scale mode holds this many
+// floats.
+constexpr int kAmaxPartials = 1024;
+
+struct QuantLaunch {
+  const void* x;
+  int in_dtype;  // 0 bf16, 1 f32
+  int64_t rows, cols, ld;
+  int format, axis, sr, rht, ts_given;
+  uint32_t signs;
+  uint32_t sr_k0, sr_k1;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* tensor_scale;
+  float* workspace;
+};
+
+struct DequantLaunch {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tensor_scale;
+  int64_t rows, cols;
+  int format, axis, inverse_rht;
+  uint32_t signs;
+  void* out;
+  int out_dtype;  // 0 bf16, 1 f32
+  int64_t ld_out;
+};
+
+struct RhtLaunch {
+  const void* x;
+  int in_dtype;
+  int64_t rows, cols, ld;
+  int axis, inverse;
+  uint32_t signs;
+  float* y;
+};
+
+hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s);
+hipError_t fp4_launch_write_scalar(float* p, float v, hipStream_t s);

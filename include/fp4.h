@@ -1,0 +1,157 @@
+/*
+ * fp4.h -- C ABI of the gfx950 (MI355X) fused RHT + block-scaled 4-bit codec.
+ *
+ * One shared library, libfp4.so, exports the functions below.  Every tensor
+ * argument is a plain device pointer (HIP device memory, e.g. a torch
+ * tensor's data_ptr()) and every size is an element count; no C++ or torch
+ * type crosses this boundary.  `stream` is a hipStream_t passed as void*
+ * (NULL = the default stream).
+ *
+ * Method (summaries on gist.science; the page title and section are given):
+ *  - Block-scaled FP4 with the E2M1 element grid and a random Hadamard
+ *    transform (RHT) before quantization: "Replanteamiento del Sesgo de
+ *    Contraccion en el Preentrenamiento de LLM en FP4" (es/paper/2606.20381),
+ *    "Declaracion del Problema", "Metodologia" 1-2 and "Eficiencia" (RHT and
+ *    quantization fused in one pass).
+ *  - The uniform E1M2/INT4 grid (UFP4) with RHT on every training GEMM and
+ *    stochastic rounding on dY: same page, "Metodologia" 2.
+ *  - NVFP4 (16-element groups, 8-bit E4M3 scale), stochastic rounding so
+ *    that E[round(x)] = x, 1x16 groups realigned for the transposed weight,
+ *    RHT on the backward GEMMs: "TetraJet-v2: Accurate NVFP4 Training for
+ *    Large Language Models ..." (it/paper/2510.27527), Riepilogo Tecnico
+ *    2.A and 2.C.
+ *  - Per-tensor dynamic scaling as part of the NVFP4 recipe: "Le
+ *    Architetture Normalizzate sono Nativamente a 4 Bit"
+ *    (it/paper/2605.06067), "Enunciato del Problema".
+ *  - MXFP4 (32-element blocks, power-of-two E8M0 scale, saturation at the
+ *    FP4 limit 6): "Unveiling the Potential of Quantization with MXFP4 ..."
+ *    (fr/paper/2603.08713), "2. Methodologie et Analyse" and 2.A.
+ *
+ * Numerics (one output per input; any launch geometry gives the same bytes):
+ *  - A is the logical operand: x (FP4_AXIS_ROW) or x^T (FP4_AXIS_COL); W is
+ *    the length of A's rows; blocks are B consecutive elements of an A-row.
+ *  - RHT: per aligned 16-group of an A-row, y = (1/4) H16 D a, H16 the
+ *    Sylvester-ordered Hadamard matrix, D = diag(+-1) from fp4_rht_signs(),
+ *    computed in binary32 as butterfly stages h = 1, 2, 4, 8, then * 0.25.
+ *  - NVFP4 (G = 6) / UFP4 (G = 7): s_t = amax|y| / (G * 448) (binary32);
+ *    per block S = E4M3_RNE_satfinite(amax_b / (s_t * G)), d = s_t * S;
+ *    elements v = y * (1/d) rounded to the grid.  S = 0 or d = 0 gives
+ *    signed-zero codes.  MXFP4: d = 2^e, e = floor(log2 amax_b) - 2 clamped
+ *    to [-127, 127], scale byte e + 127.
+ *  - Grids: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; UFP4 {0, 1, ..., 7}; values
+ *    past the top level saturate.  RTNE ties go to the even code.  SR rounds
+ *    up iff u16 < p * 65536, p = (m - L[k]) / (L[k+1] - L[k]); u16 is half of
+ *    a Philox4x32-10 word (Salmon et al., SC'11) with key = sr_seed and
+ *    counter (g, 0, 0), g = n / 8, n = row_A * W + col_A; element n % 8 takes
+ *    half (n % 2) of word (n % 8) / 2.
+ *  - Codes: 4 bits, bit 3 = sign of y, bits 0-2 = level index.
+ *
+ * Layouts (all row-major, owned and allocated by the caller):
+ *  - x: rows x cols, leading dimension ld (elements), BF16 or FP32.
+ *  - codes: rows_A x (W / 2) bytes; byte (i, j/2) holds A[i][j], even j in
+ *    the low nibble.  rows_A = rows (ROW) or cols (COL); W = cols or rows.
+ *  - scales: rows_A x (W / B) bytes.
+ *  - tensor_scale: one float (NVFP4 / UFP4 only).
+ *
+ * Ownership and concurrency: the library allocates no memory and keeps no
+ * state between calls; all work is enqueued asynchronously on `stream` and
+ * the call never synchronizes (unless FP4_DEBUG_SYNC=1 is set in the
+ * environment, which synchronizes and checks after each launch).  Calls on
+ * different streams that share an output or a workspace race.
+ *
+ * Errors: arguments are validated on the host before anything is launched;
+ * an invalid call returns a negative fp4_status and enqueues nothing.  A
+ * launch failure returns FP4_ERR_DEVICE.  Faults inside a kernel surface at
+ * the caller's next synchronization.  Inputs containing NaN or Inf, or whose
+ * RHT overflows binary32, are outside the contract.
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp4_status;
+#define FP4_OK 0
+#define FP4_ERR_NULL (-1)      /* a required pointer is NULL */
+#define FP4_ERR_FORMAT (-2)    /* bad format / block / axis / rounding / mode */
+#define FP4_ERR_SHAPE (-3)     /* negative size, ld < cols, W not divisible */
+#define FP4_ERR_ALIGN (-4)     /* pointer or leading dimension misaligned */
+#define FP4_ERR_DTYPE (-5)     /* unknown element type */
+#define FP4_ERR_WORKSPACE (-6) /* workspace missing or too small */
+#define FP4_ERR_DEVICE (-7)    /* HIP launch failed */
+
+#define FP4_NVFP4 0 /* E2M1, 16-element blocks, E4M3 scale, FP32 tensor scale */
+#define FP4_MXFP4 1 /* E2M1, 32-element blocks, E8M0 scale */
+#define FP4_UFP4 2  /* uniform 0..7 grid, 16-element blocks, E4M3 + FP32 */
+
+#define FP4_AXIS_ROW 0 /* quantize along rows of x */
+#define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
+
+#define FP4_RTNE 0 /* round to nearest, ties to even code */
+#define FP4_SR 1   /* stochastic rounding with Philox draws */
+
+#define FP4_BF16 0
+#define FP4_F32 1
+
+#define FP4_TS_COMPUTE 0 /* tensor scale computed from the data, written out */
+#define FP4_TS_GIVEN 1   /* tensor scale read from *tensor_scale */
+
+typedef struct {
+  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 */
+  int32_t block;    /* 16 for NVFP4 and UFP4, 32 for MXFP4 */
+  int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
+  int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
+  int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
+  int32_t ts_mode;  /* FP4_TS_COMPUTE / FP4_TS_GIVEN (ignored for MXFP4) */
+  uint64_t rht_seed;
+  uint64_t sr_seed;
+} fp4_params;
+
+/* Bytes of device workspace fp4_quantize needs for this call (0 when none:
+ * MXFP4, or a given tensor scale).  Contents need no initialization. */
+size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
+
+/* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
+ * scales (layouts above).  tensor_scale is written (COMPUTE) or read
+ * (GIVEN) for NVFP4/UFP4 and may be NULL for MXFP4.  workspace must hold
+ * fp4_workspace_bytes() bytes.  Requirements: block matches the format; W
+ * divisible by the block (and by 16 when rht); ld >= cols; x, codes,
+ * scales 16-byte aligned; ld * element size a multiple of 16 bytes.
+ * rows == 0 or cols == 0 is valid (COMPUTE writes s_t = 0). */
+fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                        int64_t ld, const fp4_params* p, uint8_t* codes, uint8_t* scales,
+                        float* tensor_scale, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* Rebuild x from codes, scales and tensor_scale (as produced by
+ * fp4_quantize with the same rows, cols and params) into out, in x's
+ * layout (rows x cols, leading dimension ld_out), FP32 or BF16 (RNE).
+ * inverse_rht = 1 undoes the RHT (requires p->rht).  Each value is
+ * sign * L[k] * d, one binary32 product per element. */
+fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, int64_t rows, int64_t cols,
+                          const fp4_params* p, int32_t inverse_rht, void* out,
+                          int32_t out_dtype, int64_t ld_out, void* stream);
+
+/* Standalone RHT (inverse = 0) or its inverse (inverse = 1) along `axis`,
+ * per aligned 16-group; y is rows x cols FP32, dense (leading dimension
+ * cols), in x's layout. */
+fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                   int32_t axis, uint64_t rht_seed, int32_t inverse, float* y, void* stream);
+
+/* The RHT sign mask of a seed (host function): low 16 bits of word 0 of
+ * Philox4x32-10(key = seed, counter = (0, 0, 1, 0)); bit j set: d_j = -1. */
+uint16_t fp4_rht_signs(uint64_t rht_seed);
+
+/* Static description of a status code. */
+const char* fp4_status_str(fp4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4_H */

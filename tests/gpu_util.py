@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU tests: host<->device marshalling and the
+byte-exact comparison against the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import block_scaled_bit_fp4_amd as fp4
+import oracle
+
+DEV = "cuda:0"
+
+
+def note(msg: str):
+    """Name the case on stderr before a GPU step, so a fault is attributable."""
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_device(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def f32_bits(v: float) -> int:
+    return int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+
+
+def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str):
+    if got.shape != want.shape:
+        raise AssertionError("%s: shape %s vs %s" % (what, got.shape, want.shape))
+    bad = np.argwhere(got != want)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d mismatching entries, first at %s: gpu %r oracle %r"
+                             % (what, len(bad), i, got[i], want[i]))
+
+
+def quantize_both(x: np.ndarray, fmt, axis="row", rounding="rtne", rht=False, rht_seed=0,
+                  sr_seed=0, given=None, poison=0xAA):
+    """Quantize on the GPU (through the C ABI) and in the oracle; compare
+    codes, scales and the tensor scale byte for byte.  Returns the GPU tensors."""
+    xd = to_device(x)
+    rows, cols = x.shape
+    cshape, sshape = fp4.output_shapes(rows, cols, fmt, axis)
+    codes = torch.full(cshape, poison, dtype=torch.uint8, device=DEV)
+    scales = torch.full(sshape, poison, dtype=torch.uint8, device=DEV)
+    c, s, ts = fp4.quantize(xd, fmt, axis, rounding, rht, rht_seed, sr_seed,
+                            tensor_scale=given, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    oc, osc, ots = oracle.quantize(x, fmt, axis, rounding, rht, rht_seed, sr_seed,
+                                   tensor_scale=given)
+    tag = "%s %s %s rht=%s %s %s" % (fmt, axis, rounding, rht, x.dtype, x.shape)
+    assert_bytes_equal(to_host(s), osc, "scales " + tag)
+    assert_bytes_equal(to_host(c), oc, "codes " + tag)
+    if fmt != "mxfp4":
+        assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots), "tensor scale " + tag
+    return c, s, ts, (oc, osc, ots)

@@ -1,0 +1,148 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, byte for
+byte (codes, scale bytes, tensor scale, dequantized values, RHT outputs).
+
+Sizes are small enough for the oracle to finish in well under a second, yet
+span many workgroups and leave ragged tails; the data kinds cover heavy
+tails, outlier channels, wide dynamic range, subnormals, zeros and exact
+rounding ties."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_fp4_amd as fp4
+import oracle
+import workloads
+from tests.gpu_util import (DEV, assert_bytes_equal, f32_bits, note, quantize_both, to_device,
+                            to_host)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352)]
+KINDS = workloads.SMALL_KINDS
+
+COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4"], ["row", "col"], ["rtne", "sr"],
+                                [False, True], ["bf16", "f32"]))
+
+
+def _input(kind, shape, seed, dtype):
+    a = workloads.small_case(kind, shape[0], shape[1], seed)
+    return workloads.to_bf16_bits(a) if dtype == "bf16" else a
+
+
+@pytest.mark.parametrize("fmt,axis,rounding,rht,dtype", COMBOS,
+                         ids=["-".join(map(str, c)) for c in COMBOS])
+def test_quantize_dequantize_parity(fmt, axis, rounding, rht, dtype):
+    for i, shape in enumerate(SHAPES):
+        kind = KINDS[(i + len(fmt) + (3 if rht else 0) + (1 if axis == "col" else 0)) % len(KINDS)]
+        x = _input(kind, shape, 100 + i, dtype)
+        note("parity %s %s %s rht=%s %s %s %s" % (fmt, axis, rounding, rht, dtype, shape, kind))
+        c, s, ts, (oc, osc, ots) = quantize_both(x, fmt, axis, rounding, rht, 3, 5 + i)
+        rows, cols = shape
+        for inv in ([False, True] if rht else [False]):
+            for odt in (torch.float32, torch.bfloat16):
+                out = fp4.dequantize(c, s, ts, rows, cols, fmt, axis, rht, 3, inv, odt)
+                torch.cuda.synchronize()
+                want = oracle.dequantize(oc, osc, ots, rows, cols, fmt, axis, rht, 3, inv,
+                                         "f32" if odt == torch.float32 else "bf16")
+                got = to_host(out)
+                if odt == torch.float32:
+                    got, want = got.view(np.uint32), want.view(np.uint32)
+                assert_bytes_equal(got, want, "dequant inv=%s %s %s" % (inv, odt, shape))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_every_kind_nvfp4_rht(kind):
+    for rounding in ("rtne", "sr"):
+        x = _input(kind, (320, 256), 7, "bf16")
+        note("kind %s %s" % (kind, rounding))
+        quantize_both(x, "nvfp4", "row", rounding, True, 1, 1)
+        quantize_both(x, "ufp4", "col", rounding, True, 1, 1)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4"])
+def test_given_tensor_scale(fmt):
+    x = _input("t3", (128, 256), 3, "bf16")
+    for ts in (1e-3, 2.0 ** -20, 0.37, 1e4, 0.0):
+        note("given ts %s %g" % (fmt, ts))
+        quantize_both(x, fmt, "row", "rtne", True, 0, 0, given=ts)
+        quantize_both(x, fmt, "col", "sr", False, 0, 9, given=ts)
+
+
+def test_poison_and_determinism():
+    x = _input("outlier_cols", (512, 512), 1, "bf16")
+    for fmt in ("nvfp4", "mxfp4"):
+        note("poison %s" % fmt)
+        a = quantize_both(x, fmt, "col", "sr", True, 2, 3, poison=0xAA)
+        b = quantize_both(x, fmt, "col", "sr", True, 2, 3, poison=0x55)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_col_equals_row_of_transpose_on_gpu():
+    x = _input("t3", (256, 160), 4, "bf16")
+    xt = np.ascontiguousarray(x.T)
+    for fmt in ("nvfp4", "mxfp4", "ufp4"):
+        note("transpose %s" % fmt)
+        c1, s1, t1 = fp4.quantize(to_device(x), fmt, "col", "sr", True, 6, 8)
+        c2, s2, t2 = fp4.quantize(to_device(xt), fmt, "row", "sr", True, 6, 8)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2) and torch.equal(s1, s2)
+        if t1 is not None:
+            assert torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rht_parity(axis, dtype):
+    for kind, shape in (("t3", (64, 48)), ("wide_range", (208, 352)), ("tiny", (32, 32))):
+        x = _input(kind, shape, 2, dtype)
+        for inv in (False, True):
+            note("rht %s %s %s inv=%s" % (axis, dtype, shape, inv))
+            y = fp4.rht(to_device(x), axis, 11, inv)
+            torch.cuda.synchronize()
+            want = oracle.rht(x, axis, 11, inv)
+            assert_bytes_equal(to_host(y).view(np.uint32), want.view(np.uint32), "rht")
+
+
+def test_strided_input():
+    base = workloads.to_bf16_bits(workloads.small_case("normal", 64, 96, 5))
+    note("strided")
+    xd = to_device(base)[:, :64]
+    assert xd.stride(0) == 96
+    c, s, ts = fp4.quantize(xd, "nvfp4", "row", "rtne", True, 0, 0)
+    torch.cuda.synchronize()
+    oc, osc, ots = oracle.quantize(np.ascontiguousarray(base[:, :64]), "nvfp4", "row", "rtne",
+                                   True, 0, 0)
+    assert_bytes_equal(to_host(c), oc, "codes")
+    assert_bytes_equal(to_host(s), osc, "scales")
+
+
+def test_empty_and_single_block():
+    note("empty")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    c, s, ts = fp4.quantize(x, "nvfp4")
+    torch.cuda.synchronize()
+    assert c.numel() == 0 and float(ts.item()) == 0.0
+    x1 = _input("normal", (1, 16), 0, "bf16")
+    note("single block")
+    quantize_both(x1, "nvfp4", "row", "sr", True, 0, 4)
+    x2 = _input("normal", (32, 1), 0, "f32")
+    with pytest.raises(fp4.FP4Error):
+        fp4.quantize(to_device(x2), "nvfp4", "row")  # W = 1
+
+
+def test_all_zero_tensor():
+    x = np.zeros((64, 64), dtype=np.float32)
+    x[3, 5] = -0.0
+    for fmt in ("nvfp4", "mxfp4", "ufp4"):
+        note("zeros %s" % fmt)
+        quantize_both(x, fmt, "row", "sr", True, 0, 0)
+        quantize_both(x, fmt, "col", "rtne", False, 0, 0)
+
+
+def test_error_statuses_through_binding():
+    x = to_device(_input("normal", (32, 48), 0, "bf16"))
+    with pytest.raises(fp4.FP4Error) as e:
+        fp4.quantize(x, "mxfp4")  # 48 % 32
+    assert e.value.status == -3
