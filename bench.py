@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
-KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_kernels.hip",
+KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_quantize.hip", "block_scaled_bit_fp4_amd/csrc/fp4_tiles.h",
                   "block_scaled_bit_fp4_amd/csrc/fp4_device.h"]
 
 

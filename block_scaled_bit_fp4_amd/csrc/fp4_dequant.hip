@@ -1,0 +1,216 @@
+// fp4_dequant.hip -- gfx950 kernels of the dequantize and standalone-RHT
+// paths and their launchers.
+//
+// Dequantize rebuilds each element as sign * L[k] * d with d the decoded
+// block scale (one binary32 product), optionally undoes the RHT in
+// registers, and writes x's layout (row axis: the A-row is a row of x;
+// column axis: lanes on consecutive columns, so each store of a wave is one
+// contiguous segment of a row).
+#include "fp4_device.h"
+#include "fp4_launch.h"
+#include "fp4_tiles.h"
+
+using namespace fp4dev;
+
+namespace {
+
+// Group g (16 elements) of A-row ra: row axis reads 16 contiguous elements,
+// column axis 16 rows of one column.
+template <int AXIS, typename T>
+__device__ __forceinline__ void load_group(const T* x, int64_t ld, int64_t ra, int64_t col0,
+                                           float (&t)[16]) {
+  if (AXIS == 0) {
+    RowRaw<T, 16> r;
+    r.load(x + ra * ld + col0);
+    r.group(0, t);
+  } else {
+    ColRaw<T, 1> c;
+    c.load(x + col0 * ld + ra, ld);
+    c.column(0, t);
+  }
+}
+
+__global__ void write_scalar_kernel(float* p, float v) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = v;
+}
+
+// ----------------------------------------------------------- dequantize
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+  int64_t ld_out, W;
+  int64_t n_major, M, sq, sr;
+  uint32_t signs;
+};
+
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+    *p = (uint16_t)((u >> 16) | 0x0040u);
+    return;
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  *p = (uint16_t)(u >> 16);
+}
+
+template <int FMT, bool INV, int AXIS, typename T>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ out, DequantArgs a) {
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  const float s_t = FMT == kMXFP4 ? 0.0f : a.ts[0];
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
+  while (w.major < a.n_major) {
+    const int64_t ra = AXIS == 0 ? w.major : w.minor;
+    const int64_t b = AXIS == 0 ? w.minor : w.major;
+    const uint32_t S = a.scales[ra * (a.W / B) + b];
+    float d;
+    if constexpr (FMT == kMXFP4) d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
+    else d = S ? s_t * e4m3_decode(S) : 0.0f;
+    const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
+    uint32_t words[B / 8];
+    if constexpr (B == 16) {
+      const uint2 v = *reinterpret_cast<const uint2*>(cp);
+      words[0] = v.x; words[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(cp);
+      words[0] = v.x; words[1] = v.y; words[2] = v.z; words[3] = v.w;
+    }
+#pragma unroll
+    for (int h = 0; h < B / 16; ++h) {
+      float t[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
+        const float mag = grid_level<FMT>(c & 7u) * d;
+        t[j] = (c & 8u) ? -mag : mag;
+      }
+      if (INV) rht16_inverse(t, a.signs);
+      const int64_t j0 = b * B + h * 16;
+      if (AXIS == 0 && sizeof(T) == 4) {
+        float4* o = reinterpret_cast<float4*>(out + ra * a.ld_out + j0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = make_float4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          T* p = AXIS == 0 ? out + ra * a.ld_out + j0 + j : out + (j0 + j) * a.ld_out + ra;
+          store_elem(p, t[j]);
+        }
+      }
+    }
+    w.advance(a.sq, a.sr, a.M);
+  }
+}
+
+// ------------------------------------------------------------ standalone RHT
+template <bool INV, int AXIS, typename T>
+__global__ __launch_bounds__(kThreads) void rht_kernel(const T* __restrict__ x, int64_t ld,
+                                                       int64_t cols, int64_t n_major, int64_t M,
+                                                       int64_t sq, int64_t sr, uint32_t signs,
+                                                       float* __restrict__ y) {
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, M);
+  while (w.major < n_major) {
+    const int64_t ra = AXIS == 0 ? w.major : w.minor;
+    const int64_t g = AXIS == 0 ? w.minor : w.major;
+    float t[16];
+    load_group<AXIS>(x, ld, ra, g * 16, t);
+    if (INV) rht16_inverse(t, signs);
+    else rht16_forward(t, signs);
+    if (AXIS == 0) {
+      float4* o = reinterpret_cast<float4*>(y + ra * cols + g * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = make_float4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) y[(g * 16 + j) * cols + ra] = t[j];
+    }
+    w.advance(sq, sr, M);
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+constexpr int64_t kMaxGrid = 8192;
+
+struct WalkPlan {
+  unsigned grid;
+  int64_t sq, sr;
+};
+inline WalkPlan plan_walk(int64_t n_major, int64_t M, int64_t cap) {
+  const int64_t units = n_major * M;
+  int64_t g = (units + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  const int64_t stride = g * kThreads;
+  return {(unsigned)g, stride / M, stride % M};
+}
+
+template <int FMT, bool INV, int AXIS, typename T>
+hipError_t launch_dequant_t(const DequantLaunch& q, hipStream_t s) {
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  const int64_t W = AXIS == 0 ? q.cols : q.rows;
+  const int64_t RA = AXIS == 0 ? q.rows : q.cols;
+  const int64_t nmaj = AXIS == 0 ? RA : W / B;
+  const int64_t M = AXIS == 0 ? W / B : RA;
+  const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
+  DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, nmaj, M, wp.sq, wp.sr, q.signs};
+  hipLaunchKernelGGL((dequantize_kernel<FMT, INV, AXIS, T>), dim3(wp.grid), dim3(kThreads), 0, s,
+                     static_cast<T*>(q.out), a);
+  return hipGetLastError();
+}
+template <int FMT, bool INV, int AXIS>
+hipError_t dq_dtype(const DequantLaunch& q, hipStream_t s) {
+  return q.out_dtype == 0 ? launch_dequant_t<FMT, INV, AXIS, uint16_t>(q, s)
+                          : launch_dequant_t<FMT, INV, AXIS, float>(q, s);
+}
+template <int FMT, bool INV>
+hipError_t dq_axis(const DequantLaunch& q, hipStream_t s) {
+  return q.axis == 0 ? dq_dtype<FMT, INV, 0>(q, s) : dq_dtype<FMT, INV, 1>(q, s);
+}
+template <int FMT>
+hipError_t dq_inv(const DequantLaunch& q, hipStream_t s) {
+  return q.inverse_rht ? dq_axis<FMT, true>(q, s) : dq_axis<FMT, false>(q, s);
+}
+
+template <bool INV, int AXIS, typename T>
+hipError_t launch_rht_t(const RhtLaunch& q, hipStream_t s) {
+  const int64_t W = AXIS == 0 ? q.cols : q.rows;
+  const int64_t RA = AXIS == 0 ? q.rows : q.cols;
+  const int64_t nmaj = AXIS == 0 ? RA : W / 16;
+  const int64_t M = AXIS == 0 ? W / 16 : RA;
+  const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
+  hipLaunchKernelGGL((rht_kernel<INV, AXIS, T>), dim3(wp.grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(q.x), q.ld, q.cols, nmaj, M, wp.sq, wp.sr, q.signs,
+                     q.y);
+  return hipGetLastError();
+}
+template <bool INV, int AXIS>
+hipError_t rht_dtype(const RhtLaunch& q, hipStream_t s) {
+  return q.in_dtype == 0 ? launch_rht_t<INV, AXIS, uint16_t>(q, s)
+                         : launch_rht_t<INV, AXIS, float>(q, s);
+}
+template <bool INV>
+hipError_t rht_axis(const RhtLaunch& q, hipStream_t s) {
+  return q.axis == 0 ? rht_dtype<INV, 0>(q, s) : rht_dtype<INV, 1>(q, s);
+}
+
+}  // namespace
+
+hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
+  switch (q.format) {
+    case kNVFP4: return dq_inv<kNVFP4>(q, s);
+    case kMXFP4: return dq_inv<kMXFP4>(q, s);
+    default: return dq_inv<kUFP4>(q, s);
+  }
+}
+
+hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s) {
+  return q.inverse ? rht_axis<true>(q, s) : rht_axis<false>(q, s);
+}
+
+hipError_t fp4_launch_write_scalar(float* p, float v, hipStream_t s) {
+  hipLaunchKernelGGL(write_scalar_kernel, dim3(1), dim3(64), 0, s, p, v);
+  return hipGetLastError();
+}

@@ -1,0 +1,673 @@
+// fp4_quantize.hip -- gfx950 kernels of the quantize path and its launcher.
+//
+// Terms: x is the caller's rows x cols tensor (row-major, leading dimension
+// ld).  The logical operand A is x (row axis) or x^T (column axis); W is the
+// length of A's rows, B the block size (16 or 32).  Codes are A-row-major,
+// two per byte (even column in the low nibble); scales are one byte per
+// block, A-row-major.  SR draws are keyed on the logical A coordinate, so
+// every tiling gives the same bytes.
+//
+// Two-level formats (NVFP4, uniform grid) need the tensor amax of the
+// rotated operand before any block can be coded: a first kernel writes one
+// partial maximum per workgroup, and every workgroup of the quantize kernel
+// reduces them.  MXFP4 and a given tensor scale skip that pass.
+//
+// Row axis: a lane owns a 32-element (or 16-element) piece of an A-row,
+// read with 16-byte loads; the next piece's loads are issued before the
+// current piece is coded.  Column axis: a lane owns C adjacent columns of x
+// (A-rows) and a run of NB consecutive blocks down them; each row of a
+// block is one 2C- or 4C-byte load, so a wave reads one contiguous segment
+// per row, and each lane writes NB*B/2 contiguous code bytes per column.
+#include <type_traits>
+
+#include "fp4_device.h"
+#include "fp4_launch.h"
+#include "fp4_tiles.h"
+
+using namespace fp4dev;
+
+namespace {
+
+// ------------------------------------------------------------ tensor amax
+// Partial maxima of |A| or, with the RHT, of |H16 D a| before the exact
+// scaling by 1/4 (monotone, so it is applied once to each partial).
+template <bool RHT, typename T>
+__global__ __launch_bounds__(kThreads) void amax_row_kernel(
+    const T* __restrict__ x, int64_t ld, int64_t n_major, int64_t M, int64_t sq, int64_t sr,
+    uint32_t signs, float* __restrict__ partials) {
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, M);
+  float m = 0.0f;
+  while (w.major < n_major) {
+    RowRaw<T, 16> raw;
+    raw.load(x + w.major * ld + w.minor * 16);
+    float t[16];
+    raw.group(0, t);
+    if (RHT) { apply_signs(t, signs); fwht16(t); }
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+    w.advance(sq, sr, M);
+  }
+  m = block_max_256(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = RHT ? m * 0.25f : m;
+}
+
+// Column axis: units are (16-row group, C-column group), column group fastest.
+template <bool RHT, typename T, int C>
+__global__ __launch_bounds__(kThreads) void amax_col_kernel(
+    const T* __restrict__ x, int64_t ld, int64_t n_major, int64_t M, int64_t sq, int64_t sr,
+    uint32_t signs, float* __restrict__ partials) {
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, M);
+  float m = 0.0f;
+  while (w.major < n_major) {
+    ColRaw<T, C> raw;
+    raw.load(x + w.major * 16 * ld + w.minor * C, ld);
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      float t[16];
+      raw.column(k, t);
+      if (RHT) { apply_signs(t, signs); fwht16(t); }
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+    }
+    w.advance(sq, sr, M);
+  }
+  m = block_max_256(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = RHT ? m * 0.25f : m;
+}
+
+// ---------------------------------------------------------- quantize core
+struct QuantArgs {
+  int64_t ld, W;
+  int64_t n_major, M, sq, sr;  // unit walk
+  int64_t nblk_axis;           // column axis: blocks down the rows (W / B)
+  int64_t blk_begin, blk_end;  // column axis: row-block range of this launch
+  int64_t col_begin;           // column axis: first column of this launch
+  uint8_t* codes;
+  uint8_t* scales;
+  const float* ts_in;      // given tensor scale (GIVEN mode)
+  float* ts_out;           // computed tensor scale (COMPUTE mode)
+  const float* partials;   // amax partials (COMPUTE mode)
+  int npartials;
+  uint32_t signs;
+  uint32_t sr_k0, sr_k1;
+};
+
+// Per-workgroup constants of the two-level scale.
+struct ScaleCtx {
+  float s_t, den;
+};
+
+// Tensor scale s_t = amax / (G * 448) and, in LDS, the reciprocal of every
+// decoded block scale: inv[S] = 1 / (s_t * decode(S)), 0 where that is 0.
+template <int FMT, bool GIVEN>
+__device__ __forceinline__ ScaleCtx scale_prologue(const QuantArgs& a, float* inv_tab) {
+  ScaleCtx c{0.0f, 0.0f};
+  if constexpr (FMT != kMXFP4) {
+    if (GIVEN) {
+      c.s_t = a.ts_in[0];
+    } else {
+      float m = 0.0f;
+      for (int i = threadIdx.x; i < a.npartials; i += kThreads) m = fmaxf(m, a.partials[i]);
+      m = block_max_256(m);
+      c.s_t = m / (grid_max<FMT>() * 448.0f);
+      if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
+    }
+    c.den = c.s_t * grid_max<FMT>();
+    if (threadIdx.x < 128) {
+      const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
+      const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
+      inv_tab[threadIdx.x] = d != 0.0f ? 1.0f / d : 0.0f;
+    }
+    __syncthreads();
+  }
+  return c;
+}
+
+// Encode 8 scaled values (all finite) into one word of 4-bit codes.
+template <int FMT, bool SR>
+__device__ __forceinline__ uint32_t encode8_fast(const float* v, const uint32_t (&r)[4]) {
+  uint32_t word = 0;
+  if constexpr (FMT != kUFP4 && !SR) {
+    // E2M1 round-to-nearest-even in hardware: two values per instruction,
+    // sign and saturation included; scale operand 1.0 (no rescaling).
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
+  } else {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const float m = fabsf(v[l]);
+      uint32_t k;
+      if constexpr (SR) k = round_sr_sw<FMT>(m, (r[l >> 1] >> (16 * (l & 1))) & 0xFFFFu);
+      else k = round_rtne_sw<FMT>(m);
+      word |= (((__float_as_uint(v[l]) >> 28) & 8u) | k) << (4 * l);
+    }
+  }
+  return word;
+}
+
+// Per-element path for blocks whose reciprocal scale, or its product with
+// the block amax, is not finite: zero elements code as signed zeros and the
+// rest follow v = y * inv exactly as in the scalar definition.
+template <int FMT, bool SR>
+__device__ __forceinline__ uint32_t encode8_careful(const float* y, float inv,
+                                                    const uint32_t (&r)[4]) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    const float yi = y[l];
+    uint32_t k = 0;
+    if (yi != 0.0f) {
+      const float m = fabsf(yi * inv);
+      if constexpr (SR) k = round_sr_sw<FMT>(m, (r[l >> 1] >> (16 * (l & 1))) & 0xFFFFu);
+      else k = round_rtne_sw<FMT>(m);
+    }
+    word |= (((__float_as_uint(yi) >> 28) & 8u) | k) << (4 * l);
+  }
+  return word;
+}
+
+// Code one block.  t[] holds the rotated values before the 1/4 (RHT) or the
+// plain values, amax_t their largest magnitude, n0 the logical index of the
+// first element (SR draws).
+// Two-level formats ([TJ2] 2.A; [NGPT] per-tensor dynamic scaling):
+//   r = amax_b / (s_t * G), S = E4M3(r), d = s_t * decode(S), v = y * (1/d).
+// MXFP4 ([MXFP4] 2): d = 2^e, e = floor(log2 amax_b) - 2.
+// With BF16 input every RHT partial sum is a multiple of 2^-133, so y = t/4
+// is exact and, while inv >= 2^-124, v = t * (inv / 4) equals y * inv.
+template <int FMT, bool SR, bool RHT, bool BF16IN, int B>
+__device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, const ScaleCtx& c,
+                                             const float* inv_tab, uint32_t k0, uint32_t k1,
+                                             uint64_t n0, uint32_t (&packed)[B / 8],
+                                             uint32_t& sbyte) {
+  constexpr bool kFold = RHT && BF16IN;
+  const float amax_b = RHT ? amax_t * 0.25f : amax_t;
+  float inv;
+  if constexpr (FMT == kMXFP4) {
+    const int e = e8m0_exponent(amax_b);
+    sbyte = (uint32_t)(e + 127);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+  } else {
+    sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
+    inv = inv_tab[sbyte];
+  }
+  float mul;
+  bool fast;
+  if constexpr (kFold) {
+    mul = inv * 0.25f;
+    fast = inv >= 4.70197740328915e-38f && amax_t * mul < __builtin_inff();
+  } else {
+    mul = inv;
+    fast = amax_b * inv < __builtin_inff();
+  }
+#pragma unroll
+  for (int q = 0; q < B / 8; ++q) {
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+    if constexpr (SR) {
+      const uint64_t g = (n0 >> 3) + (uint64_t)q;
+      const u32x4 o = philox4x32_10(k0, k1, (uint32_t)g, (uint32_t)(g >> 32), 0u, 0u);
+      r[0] = o.x; r[1] = o.y; r[2] = o.z; r[3] = o.w;
+    }
+    const float* tq = t + 8 * q;
+    if (fast) {
+      float v[8];
+#pragma unroll
+      for (int l = 0; l < 8; ++l) v[l] = ((RHT && !kFold) ? tq[l] * 0.25f : tq[l]) * mul;
+      packed[q] = encode8_fast<FMT, SR>(v, r);
+    } else {
+      float y[8];
+#pragma unroll
+      for (int l = 0; l < 8; ++l) y[l] = RHT ? tq[l] * 0.25f : tq[l];
+      packed[q] = encode8_careful<FMT, SR>(y, inv, r);
+    }
+  }
+}
+
+// ------------------------------------------------------------- row axis
+// Units: major = A-row, minor = piece of U elements within it.
+template <int FMT, bool SR, bool RHT, bool GIVEN, typename T, int U>
+__global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restrict__ x,
+                                                                QuantArgs a) {
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int NBU = U / B;  // blocks per unit
+  __shared__ float inv_tab[128];
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
+  RowRaw<T, U> cur;
+  bool have = w.major < a.n_major;
+  if (have) cur.load(x + w.major * a.ld + w.minor * U);  // in flight during the prologue
+  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  while (have) {
+    Walk nw = w;
+    nw.advance(a.sq, a.sr, a.M);
+    const bool have_next = nw.major < a.n_major;
+    RowRaw<T, U> nxt;
+    if (have_next) nxt.load(x + nw.major * a.ld + nw.minor * U);
+
+    uint32_t packed[U / 8];
+    uint32_t sb[NBU];
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) {
+      float t[B];
+      float amax_t = 0.0f;
+#pragma unroll
+      for (int h = 0; h < B / 16; ++h) {
+        float g[16];
+        cur.group(bi * (B / 16) + h, g);
+        if (RHT) { apply_signs(g, a.signs); fwht16(g); }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          t[16 * h + j] = g[j];
+          amax_t = fmaxf(amax_t, fabsf(g[j]));
+        }
+      }
+      const uint64_t n0 = (uint64_t)w.major * (uint64_t)a.W + (uint64_t)(w.minor * U + bi * B);
+      uint32_t pk[B / 8];
+      encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1, n0,
+                                                     pk, sb[bi]);
+#pragma unroll
+      for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
+    }
+    uint8_t* cp = a.codes + w.major * (a.W / 2) + w.minor * (U / 2);
+    if constexpr (U >= 32) {
+#pragma unroll
+      for (int i = 0; i < U / 32; ++i)
+        reinterpret_cast<uint4*>(cp)[i] =
+            make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+    } else {
+      *reinterpret_cast<uint2*>(cp) = make_uint2(packed[0], packed[1]);
+    }
+    uint8_t* sp = a.scales + w.major * (a.W / B) + w.minor * NBU;
+    if constexpr (NBU == 4)
+      *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+    else if constexpr (NBU == 2)
+      *reinterpret_cast<uint16_t*>(sp) = (uint16_t)(sb[0] | (sb[1] << 8));
+    else
+      sp[0] = (uint8_t)sb[0];
+
+    cur = nxt;
+    w = nw;
+    have = have_next;
+  }
+}
+
+
+// ---------------------------------------------------------- column axis
+// Units: major = run of NB blocks down the rows, minor = group of C columns.
+template <int FMT, bool SR, bool RHT, bool GIVEN, typename T, int C, int NB>
+__global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restrict__ x,
+                                                                QuantArgs a) {
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int WPB = B / 8;  // code words per block
+  __shared__ float inv_tab[128];
+  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  const bool vec_codes = (a.W % 32) == 0;  // 16-byte aligned A-rows of codes
+
+  Walk w;
+  w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
+  while (w.major < a.n_major) {
+    const int64_t col = a.col_begin + w.minor * C;
+    const int64_t blk0 = a.blk_begin + w.major * NB;
+    const int nb = (int)min((int64_t)NB, a.blk_end - blk0);
+    uint32_t codes[C][NB * WPB];
+    uint32_t sbw[C][(NB + 3) / 4];  // scale bytes, four per word
+#pragma unroll
+    for (int k = 0; k < C; ++k)
+#pragma unroll
+      for (int i = 0; i < (NB + 3) / 4; ++i) sbw[k][i] = 0u;
+    const T* base = x + blk0 * B * a.ld + col;
+    ColRaw<T, C> cur[B / 16];
+#pragma unroll
+    for (int h = 0; h < B / 16; ++h) cur[h].load(base + (int64_t)h * 16 * a.ld, a.ld);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j < nb) {
+        ColRaw<T, C> nxt[B / 16];
+        if (j + 1 < nb) {
+#pragma unroll
+          for (int h = 0; h < B / 16; ++h)
+            nxt[h].load(base + ((int64_t)(j + 1) * B + h * 16) * a.ld, a.ld);
+        }
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+          float t[B];
+          float amax_t = 0.0f;
+#pragma unroll
+          for (int h = 0; h < B / 16; ++h) {
+            float g[16];
+            cur[h].column(k, g);
+            if (RHT) { apply_signs(g, a.signs); fwht16(g); }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              t[16 * h + i] = g[i];
+              amax_t = fmaxf(amax_t, fabsf(g[i]));
+            }
+          }
+          const uint64_t n0 = (uint64_t)(col + k) * (uint64_t)a.W + (uint64_t)((blk0 + j) * B);
+          uint32_t pk[WPB];
+          uint32_t sbyte;
+          encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1,
+                                                         n0, pk, sbyte);
+          sbw[k][j / 4] |= sbyte << (8 * (j % 4));
+#pragma unroll
+          for (int q = 0; q < WPB; ++q) codes[k][j * WPB + q] = pk[q];
+        }
+#pragma unroll
+        for (int h = 0; h < B / 16; ++h) cur[h] = nxt[h];
+      }
+    }
+    // stores: NB*B/2 contiguous code bytes and NB scale bytes per column
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      uint8_t* cp = a.codes + (col + k) * (a.W / 2) + blk0 * (B / 2);
+      uint8_t* sp = a.scales + (col + k) * a.nblk_axis + blk0;
+      if (nb == NB && vec_codes) {
+#pragma unroll
+        for (int q = 0; q < NB * WPB; q += 4)
+          *reinterpret_cast<uint4*>(cp + 4 * q) =
+              make_uint4(codes[k][q], codes[k][q + 1], codes[k][q + 2], codes[k][q + 3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (j < nb) {
+#pragma unroll
+            for (int q = 0; q < WPB; q += 2)
+              *reinterpret_cast<uint2*>(cp + 4 * (j * WPB + q)) =
+                  make_uint2(codes[k][j * WPB + q], codes[k][j * WPB + q + 1]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (j < nb) sp[j] = (uint8_t)(sbw[k][j / 4] >> (8 * (j % 4)));
+    }
+    w.advance(a.sq, a.sr, a.M);
+  }
+}
+
+
+// Column axis, interior tiles: TR x-rows by TC x-columns (TC * sizeof(T) =
+// 128 bytes), staged through LDS.  Every global load is a 16-byte piece of a
+// row (8 lanes read one 128-byte row segment); the tile is written to LDS
+// transposed (A-row-major, packed row pairs for BF16) with an odd word pitch,
+// so the scattered 4-byte writes and reads fall on distinct banks; each lane
+// then codes whole blocks of one A-row, and the lanes of one A-row write its
+// TR/2 code bytes as one contiguous run.
+template <typename T>
+struct ColTile {
+  static constexpr int TR = 256;                        // rows per tile
+  static constexpr int TC = 128 / (int)sizeof(T);       // columns per tile
+  static constexpr int EPW = 4 / (int)sizeof(T);        // elements per LDS word
+  static constexpr int P = TR / EPW + 1;                // LDS words per A-row (odd)
+  static constexpr int kWords = TC * P;
+};
+
+template <int FMT, bool SR, bool RHT, bool GIVEN, typename T>
+__global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __restrict__ x,
+                                                                     QuantArgs a) {
+  using Tile = ColTile<T>;
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int TR = Tile::TR, TC = Tile::TC, P = Tile::P, EPW = Tile::EPW;
+  constexpr int kLoads = TR * TC * (int)sizeof(T) / 16 / kThreads;  // 16-byte loads per lane
+  constexpr int kUnits = TC * (TR / B) / kThreads;                  // blocks coded per lane
+  __shared__ float inv_tab[128];
+  __shared__ uint32_t lds[Tile::kWords];
+  ScaleCtx c{0.0f, 0.0f};
+  bool first = true;
+
+  // a.n_major row tiles x a.M column tiles, column tile fastest
+  for (int64_t tile = blockIdx.x; tile < a.n_major * a.M; tile += gridDim.x) {
+    const int64_t tr = tile / a.M, tc = tile - tr * a.M;
+    const int64_t r0 = tr * TR, c0 = tc * TC;
+    // ---- global -> registers (all loads in flight), then -> LDS transposed
+    // load i: segment threadIdx % 8 of row tile_row(i); for BF16, loads i and
+    // i + kLoads/2 are the two rows of one pair
+    uint4 buf[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      int row;
+      if constexpr (sizeof(T) == 2)
+        row = 2 * ((threadIdx.x >> 3) + 32 * (i % (kLoads / 2))) + (i >= kLoads / 2 ? 1 : 0);
+      else
+        row = (threadIdx.x >> 3) + 32 * i;
+      const int seg = threadIdx.x & 7;
+      buf[i] = *reinterpret_cast<const uint4*>(x + (r0 + row) * a.ld + c0 +
+                                               seg * (16 / (int)sizeof(T)));
+    }
+    if (first) {  // the first tile's loads are in flight during the prologue
+      c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+      first = false;
+    }
+    __syncthreads();  // previous tile's LDS reads are done
+    if constexpr (sizeof(T) == 2) {
+      // rows are processed in pairs: load i and i + kLoads/2 hold rows 2p and 2p+1
+#pragma unroll
+      for (int i = 0; i < kLoads / 2; ++i) {
+        const int pr = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;  // row pair, segment
+        const uint4 e = buf[i], o = buf[i + kLoads / 2];
+        const uint32_t ev[4] = {e.x, e.y, e.z, e.w}, od[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int col = seg * 8 + 2 * k;
+          lds[col * P + pr] = (ev[k] & 0xFFFFu) | (od[k] << 16);
+          lds[(col + 1) * P + pr] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int row = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;
+        const uint32_t v[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lds[(seg * 4 + k) * P + row] = v[k];
+      }
+    }
+    __syncthreads();
+    // ---- code blocks: unit u -> (A-row cl, block j), block fastest
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int u = threadIdx.x + i * kThreads;
+      const int cl = u / (TR / B), j = u % (TR / B);
+      float t[B];
+      float amax_t = 0.0f;
+#pragma unroll
+      for (int h = 0; h < B / 16; ++h) {
+        float g[16];
+        const uint32_t* src = lds + cl * P + (j * B + h * 16) / EPW;
+#pragma unroll
+        for (int e = 0; e < 16 / EPW; ++e) {
+          const uint32_t wv = src[e];
+          if constexpr (sizeof(T) == 2) {
+            g[2 * e] = bf16_lo(wv);
+            g[2 * e + 1] = bf16_hi(wv);
+          } else {
+            g[e] = __uint_as_float(wv);
+          }
+        }
+        if (RHT) { apply_signs(g, a.signs); fwht16(g); }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          t[16 * h + e] = g[e];
+          amax_t = fmaxf(amax_t, fabsf(g[e]));
+        }
+      }
+      const int64_t ra = c0 + cl;                 // A-row = column of x
+      const int64_t rb = r0 / B + j;              // block index along the A-row
+      const uint64_t n0 = (uint64_t)ra * (uint64_t)a.W + (uint64_t)(rb * B);
+      uint32_t pk[B / 8];
+      uint32_t sbyte;
+      encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1, n0,
+                                                     pk, sbyte);
+      uint8_t* cp = a.codes + ra * (a.W / 2) + rb * (B / 2);
+      if constexpr (B == 16) *reinterpret_cast<uint2*>(cp) = make_uint2(pk[0], pk[1]);
+      else *reinterpret_cast<uint4*>(cp) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      a.scales[ra * a.nblk_axis + rb] = (uint8_t)sbyte;
+    }
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+// Launch geometry (measured on MI355X; overridable at build time for sweeps).
+#ifndef FP4_ROW_GRID
+#define FP4_ROW_GRID 2048
+#endif
+#ifndef FP4_COL_GRID
+#define FP4_COL_GRID 4096
+#endif
+#ifndef FP4_COL_BLOCKS
+#define FP4_COL_BLOCKS 8
+#endif
+#ifndef FP4_ROW_UNIT
+#define FP4_ROW_UNIT 32
+#endif
+#ifndef FP4_COL_PAIR
+#define FP4_COL_PAIR 1
+#endif
+constexpr int64_t kRowGrid = FP4_ROW_GRID;  // workgroups of the row kernel (cap)
+constexpr int64_t kColGrid = FP4_COL_GRID;  // workgroups of the column kernel (cap)
+constexpr int kColBlocks = FP4_COL_BLOCKS;  // NB for 16-element blocks (half for 32)
+
+struct WalkPlan {
+  unsigned grid;
+  int64_t sq, sr;
+};
+inline WalkPlan plan_walk(int64_t n_major, int64_t M, int64_t cap) {
+  const int64_t units = n_major * M;
+  int64_t g = (units + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  const int64_t stride = g * kThreads;
+  return {(unsigned)g, stride / M, stride % M};
+}
+
+
+template <bool RHT, typename T>
+void launch_amax(const QuantLaunch& q, hipStream_t s) {
+  const T* x = static_cast<const T*>(q.x);
+  const int64_t stride = (int64_t)kAmaxPartials * kThreads;
+  if (q.axis == 0) {
+    const int64_t nmaj = q.rows, M = q.cols / 16;
+    hipLaunchKernelGGL((amax_row_kernel<RHT, T>), dim3(kAmaxPartials), dim3(kThreads), 0, s, x,
+                       q.ld, nmaj, M, stride / M, stride % M, q.signs, q.workspace);
+  } else if (q.cols % 2 == 0) {
+    const int64_t nmaj = q.rows / 16, M = q.cols / 2;
+    hipLaunchKernelGGL((amax_col_kernel<RHT, T, 2>), dim3(kAmaxPartials), dim3(kThreads), 0, s,
+                       x, q.ld, nmaj, M, stride / M, stride % M, q.signs, q.workspace);
+  } else {
+    const int64_t nmaj = q.rows / 16, M = q.cols;
+    hipLaunchKernelGGL((amax_col_kernel<RHT, T, 1>), dim3(kAmaxPartials), dim3(kThreads), 0, s,
+                       x, q.ld, nmaj, M, stride / M, stride % M, q.signs, q.workspace);
+  }
+}
+
+template <int FMT, bool SR, bool RHT, bool GIVEN, typename T>
+hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
+  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  const T* x = static_cast<const T*>(q.x);
+  if (FMT != kMXFP4 && !GIVEN) launch_amax<RHT, T>(q, s);
+  QuantArgs a{};
+  a.ld = q.ld;
+  a.codes = q.codes;
+  a.scales = q.scales;
+  a.ts_in = q.tensor_scale;
+  a.ts_out = q.tensor_scale;
+  a.partials = q.workspace;
+  a.npartials = kAmaxPartials;
+  a.signs = q.signs;
+  a.sr_k0 = q.sr_k0;
+  a.sr_k1 = q.sr_k1;
+  if (q.axis == 0) {
+    a.W = q.cols;
+    const bool wide = q.cols % 32 == 0;
+    const bool wider = FP4_ROW_UNIT >= 64 && q.cols % 64 == 0;
+    const int U = wider ? 64 : (wide ? 32 : 16);
+    const WalkPlan wp = plan_walk(q.rows, q.cols / U, kRowGrid);
+    a.n_major = q.rows;
+    a.M = q.cols / U;
+    a.sq = wp.sq;
+    a.sr = wp.sr;
+    if (wider)
+      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 64>), dim3(wp.grid),
+                         dim3(kThreads), 0, s, x, a);
+    else if (wide)
+      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 32>), dim3(wp.grid),
+                         dim3(kThreads), 0, s, x, a);
+    else if constexpr (B == 16)
+      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 16>), dim3(wp.grid),
+                         dim3(kThreads), 0, s, x, a);
+  } else {
+    a.W = q.rows;
+    a.nblk_axis = q.rows / B;
+    using Tile = ColTile<T>;
+    // interior: whole tiles; edges (bottom rows, right columns): run kernel
+    const int64_t nrt = q.rows / Tile::TR, nct = q.cols / Tile::TC;
+    const bool tiles = nrt > 0 && nct > 0 && (q.ld * (int64_t)sizeof(T)) % 16 == 0;
+    const int64_t rows_main = tiles ? nrt * Tile::TR : 0;
+    const int64_t cols_main = tiles ? nct * Tile::TC : 0;
+    if (tiles) {
+      QuantArgs t = a;
+      t.n_major = nrt;
+      t.M = nct;
+      const int64_t ntile = nrt * nct;
+      const unsigned grid = (unsigned)(ntile < kColGrid ? ntile : kColGrid);
+      hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, GIVEN, T>), dim3(grid),
+                         dim3(kThreads), 0, s, x, t);
+    }
+    // runs of 128 rows (64 with SR, whose Philox state needs the registers)
+    constexpr int NB = (B == 16 ? kColBlocks : kColBlocks / 2) / (SR ? 2 : 1);
+    auto run = [&](int64_t blk_begin, int64_t blk_end, int64_t col_begin, int64_t col_end) {
+      if (blk_end <= blk_begin || col_end <= col_begin) return;
+      QuantArgs r = a;
+      r.blk_begin = blk_begin;
+      r.blk_end = blk_end;
+      r.col_begin = col_begin;
+      r.n_major = (blk_end - blk_begin + NB - 1) / NB;
+      const int C = (FP4_COL_PAIR && (col_end - col_begin) % 2 == 0) ? 2 : 1;
+      r.M = (col_end - col_begin) / C;
+      const WalkPlan wp = plan_walk(r.n_major, r.M, kColGrid);
+      r.sq = wp.sq;
+      r.sr = wp.sr;
+      if (C == 2)
+        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, GIVEN, T, 2, NB>), dim3(wp.grid),
+                           dim3(kThreads), 0, s, x, r);
+      else
+        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, GIVEN, T, 1, NB>), dim3(wp.grid),
+                           dim3(kThreads), 0, s, x, r);
+    };
+    // right strip over the tiled rows, then the bottom strip over all columns
+    run(0, rows_main / B, cols_main, q.cols);
+    run(rows_main / B, a.nblk_axis, 0, q.cols);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, bool SR, bool RHT, bool GIVEN>
+hipError_t pick_dtype(const QuantLaunch& q, hipStream_t s) {
+  return q.in_dtype == 0 ? launch_quantize_t<FMT, SR, RHT, GIVEN, uint16_t>(q, s)
+                         : launch_quantize_t<FMT, SR, RHT, GIVEN, float>(q, s);
+}
+template <int FMT, bool SR, bool RHT>
+hipError_t pick_given(const QuantLaunch& q, hipStream_t s) {
+  return q.ts_given ? pick_dtype<FMT, SR, RHT, true>(q, s) : pick_dtype<FMT, SR, RHT, false>(q, s);
+}
+template <int FMT, bool SR>
+hipError_t pick_rht(const QuantLaunch& q, hipStream_t s) {
+  return q.rht ? pick_given<FMT, SR, true>(q, s) : pick_given<FMT, SR, false>(q, s);
+}
+template <int FMT>
+hipError_t pick_sr(const QuantLaunch& q, hipStream_t s) {
+  return q.sr ? pick_rht<FMT, true>(q, s) : pick_rht<FMT, false>(q, s);
+}
+
+}  // namespace
+
+hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
+  switch (q.format) {
+    case kNVFP4: return pick_sr<kNVFP4>(q, s);
+    case kMXFP4: return pick_sr<kMXFP4>(q, s);
+    default: return pick_sr<kUFP4>(q, s);
+  }
+}

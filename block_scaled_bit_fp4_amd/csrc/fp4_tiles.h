@@ -1,0 +1,96 @@
+// fp4_tiles.h -- memory-side helpers shared by the gfx950 kernels: vector
+// loads and widening of BF16/FP32 rows and columns, and the incremental
+// walk of a workgroup grid over units of work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fp4_device.h"
+
+namespace fp4dev {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- rows
+// Raw bytes of N consecutive elements of a row (16-byte aligned).
+template <typename T, int N>
+struct RowRaw {
+  static constexpr int kVec = N * (int)sizeof(T) / 16;
+  uint4 q[kVec];
+  __device__ __forceinline__ void load(const T* p) {
+    const uint4* s = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) q[i] = s[i];
+  }
+  // widen elements [16h, 16h + 16) to fp32
+  __device__ __forceinline__ void group(int h, float (&t)[16]) const {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 v = q[2 * h + i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          t[8 * i + 2 * k] = bf16_lo(w[k]);
+          t[8 * i + 2 * k + 1] = bf16_hi(w[k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = q[4 * h + i];
+        t[4 * i] = __uint_as_float(v.x); t[4 * i + 1] = __uint_as_float(v.y);
+        t[4 * i + 2] = __uint_as_float(v.z); t[4 * i + 3] = __uint_as_float(v.w);
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------- columns
+// C adjacent columns (C = 1 or 2) of 16 consecutive rows: one 2*C- or
+// 4*C-byte load per row, so a wave of lanes on consecutive column groups
+// reads one contiguous segment per row.
+template <typename T, int C>
+struct ColRaw {
+  using Word = typename std::conditional<sizeof(T) == 2,
+      typename std::conditional<C == 2, uint32_t, uint16_t>::type,
+      typename std::conditional<C == 2, uint2, uint32_t>::type>::type;
+  Word w[16];
+  __device__ __forceinline__ void load(const T* p, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = *reinterpret_cast<const Word*>(p + (int64_t)i * ld);
+  }
+  // widen column k (0 <= k < C) of the 16 rows
+  __device__ __forceinline__ void column(int k, float (&t)[16]) const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (sizeof(T) == 2) {
+        if constexpr (C == 2) t[i] = k ? bf16_hi(w[i]) : bf16_lo(w[i]);
+        else t[i] = __uint_as_float((uint32_t)w[i] << 16);
+      } else {
+        if constexpr (C == 2) t[i] = __uint_as_float(k ? w[i].y : w[i].x);
+        else t[i] = __uint_as_float(w[i]);
+      }
+    }
+  }
+};
+
+// Incremental (major, minor) walk over n_major x M units for a grid stride
+// sq * M + sr: no integer division inside loops.
+struct Walk {
+  int64_t major, minor;
+  __device__ __forceinline__ void init(int64_t u, int64_t M) {
+    major = u / M;
+    minor = u - major * M;
+  }
+  __device__ __forceinline__ void advance(int64_t sq, int64_t sr, int64_t M) {
+    minor += sr;
+    major += sq;
+    if (minor >= M) { minor -= M; major += 1; }
+  }
+};
+
+}  // namespace fp4dev

@@ -19,7 +19,9 @@ from tests.gpu_util import (DEV, assert_bytes_equal, f32_bits, note, quantize_bo
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352)]
+# (48, 80): rows and cols = 16 mod 32 (16-element row pieces, unaligned
+# column code rows); 1056 rows leave a 32-row tail below the 128-row runs.
+SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352), (48, 80)]
 KINDS = workloads.SMALL_KINDS
 
 COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4"], ["row", "col"], ["rtne", "sr"],
@@ -35,6 +37,9 @@ def _input(kind, shape, seed, dtype):
                          ids=["-".join(map(str, c)) for c in COMBOS])
 def test_quantize_dequantize_parity(fmt, axis, rounding, rht, dtype):
     for i, shape in enumerate(SHAPES):
+        W = shape[1] if axis == "row" else shape[0]
+        if W % fp4.BLOCK[fmt]:
+            continue
         kind = KINDS[(i + len(fmt) + (3 if rht else 0) + (1 if axis == "col" else 0)) % len(KINDS)]
         x = _input(kind, shape, 100 + i, dtype)
         note("parity %s %s %s rht=%s %s %s %s" % (fmt, axis, rounding, rht, dtype, shape, kind))
@@ -116,6 +121,23 @@ def test_strided_input():
                                    True, 0, 0)
     assert_bytes_equal(to_host(c), oc, "codes")
     assert_bytes_equal(to_host(s), osc, "scales")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_column_axis_odd_column_count(fmt, rounding):
+    """cols odd (one column per lane) through a strided view, ld = 40."""
+    base = _input("t3", (160, 40), 8, "bf16")
+    x = np.ascontiguousarray(base[:, :33])
+    note("odd cols %s %s" % (fmt, rounding))
+    xd = to_device(base)[:, :33]
+    c, s, ts = fp4.quantize(xd, fmt, "col", rounding, True, 2, 7)
+    torch.cuda.synchronize()
+    oc, osc, ots = oracle.quantize(x, fmt, "col", rounding, True, 2, 7)
+    assert_bytes_equal(to_host(c), oc, "codes")
+    assert_bytes_equal(to_host(s), osc, "scales")
+    if ts is not None:
+        assert f32_bits(float(ts.item())) == f32_bits(ots)
 
 
 def test_empty_and_single_block():
