@@ -135,7 +135,7 @@ def main():
             codes=torch.empty(cs, dtype=torch.uint8, device=dev),
             scales=torch.empty(ss, dtype=torch.uint8, device=dev),
             ts=torch.empty(1, dtype=torch.float32, device=dev),
-            ws=torch.empty(max(nws, 16), dtype=torch.uint8, device=dev) if nws else None,
+            ws=fp4.new_workspace(rows, cols, p, dev),
             alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size()),
             in_bytes=x.numel() * x.element_size()))
     stream = torch.cuda.current_stream()

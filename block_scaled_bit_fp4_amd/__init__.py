@@ -117,6 +117,13 @@ def workspace_bytes(rows: int, cols: int, params: Params) -> int:
     return int(load().fp4_workspace_bytes(rows, cols, ctypes.byref(params)))
 
 
+def new_workspace(rows: int, cols: int, params: Params, device) -> Optional[torch.Tensor]:
+    """A workspace for repeated quantize calls (None if none is needed); its
+    contents need no initialization."""
+    n = workspace_bytes(rows, cols, params)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def output_shapes(rows: int, cols: int, fmt: str, axis: str):
     ra, w = (rows, cols) if axis == "row" else (cols, rows)
     return (ra, w // 2), (ra, w // BLOCK[fmt])
