@@ -67,6 +67,49 @@ def traffic_for(workload: str, call_index: int):
     return per[call_index]
 
 
+def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, copy_mib: int,
+                          commands: list) -> dict:
+    """Per-call HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE;
+    KiB per dispatch) of `bench.py --copy-mib N`: the last dispatches are the
+    calls, each followed by a 1 MiB delimiter copy, then one N MiB copy whose
+    readings calibrate each counter (known bytes / reported bytes).  One more
+    delimiter precedes the first call."""
+    import csv
+
+    def segments(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        copies = [i for i, r in enumerate(rows) if "copyBuffer" in r["Kernel_Name"]]
+        big = copies[-1]
+        reported = float(rows[big]["Counter_Value"]) * 1024.0
+        delims = [i for i in copies[:-1]]
+        return rows, big, reported, delims
+
+    import workloads
+    ncalls = len(workloads.workload(workload).calls)
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "copy_mib": copy_mib, "commands": commands}
+    per = {}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows, big, reported, delims = segments(path)
+        factor = (copy_mib << 20) / reported
+        # the last ncalls + 1 delimiters bracket the calls' segments
+        bounds = delims[-ncalls - 1:]
+        starts, ends = [b + 1 for b in bounds[:-1]], bounds[1:]
+        vals, names = [], []
+        for a, b in zip(starts, ends):
+            seg = rows[a:b]
+            vals.append(sum(float(r["Counter_Value"]) for r in seg) * 1024.0 * factor)
+            names.append([r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                          .replace("void ", "").split("(")[0] for r in seg])
+        out[name + "_factor"] = round(factor, 5)
+        per[name] = vals
+        out["per_call_kernels"] = names
+    out["per_call_fetch_bytes"] = [int(v) for v in per["fetch"]]
+    out["per_call_write_bytes"] = [int(v) for v in per["write"]]
+    out["per_call_bytes"] = [int(a + b) for a, b in zip(per["fetch"], per["write"])]
+    return out
+
+
 def cpu_baseline(w, tensors, budget_s=12.0):
     """The oracle, as it is, on the host: whole workload steps repeated until
     ~budget_s of CPU time has passed (at least one step)."""
@@ -95,7 +138,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="activation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB "
+                         "(a known-size reference for hardware byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two counter runs")
     args = ap.parse_args()
+    if args.traffic_from:
+        cmd = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <dir> -o run -- python3 "
+               "bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline --copy-mib %d"
+               % (args.workload, args.copy_mib or 256))
+        t = traffic_from_counters(args.workload, args.traffic_from[0], args.traffic_from[1],
+                                  args.copy_mib or 256,
+                                  [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")])
+        path = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path is single-GPU in this build "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -190,6 +250,21 @@ def main():
         "kernel": "fp4_quantize call %d (%s %s %s rht=%s): tensor-amax + quantize kernels"
                   % (dom, c.fmt, c.axis, c.rounding, c.rht),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
+
+    if args.copy_mib:
+        # Counter runs: each call once, each followed by a 1 MiB delimiter
+        # copy, then one copy of known size that calibrates the counters.
+        small = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        small2 = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        small2.copy_(small)
+        for pl in plans:
+            run(pl)
+            small2.copy_(small)
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:

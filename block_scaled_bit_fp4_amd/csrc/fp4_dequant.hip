@@ -22,7 +22,7 @@ __device__ __forceinline__ void load_group(const T* x, int64_t ld, int64_t ra, i
   if (AXIS == 0) {
     RowRaw<T, 16> r;
     r.load(x + ra * ld + col0);
-    r.group(0, t);
+    r.template group<false>(0, t, 0u);
   } else {
     ColRaw<T, 1> c;
     c.load(x + col0 * ld + ra, ld);

@@ -23,6 +23,25 @@ enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2 };
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Sign flips of the RHT's D on packed BF16: word e of a 16-group holds
+// elements 2e (low half) and 2e + 1 (high half), so one xor with bits 15
+// and 31 flips both before widening.
+__device__ __forceinline__ uint32_t pair_sign_mask(uint32_t signs, int e) {
+  return (((signs >> (2 * e)) & 1u) << 15) | (((signs >> (2 * e + 1)) & 1u) << 31);
+}
+
+// Widen the 8 words of a BF16 16-group, flipping signs when SIGN.
+template <bool SIGN>
+__device__ __forceinline__ void widen_bf16_group(const uint32_t (&w)[8], uint32_t signs,
+                                                 float (&t)[16]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t v = SIGN ? w[e] ^ pair_sign_mask(signs, e) : w[e];
+    t[2 * e] = bf16_lo(v);
+    t[2 * e + 1] = bf16_hi(v);
+  }
+}
+
 // ------------------------------------------------------------ Philox4x32-10
 // Counter-based generator of Salmon et al. (SC'11): ten rounds of
 // 32x32->64-bit products of counter words with the two round multipliers,
@@ -37,8 +56,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t k0, uint32_t k1, uint32_
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input exclusive or (truth table 0x96): one instruction each
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
   }

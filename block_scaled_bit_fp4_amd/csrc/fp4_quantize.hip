@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void amax_row_kernel(
     RowRaw<T, 16> raw;
     raw.load(x + w.major * ld + w.minor * 16);
     float t[16];
-    raw.group(0, t);
-    if (RHT) { apply_signs(t, signs); fwht16(t); }
+    raw.template group<RHT>(0, t, signs);
+    if (RHT) fwht16(t);
 #pragma unroll
     for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
     w.advance(sq, sr, M);
@@ -136,6 +136,30 @@ __device__ __forceinline__ uint32_t encode8_fast(const float* v, const uint32_t 
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
+  } else if constexpr (FMT != kUFP4) {
+    // E2M1 stochastic rounding.  With E = max(floor(log2 m), 0) the levels
+    // around m are spaced sp = 2^(E-1) (0.5 below 2), q = m / sp is exact,
+    // floor(q) * sp is the level below and (floor(q) + 1) * sp the one above
+    // (>= 8 only past the top level, where the conversion saturates).  The
+    // chosen level, signed like v, goes through the exact hardware
+    // conversion, which also packs the codes.  Needs m < 2^126.
+    float lv[8];
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const float m = fabsf(v[l]);
+      const uint32_t e = max(__float_as_uint(m) & 0x7F800000u, 0x3F800000u);
+      const float inv_sp = __uint_as_float(0x7F800000u - e);
+      const float sp = __uint_as_float(e - 0x00800000u);
+      const float q = m * inv_sp;
+      const float fl = __builtin_floorf(q);
+      const float u = (float)((r[l >> 1] >> (16 * (l & 1))) & 0xFFFFu);
+      const float lvl = (u < (q - fl) * 65536.0f ? fl + 1.0f : fl) * sp;
+      lv[l] = __uint_as_float(__float_as_uint(lvl) | (__float_as_uint(v[l]) & 0x80000000u));
+    }
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lv[0], lv[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lv[2], lv[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lv[4], lv[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, lv[6], lv[7], 1.0f, 3);
   } else {
 #pragma unroll
     for (int l = 0; l < 8; ++l) {
@@ -194,14 +218,16 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
     sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
     inv = inv_tab[sbyte];
   }
+  // E2M1 stochastic rounding in encode8_fast needs |v| < 2^126.
+  const float limit = (SR && FMT != kUFP4) ? 0x1p126f : __builtin_inff();
   float mul;
   bool fast;
   if constexpr (kFold) {
     mul = inv * 0.25f;
-    fast = inv >= 4.70197740328915e-38f && amax_t * mul < __builtin_inff();
+    fast = inv >= 4.70197740328915e-38f && amax_t * mul < limit;
   } else {
     mul = inv;
-    fast = amax_b * inv < __builtin_inff();
+    fast = amax_b * inv < limit;
   }
 #pragma unroll
   for (int q = 0; q < B / 8; ++q) {
@@ -256,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
 #pragma unroll
       for (int h = 0; h < B / 16; ++h) {
         float g[16];
-        cur.group(bi * (B / 16) + h, g);
-        if (RHT) { apply_signs(g, a.signs); fwht16(g); }
+        cur.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+        if (RHT) fwht16(g);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           t[16 * h + j] = g[j];
@@ -392,40 +418,50 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
 // Column axis, interior tiles: TR x-rows by TC x-columns (TC * sizeof(T) =
 // 128 bytes), staged through LDS.  Every global load is a 16-byte piece of a
 // row (8 lanes read one 128-byte row segment); the tile is written to LDS
-// transposed (A-row-major, packed row pairs for BF16) with an odd word pitch,
-// so the scattered 4-byte writes and reads fall on distinct banks; each lane
-// then codes whole blocks of one A-row, and the lanes of one A-row write its
-// TR/2 code bytes as one contiguous run.
+// transposed (A-row-major, packed row pairs for BF16; layout in ColTile);
+// each lane then codes whole blocks of one A-row, and the lanes of one A-row
+// write its TR/2 code bytes as one contiguous run.  A workgroup walks tiles
+// with a grid stride and loads its next tile while coding the current one.
 template <typename T>
 struct ColTile {
   static constexpr int TR = 256;                        // rows per tile
   static constexpr int TC = 128 / (int)sizeof(T);       // columns per tile
   static constexpr int EPW = 4 / (int)sizeof(T);        // elements per LDS word
-  static constexpr int P = TR / EPW + 1;                // LDS words per A-row (odd)
+  // Words per A-row.  BF16: 128 words (row pairs) plus 4 of padding, so
+  // every A-row starts 16-byte aligned and a block reads as 128-bit words;
+  // FP32: an odd pitch.
+  static constexpr int P = sizeof(T) == 2 ? TR / 2 + 4 : TR + 1;
   static constexpr int kWords = TC * P;
+  // LDS word of (A-row col, position pr).  BF16 positions are XOR-swizzled
+  // in 4-word units, by bits 3-5 of col (the transposing stores of one
+  // instruction then reach 32 distinct banks per half wave) and by bit 5 of
+  // pr (the eight 128-bit reads of lanes on consecutive blocks then reach
+  // distinct 4-bank groups); aligned 4-word groups stay whole.
+  __device__ static __forceinline__ int at(int col, int pr) {
+    if constexpr (sizeof(T) == 2)
+      return col * P + (pr ^ (((col >> 3) & 7) << 2) ^ (((pr >> 5) & 1) << 2));
+    else
+      return col * P + pr;
+  }
 };
 
 template <int FMT, bool SR, bool RHT, bool GIVEN, typename T>
-__global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T* __restrict__ x,
                                                                      QuantArgs a) {
   using Tile = ColTile<T>;
   constexpr int B = FMT == kMXFP4 ? 32 : 16;
-  constexpr int TR = Tile::TR, TC = Tile::TC, P = Tile::P, EPW = Tile::EPW;
+  constexpr int TR = Tile::TR, TC = Tile::TC;
   constexpr int kLoads = TR * TC * (int)sizeof(T) / 16 / kThreads;  // 16-byte loads per lane
   constexpr int kUnits = TC * (TR / B) / kThreads;                  // blocks coded per lane
   __shared__ float inv_tab[128];
-  __shared__ uint32_t lds[Tile::kWords];
-  ScaleCtx c{0.0f, 0.0f};
-  bool first = true;
+  __shared__ __align__(16) uint32_t lds[Tile::kWords];
+  const int64_t ntile = a.n_major * a.M;  // row tiles x column tiles, column tile fastest
 
-  // a.n_major row tiles x a.M column tiles, column tile fastest
-  for (int64_t tile = blockIdx.x; tile < a.n_major * a.M; tile += gridDim.x) {
+  // load i: segment threadIdx % 8 of row tile_row(i); for BF16, loads i and
+  // i + kLoads/2 are the two rows of one pair
+  auto load_tile = [&](int64_t tile, uint4 (&buf)[kLoads]) {
     const int64_t tr = tile / a.M, tc = tile - tr * a.M;
-    const int64_t r0 = tr * TR, c0 = tc * TC;
-    // ---- global -> registers (all loads in flight), then -> LDS transposed
-    // load i: segment threadIdx % 8 of row tile_row(i); for BF16, loads i and
-    // i + kLoads/2 are the two rows of one pair
-    uint4 buf[kLoads];
+    const T* base = x + tr * TR * a.ld + tc * TC;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       int row;
@@ -434,16 +470,21 @@ __global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __
       else
         row = (threadIdx.x >> 3) + 32 * i;
       const int seg = threadIdx.x & 7;
-      buf[i] = *reinterpret_cast<const uint4*>(x + (r0 + row) * a.ld + c0 +
-                                               seg * (16 / (int)sizeof(T)));
+      buf[i] = *reinterpret_cast<const uint4*>(base + row * a.ld + seg * (16 / (int)sizeof(T)));
     }
-    if (first) {  // the first tile's loads are in flight during the prologue
-      c = scale_prologue<FMT, GIVEN>(a, inv_tab);
-      first = false;
-    }
+  };
+
+  int64_t tile = blockIdx.x;
+  bool have = tile < ntile;
+  uint4 buf[kLoads];
+  if (have) load_tile(tile, buf);  // in flight during the prologue
+  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  while (have) {
+    const int64_t tr = tile / a.M, tc = tile - tr * a.M;
+    const int64_t r0 = tr * TR, c0 = tc * TC;
     __syncthreads();  // previous tile's LDS reads are done
+    // ---- registers -> LDS, transposed
     if constexpr (sizeof(T) == 2) {
-      // rows are processed in pairs: load i and i + kLoads/2 hold rows 2p and 2p+1
 #pragma unroll
       for (int i = 0; i < kLoads / 2; ++i) {
         const int pr = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;  // row pair, segment
@@ -452,8 +493,8 @@ __global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int col = seg * 8 + 2 * k;
-          lds[col * P + pr] = (ev[k] & 0xFFFFu) | (od[k] << 16);
-          lds[(col + 1) * P + pr] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
+          lds[Tile::at(col, pr)] = (ev[k] & 0xFFFFu) | (od[k] << 16);
+          lds[Tile::at(col + 1, pr)] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
         }
       }
     } else {
@@ -462,10 +503,14 @@ __global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __
         const int row = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;
         const uint32_t v[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lds[(seg * 4 + k) * P + row] = v[k];
+        for (int k = 0; k < 4; ++k) lds[Tile::at(seg * 4 + k, row)] = v[k];
       }
     }
     __syncthreads();
+    // ---- the next tile's loads fly while this one is coded
+    const int64_t next = tile + gridDim.x;
+    const bool have_next = next < ntile;
+    if (have_next) load_tile(next, buf);
     // ---- code blocks: unit u -> (A-row cl, block j), block fastest
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
@@ -476,18 +521,19 @@ __global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __
 #pragma unroll
       for (int h = 0; h < B / 16; ++h) {
         float g[16];
-        const uint32_t* src = lds + cl * P + (j * B + h * 16) / EPW;
+        if constexpr (sizeof(T) == 2) {
+          const int pr0 = (j * B + h * 16) / 2;
+          const uint4 lo = *reinterpret_cast<const uint4*>(lds + Tile::at(cl, pr0));
+          const uint4 hi = *reinterpret_cast<const uint4*>(lds + Tile::at(cl, pr0 + 4));
+          const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          widen_bf16_group<RHT>(w, a.signs, g);
+        } else {
+          const uint32_t* src = lds + Tile::at(cl, j * B + h * 16);
 #pragma unroll
-        for (int e = 0; e < 16 / EPW; ++e) {
-          const uint32_t wv = src[e];
-          if constexpr (sizeof(T) == 2) {
-            g[2 * e] = bf16_lo(wv);
-            g[2 * e + 1] = bf16_hi(wv);
-          } else {
-            g[e] = __uint_as_float(wv);
-          }
+          for (int e = 0; e < 16; ++e) g[e] = __uint_as_float(src[e]);
+          if (RHT) apply_signs(g, a.signs);
         }
-        if (RHT) { apply_signs(g, a.signs); fwht16(g); }
+        if (RHT) fwht16(g);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           t[16 * h + e] = g[e];
@@ -506,6 +552,8 @@ __global__ __launch_bounds__(kThreads) void quantize_col_tile_kernel(const T* __
       else *reinterpret_cast<uint4*>(cp) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       a.scales[ra * a.nblk_axis + rb] = (uint8_t)sbyte;
     }
+    tile = next;
+    have = have_next;
   }
 }
 

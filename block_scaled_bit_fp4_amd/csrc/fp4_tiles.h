@@ -25,19 +25,14 @@ struct RowRaw {
 #pragma unroll
     for (int i = 0; i < kVec; ++i) q[i] = s[i];
   }
-  // widen elements [16h, 16h + 16) to fp32
-  __device__ __forceinline__ void group(int h, float (&t)[16]) const {
+  // widen elements [16h, 16h + 16) to fp32; SIGN applies the RHT's sign
+  // flips (bit j of signs: element j negated)
+  template <bool SIGN>
+  __device__ __forceinline__ void group(int h, float (&t)[16], uint32_t signs) const {
     if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 v = q[2 * h + i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          t[8 * i + 2 * k] = bf16_lo(w[k]);
-          t[8 * i + 2 * k + 1] = bf16_hi(w[k]);
-        }
-      }
+      const uint4 a = q[2 * h], b = q[2 * h + 1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      widen_bf16_group<SIGN>(w, signs, t);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -45,6 +40,7 @@ struct RowRaw {
         t[4 * i] = __uint_as_float(v.x); t[4 * i + 1] = __uint_as_float(v.y);
         t[4 * i + 2] = __uint_as_float(v.z); t[4 * i + 3] = __uint_as_float(v.w);
       }
+      if (SIGN) apply_signs(t, signs);
     }
   }
 };

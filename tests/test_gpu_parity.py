@@ -69,7 +69,9 @@ def test_every_kind_nvfp4_rht(kind):
 @pytest.mark.parametrize("fmt", ["nvfp4", "ufp4"])
 def test_given_tensor_scale(fmt):
     x = _input("t3", (128, 256), 3, "bf16")
-    for ts in (1e-3, 2.0 ** -20, 0.37, 1e4, 0.0):
+    # 1e-39 (subnormal): 1/d overflows, blocks take the per-element careful
+    # path; 1e38: decoded block scales overflow to infinity.
+    for ts in (1e-3, 2.0 ** -20, 0.37, 1e4, 0.0, 1e-39, 1e38):
         note("given ts %s %g" % (fmt, ts))
         quantize_both(x, fmt, "row", "rtne", True, 0, 0, given=ts)
         quantize_both(x, fmt, "col", "sr", False, 0, 9, given=ts)
