@@ -18,7 +18,9 @@
 // (A-rows) and a run of NB consecutive blocks down them; each row of a
 // block is one 2C- or 4C-byte load, so a wave reads one contiguous segment
 // per row, and each lane writes NB*B/2 contiguous code bytes per column.
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "fp4_device.h"
 #include "fp4_launch.h"
@@ -63,11 +65,12 @@ __global__ __launch_bounds__(kThreads) void amax_col_kernel(
   while (w.major < n_major) {
     ColRaw<T, C> raw;
     raw.load(x + w.major * 16 * ld + w.minor * C, ld);
+    if (RHT) raw.flip_rows(signs);
 #pragma unroll
     for (int k = 0; k < C; ++k) {
       float t[16];
       raw.column(k, t);
-      if (RHT) { apply_signs(t, signs); fwht16(t); }
+      if (RHT) fwht16(t);
 #pragma unroll
       for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
     }
@@ -129,7 +132,17 @@ __device__ __forceinline__ ScaleCtx scale_prologue(const QuantArgs& a, float* in
 template <int FMT, bool SR>
 __device__ __forceinline__ uint32_t encode8_fast(const float* v, const uint32_t (&r)[4]) {
   uint32_t word = 0;
-  if constexpr (FMT != kUFP4 && !SR) {
+  if constexpr (FMT == kUFP4 && !SR) {
+    // Uniform grid, round to nearest even: adding 2^23 to min(m, 7) rounds
+    // it to an integer (binary32 addition, ties to even) held in the low
+    // mantissa bits; the sign bit of v becomes bit 3.
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      const float m = fminf(fabsf(v[l]), 7.0f);
+      const uint32_t k = __float_as_uint(m + 8388608.0f) & 7u;
+      word |= (k | ((__float_as_uint(v[l]) >> 28) & 8u)) << (4 * l);
+    }
+  } else if constexpr (FMT != kUFP4 && !SR) {
     // E2M1 round-to-nearest-even in hardware: two values per instruction,
     // sign and saturation included; scale operand 1.0 (no rescaling).
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
@@ -511,8 +524,10 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
     const int64_t next = tile + gridDim.x;
     const bool have_next = next < ntile;
     if (have_next) load_tile(next, buf);
-    // ---- code blocks: unit u -> (A-row cl, block j), block fastest
-#pragma unroll
+    // ---- code blocks: unit u -> (A-row cl, block j), block fastest; units
+    // one at a time for 32-element blocks (register pressure)
+    constexpr int kUnroll = B == 32 ? 1 : kUnits;
+#pragma unroll kUnroll
     for (int i = 0; i < kUnits; ++i) {
       const int u = threadIdx.x + i * kThreads;
       const int cl = u / (TR / B), j = u % (TR / B);
@@ -560,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
 // ------------------------------------------------------------ dispatch
 // Launch geometry (measured on MI355X; overridable at build time for sweeps).
 #ifndef FP4_ROW_GRID
-#define FP4_ROW_GRID 2048
+#define FP4_ROW_GRID 1024
 #endif
 #ifndef FP4_COL_GRID
 #define FP4_COL_GRID 4096
@@ -578,13 +593,50 @@ constexpr int64_t kRowGrid = FP4_ROW_GRID;  // workgroups of the row kernel (cap
 constexpr int64_t kColGrid = FP4_COL_GRID;  // workgroups of the column kernel (cap)
 constexpr int kColBlocks = FP4_COL_BLOCKS;  // NB for 16-element blocks (half for 32)
 
+#ifndef FP4_RESIDENT_CAP
+#define FP4_RESIDENT_CAP 1
+#endif
+
+// Workgroups of `kernel` (kThreads lanes, static LDS only) that the current
+// device holds at once over all its CUs; cached per kernel and device.
+// Grids no larger than this run as a single wave of workgroups, with no
+// partial last wave.  0 when the runtime cannot tell.
+int64_t resident_wgs(const void* kernel) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache[dev].find(kernel);
+  if (it != cache[dev].end()) return it->second;
+  int per_cu = 0, cus = 0;
+  int64_t n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    n = (int64_t)per_cu * cus;
+  cache[dev][kernel] = n;
+  return n;
+}
+
+// Grid cap for `kernel`: the fixed cap, lowered to one resident wave.
+int64_t grid_cap(const void* kernel, int64_t cap) {
+  if (!FP4_RESIDENT_CAP) return cap;
+  const int64_t r = resident_wgs(kernel);
+  return r > 0 && r < cap ? r : cap;
+}
+
 struct WalkPlan {
   unsigned grid;
   int64_t sq, sr;
 };
+// Grid of at most `cap` workgroups over n_major x M units, one unit per
+// lane per round, sized so that every round but the last is whole and the
+// rounds are spread evenly (no lone partial round).
 inline WalkPlan plan_walk(int64_t n_major, int64_t M, int64_t cap) {
   const int64_t units = n_major * M;
-  int64_t g = (units + kThreads - 1) / kThreads;
+  if (cap < 1) cap = 1;
+  const int64_t rounds = (units + cap * kThreads - 1) / (cap * kThreads);
+  int64_t g = rounds > 0 ? (units + rounds * kThreads - 1) / (rounds * kThreads) : 1;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   const int64_t stride = g * kThreads;
@@ -601,6 +653,7 @@ void launch_amax(const QuantLaunch& q, hipStream_t s) {
     hipLaunchKernelGGL((amax_row_kernel<RHT, T>), dim3(kAmaxPartials), dim3(kThreads), 0, s, x,
                        q.ld, nmaj, M, stride / M, stride % M, q.signs, q.workspace);
   } else if (q.cols % 2 == 0) {
+    // (16-byte row pieces, C = 8 for BF16, measured slower)
     const int64_t nmaj = q.rows / 16, M = q.cols / 2;
     hipLaunchKernelGGL((amax_col_kernel<RHT, T, 2>), dim3(kAmaxPartials), dim3(kThreads), 0, s,
                        x, q.ld, nmaj, M, stride / M, stride % M, q.signs, q.workspace);
@@ -632,20 +685,21 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
     const bool wide = q.cols % 32 == 0;
     const bool wider = FP4_ROW_UNIT >= 64 && q.cols % 64 == 0;
     const int U = wider ? 64 : (wide ? 32 : 16);
-    const WalkPlan wp = plan_walk(q.rows, q.cols / U, kRowGrid);
     a.n_major = q.rows;
     a.M = q.cols / U;
-    a.sq = wp.sq;
-    a.sr = wp.sr;
+    auto launch = [&](auto kernel) {
+      const WalkPlan wp =
+          plan_walk(a.n_major, a.M, grid_cap(reinterpret_cast<const void*>(kernel), kRowGrid));
+      a.sq = wp.sq;
+      a.sr = wp.sr;
+      hipLaunchKernelGGL(kernel, dim3(wp.grid), dim3(kThreads), 0, s, x, a);
+    };
     if (wider)
-      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 64>), dim3(wp.grid),
-                         dim3(kThreads), 0, s, x, a);
+      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 64>);
     else if (wide)
-      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 32>), dim3(wp.grid),
-                         dim3(kThreads), 0, s, x, a);
+      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 32>);
     else if constexpr (B == 16)
-      hipLaunchKernelGGL((quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 16>), dim3(wp.grid),
-                         dim3(kThreads), 0, s, x, a);
+      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 16>);
   } else {
     a.W = q.rows;
     a.nblk_axis = q.rows / B;
@@ -660,6 +714,8 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       t.n_major = nrt;
       t.M = nct;
       const int64_t ntile = nrt * nct;
+      // more workgroups than fit at once measured faster here than one
+      // resident wave
       const unsigned grid = (unsigned)(ntile < kColGrid ? ntile : kColGrid);
       hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, GIVEN, T>), dim3(grid),
                          dim3(kThreads), 0, s, x, t);

@@ -46,29 +46,53 @@ struct RowRaw {
 };
 
 // ------------------------------------------------------------- columns
-// C adjacent columns (C = 1 or 2) of 16 consecutive rows: one 2*C- or
-// 4*C-byte load per row, so a wave of lanes on consecutive column groups
+// C adjacent columns of 16 consecutive rows: one load of C * sizeof(T)
+// bytes (2 to 16) per row, so a wave of lanes on consecutive column groups
 // reads one contiguous segment per row.
 template <typename T, int C>
 struct ColRaw {
-  using Word = typename std::conditional<sizeof(T) == 2,
-      typename std::conditional<C == 2, uint32_t, uint16_t>::type,
-      typename std::conditional<C == 2, uint2, uint32_t>::type>::type;
-  Word w[16];
+  static constexpr int kBytes = C * (int)sizeof(T);
+  static constexpr int NW = kBytes < 4 ? 1 : kBytes / 4;  // 32-bit words per row
+  static_assert(kBytes == 2 || kBytes == 4 || kBytes == 8 || kBytes == 16, "row piece");
+  uint32_t w[16][NW];
   __device__ __forceinline__ void load(const T* p, int64_t ld) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = *reinterpret_cast<const Word*>(p + (int64_t)i * ld);
+    for (int i = 0; i < 16; ++i) {
+      const T* r = p + (int64_t)i * ld;
+      if constexpr (kBytes == 2) {
+        w[i][0] = *reinterpret_cast<const uint16_t*>(r);
+      } else if constexpr (kBytes == 4) {
+        w[i][0] = *reinterpret_cast<const uint32_t*>(r);
+      } else if constexpr (kBytes == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(r);
+        w[i][0] = v.x; w[i][1] = v.y;
+      } else {
+        const uint4 v = *reinterpret_cast<const uint4*>(r);
+        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+      }
+    }
+  }
+  // the RHT's sign flips down the columns: row i negated where bit i of
+  // signs is set (one xor per 32-bit word)
+  __device__ __forceinline__ void flip_rows(uint32_t signs) {
+    constexpr uint32_t kSign =
+        sizeof(T) == 2 ? (kBytes == 2 ? 0x8000u : 0x80008000u) : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t m = ((signs >> i) & 1u) ? kSign : 0u;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) w[i][k] ^= m;
+    }
   }
   // widen column k (0 <= k < C) of the 16 rows
   __device__ __forceinline__ void column(int k, float (&t)[16]) const {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if constexpr (sizeof(T) == 2) {
-        if constexpr (C == 2) t[i] = k ? bf16_hi(w[i]) : bf16_lo(w[i]);
-        else t[i] = __uint_as_float((uint32_t)w[i] << 16);
+        const uint32_t v = w[i][k / 2];
+        t[i] = (k & 1) ? bf16_hi(v) : bf16_lo(v);
       } else {
-        if constexpr (C == 2) t[i] = __uint_as_float(k ? w[i].y : w[i].x);
-        else t[i] = __uint_as_float(w[i]);
+        t[i] = __uint_as_float(w[i][k]);
       }
     }
   }
