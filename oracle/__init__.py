@@ -38,11 +38,14 @@ _SO = os.path.join(_HERE, "libfp4_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3}
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 GRIDS = {"e2m1": 0, "uniform": 1}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32}
+TS_MODES = {"compute": 0, "given": 1, "outer128": 2}
+OUTER = 128  # outer block of the double-block mode
+MX = ("mxfp4", "mxfp4_oas")
 E2M1_LEVELS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 UNIFORM_LEVELS = (0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0)
 
@@ -99,6 +102,8 @@ def lib():
         L.fp4r_e4m3_decode.restype = ctypes.c_float
         L.fp4r_e8m0_exponent.argtypes = [ctypes.c_float]
         L.fp4r_e8m0_exponent.restype = ctypes.c_int
+        L.fp4r_e8m0_exponent_oas.argtypes = [ctypes.c_float]
+        L.fp4r_e8m0_exponent_oas.restype = ctypes.c_int
         L.fp4r_round_rtne.argtypes = [ctypes.c_float, ctypes.c_int]
         L.fp4r_round_rtne.restype = ctypes.c_int
         L.fp4r_round_sr.argtypes = [ctypes.c_float, ctypes.c_int, ctypes.c_uint32]
@@ -133,7 +138,7 @@ def _ptr(a: np.ndarray, ctype):
 def make_params(fmt="nvfp4", axis="row", rounding="rtne", rht=False, rht_seed=0,
                 sr_seed=0, ts_mode="compute") -> Params:
     return Params(FORMATS[fmt], BLOCK[fmt], AXES[axis], ROUNDINGS[rounding], int(bool(rht)),
-                  0 if ts_mode == "compute" else 1, int(rht_seed) & (2**64 - 1),
+                  TS_MODES[ts_mode], int(rht_seed) & (2**64 - 1),
                   int(sr_seed) & (2**64 - 1))
 
 
@@ -189,6 +194,10 @@ def e8m0_exponent(amax: float) -> int:
     return int(lib().fp4r_e8m0_exponent(amax))
 
 
+def e8m0_exponent_oas(amax: float) -> int:
+    return int(lib().fp4r_e8m0_exponent_oas(amax))
+
+
 def round_grid(m, grid="e2m1", rounding="rtne", u16=None) -> np.ndarray:
     m = np.ascontiguousarray(np.asarray(m, dtype=np.float32).ravel())
     if u16 is None:
@@ -206,34 +215,47 @@ def max_threads() -> int:
 
 # ------------------------------------------------------------------- tensors
 def quantize(x: np.ndarray, fmt="nvfp4", axis="row", rounding="rtne", rht=False,
-             rht_seed=0, sr_seed=0, tensor_scale: float | None = None):
+             rht_seed=0, sr_seed=0, tensor_scale: float | None = None, outer=False):
     """Quantize a 2-D array; returns (codes, scales, tensor_scale).
 
     codes: uint8 [rows_A, W/2]; scales: uint8 [rows_A, W/B]; tensor_scale is a
     float for NVFP4/UFP4 (computed, or the given one) and None for MXFP4.
-    Passing ``tensor_scale`` selects the given-scale mode."""
+    Passing ``tensor_scale`` selects the given-scale mode; ``outer=True`` the
+    double-block mode, where tensor_scale is a float32 [rows_A, W/128] array
+    of outer scales."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
-    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed,
-                    "given" if tensor_scale is not None else "compute")
+    mode = "outer128" if outer else ("given" if tensor_scale is not None else "compute")
+    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, mode)
     ra, w = (rows, cols) if axis == "row" else (cols, rows)
     codes = np.zeros((ra, w // 2), dtype=np.uint8)
     scales = np.zeros((ra, w // BLOCK[fmt]), dtype=np.uint8)
-    ts = np.array([tensor_scale if tensor_scale is not None else 0.0], dtype=np.float32)
+    if outer:
+        ts = np.zeros((ra, max(w // OUTER, 1)), dtype=np.float32)
+    else:
+        ts = np.array([tensor_scale if tensor_scale is not None else 0.0], dtype=np.float32)
     rc = lib().fp4r_quantize(x.ctypes.data, _dtype_code(x), rows, cols, cols, ctypes.byref(p),
                              _ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
                              _ptr(ts, ctypes.c_float))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    return codes, scales, (None if fmt == "mxfp4" else float(ts[0]))
+    if fmt in MX:
+        return codes, scales, None
+    return codes, scales, (ts[:, : w // OUTER] if outer else float(ts[0]))
 
 
 def dequantize(codes, scales, tensor_scale, rows, cols, fmt="nvfp4", axis="row", rht=False,
                rht_seed=0, inverse_rht=False, out_dtype="f32") -> np.ndarray:
+    """Rebuild x.  tensor_scale: a float, or the [rows_A, W/128] outer-scale
+    array of the double-block mode."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
-    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, "given")
-    ts = np.array([tensor_scale if tensor_scale is not None else 0.0], dtype=np.float32)
+    outer = isinstance(tensor_scale, np.ndarray) and tensor_scale.ndim == 2
+    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, "outer128" if outer else "given")
+    if outer:
+        ts = np.ascontiguousarray(tensor_scale, dtype=np.float32)
+    else:
+        ts = np.array([tensor_scale if tensor_scale is not None else 0.0], dtype=np.float32)
     out = np.zeros((rows, cols), dtype=np.float32 if out_dtype == "f32" else np.uint16)
     rc = lib().fp4r_dequantize(_ptr(codes, ctypes.c_uint8), _ptr(scales, ctypes.c_uint8),
                                _ptr(ts, ctypes.c_float), rows, cols, ctypes.byref(p),

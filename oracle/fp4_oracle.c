@@ -175,6 +175,21 @@ int fp4r_e8m0_exponent(float amax) {
   return e;
 }
 
+/* [MXFP4] 2.A (overflow-aware scaling): the block amax is mapped into
+ * (3.5, 7] instead of [4, 8), so the largest element no longer lands past
+ * the top level 6 by up to a third.  Search upward from an exponent that is
+ * certainly too small; amax <= 7 * 2^e is exact in binary64. */
+int fp4r_e8m0_exponent_oas(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int ex;
+  (void)frexp((double)amax, &ex); /* 2^(ex-1) <= amax < 2^ex */
+  int e = ex - 5;                 /* 7 * 2^(ex-5) < 2^(ex-1) <= amax */
+  while ((double)amax > 7.0 * ldexp(1.0, e)) ++e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
 /* ------------------------------------------------------------------------
  * Rounding a magnitude m >= 0 to a grid.  k is the bin with
  * L[k] <= m < L[k+1]; m >= L[7] saturates at 7 ([MXFP4] 2.A: saturation at
@@ -247,17 +262,23 @@ static float grid_max(int format) {
   return format == FP4R_UFP4 ? 7.0f : 6.0f;
 }
 
+static int is_mx(int format) {
+  return format == FP4R_MXFP4 || format == FP4R_MXFP4_OAS;
+}
+
 static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
                         int64_t ld) {
   if (!p) return -1;
-  if (p->format < 0 || p->format > 2) return -1;
-  if (p->format == FP4R_MXFP4 ? p->block != 32 : p->block != 16) return -1;
+  if (p->format < 0 || p->format > 3) return -1;
+  if (is_mx(p->format) ? p->block != 32 : p->block != 16) return -1;
+  if (!is_mx(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
   if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;
   if (p->rounding != FP4R_RTNE && p->rounding != FP4R_SR) return -1;
   if (rows < 0 || cols < 0 || ld < cols) return -1;
   int64_t W = p->axis == FP4R_ROW ? cols : rows;
   if (W % p->block) return -1;
   if (p->rht && (W % 16)) return -1;
+  if (!is_mx(p->format) && p->ts_mode == FP4R_TS_OUTER128 && (W % FP4R_OUTER)) return -1;
   return 0;
 }
 
@@ -277,17 +298,22 @@ static void load_row(const void* x, int dt, int axis, int64_t ld, int64_t i,
  * per-tensor dynamic scaling):
  *   s_t = amax_t / (G * 448);  r_b = amax_b / (s_t * G);  S_b = E4M3(r_b);
  *   d_b = s_t * decode(S_b);  v = y * (1 / d_b).
- * MXFP4 ([MXFP4] 2): d_b = 2^e with e = floor(log2 amax_b) - 2.
+ * MXFP4 ([MXFP4] 2): d_b = 2^e with e = floor(log2 amax_b) - 2; with
+ * overflow-aware scaling ([MXFP4] 2.A) e places amax_b / 2^e in (3.5, 7].
+ * Double block ([TJ2] 2.A): s_t is replaced by the outer scale of the
+ * 128-element piece of the A-row that holds the block.
  * A block whose scale decodes to zero codes every element as a signed zero.
  * ---------------------------------------------------------------------- */
 static float block_decode_scale(const fp4r_params* p, uint8_t sbyte, float s_t) {
-  if (p->format == FP4R_MXFP4) return ldexpf(1.0f, (int)sbyte - 127);
+  if (is_mx(p->format)) return ldexpf(1.0f, (int)sbyte - 127);
   if (sbyte == 0) return 0.0f;
   return s_t * fp4r_e4m3_decode(sbyte);
 }
 
 static uint8_t block_scale_byte(const fp4r_params* p, float amax_b, float s_t) {
   if (p->format == FP4R_MXFP4) return (uint8_t)(fp4r_e8m0_exponent(amax_b) + 127);
+  if (p->format == FP4R_MXFP4_OAS)
+    return (uint8_t)(fp4r_e8m0_exponent_oas(amax_b) + 127);
   if (s_t == 0.0f || amax_b == 0.0f) return 0x00;
   float den = s_t * grid_max(p->format);
   float r = amax_b / den;
@@ -328,13 +354,16 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
   const int64_t RA = axis == FP4R_ROW ? rows : cols;
   const int64_t W = axis == FP4R_ROW ? cols : rows;
   const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
-  const int two_level = p->format != FP4R_MXFP4;
+  const int two_level = !is_mx(p->format);
+  const int outer = two_level && p->ts_mode == FP4R_TS_OUTER128;
 
   /* tensor scale: amax over the whole (rotated) operand */
   float s_t = 0.0f;
   if (two_level) {
     if (!tensor_scale) return -1;
-    if (p->ts_mode == FP4R_TS_GIVEN) {
+    if (outer) {
+      /* double block: one scale per 128-element piece, in the row loop */
+    } else if (p->ts_mode == FP4R_TS_GIVEN) {
       s_t = *tensor_scale;
     } else {
       float amax = 0.0f;
@@ -358,6 +387,7 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
   }
 
   const int64_t nblk = W / B;
+  const int64_t nout = W / FP4R_OUTER;
 #pragma omp parallel
   {
     float* y = (float*)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
@@ -365,14 +395,25 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < RA; ++i) {
       load_row(x, in_dtype, axis, ld, i, W, p->rht, signs, y);
+      if (outer) {
+        /* [TJ2] 2.A double block: the outer scale of a 128-element piece
+         * takes the place of the tensor scale, from that piece's amax. */
+        for (int64_t o = 0; o < nout; ++o) {
+          float amax_o = 0.0f;
+          for (int e = 0; e < FP4R_OUTER; ++e)
+            if (fabsf(y[o * FP4R_OUTER + e]) > amax_o) amax_o = fabsf(y[o * FP4R_OUTER + e]);
+          tensor_scale[i * nout + o] = amax_o / (grid_max(p->format) * 448.0f);
+        }
+      }
       for (int64_t b = 0; b < nblk; ++b) {
         const float* yb = y + b * B;
+        const float s_b = outer ? tensor_scale[i * nout + (b * B) / FP4R_OUTER] : s_t;
         float amax_b = 0.0f;
         for (int e = 0; e < B; ++e)
           if (fabsf(yb[e]) > amax_b) amax_b = fabsf(yb[e]);
-        uint8_t sbyte = block_scale_byte(p, amax_b, s_t);
+        uint8_t sbyte = block_scale_byte(p, amax_b, s_b);
         scales[i * nblk + b] = sbyte;
-        fp4r_quantize_block(yb, p, sbyte, s_t, i, b * B, W, kb);
+        fp4r_quantize_block(yb, p, sbyte, s_b, i, b * B, W, kb);
         for (int e = 0; e < B; e += 2) {
           int64_t c = b * B + e; /* even column: low nibble */
           codes[i * (W / 2) + c / 2] = (uint8_t)(kb[e] | (kb[e + 1] << 4));
@@ -396,10 +437,11 @@ int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
   const int64_t W = axis == FP4R_ROW ? cols : rows;
   const int64_t nblk = W / B;
   const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
+  const int outer = !is_mx(p->format) && p->ts_mode == FP4R_TS_OUTER128;
   float s_t = 0.0f;
-  if (p->format != FP4R_MXFP4) {
+  if (!is_mx(p->format)) {
     if (!tensor_scale) return -1;
-    s_t = *tensor_scale;
+    if (!outer) s_t = *tensor_scale;
   }
 #pragma omp parallel
   {
@@ -407,7 +449,9 @@ int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < RA; ++i) {
       for (int64_t b = 0; b < nblk; ++b) {
-        float d = block_decode_scale(p, scales[i * nblk + b], s_t);
+        const float s_b =
+            outer ? tensor_scale[i * (W / FP4R_OUTER) + (b * B) / FP4R_OUTER] : s_t;
+        float d = block_decode_scale(p, scales[i * nblk + b], s_b);
         for (int e = 0; e < B; ++e) {
           int64_t c = b * B + e;
           uint8_t byte = codes[i * (W / 2) + c / 2];

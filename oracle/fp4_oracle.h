@@ -44,20 +44,22 @@ extern "C" {
 #endif
 
 /* enumerations (values mirror the product's C-ABI by convention only) */
-enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2 };
+enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3 };
 enum { FP4R_ROW = 0, FP4R_COL = 1 };
 enum { FP4R_RTNE = 0, FP4R_SR = 1 };
 enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
-enum { FP4R_TS_COMPUTE = 0, FP4R_TS_GIVEN = 1 };
+enum { FP4R_TS_COMPUTE = 0, FP4R_TS_GIVEN = 1, FP4R_TS_OUTER128 = 2 };
+/* Outer blocks of the double-block mode ([TJ2] 2.A): 128 elements. */
+enum { FP4R_OUTER = 128 };
 enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1 };
 
 typedef struct {
-  int32_t format;   /* FP4R_NVFP4 / FP4R_MXFP4 / FP4R_UFP4 */
-  int32_t block;    /* 16 (NVFP4, UFP4) or 32 (MXFP4) */
+  int32_t format;   /* FP4R_NVFP4 / FP4R_MXFP4 / FP4R_UFP4 / FP4R_MXFP4_OAS */
+  int32_t block;    /* 16 (NVFP4, UFP4) or 32 (MXFP4, MXFP4_OAS) */
   int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
   int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4R_TS_COMPUTE or FP4R_TS_GIVEN (NVFP4/UFP4) */
+  int32_t ts_mode;  /* FP4R_TS_COMPUTE, _GIVEN or _OUTER128 (NVFP4/UFP4) */
   uint64_t rht_seed;
   uint64_t sr_seed;
 } fp4r_params;
@@ -89,6 +91,11 @@ float fp4r_e4m3_decode(uint8_t b);
  * [-127, 127]; amax == 0 gives -127. */
 int fp4r_e8m0_exponent(float amax);
 
+/* Overflow-aware MX exponent ([MXFP4] 2.A): the e that places amax / 2^e
+ * in (3.5, 7], i.e. the smallest e with amax <= 7 * 2^e, clamped to
+ * [-127, 127]; amax == 0 gives -127. */
+int fp4r_e8m0_exponent_oas(float amax);
+
 /* Magnitude code k (0..7) of m >= 0 on a grid, RTNE or SR with draw u16. */
 int fp4r_round_rtne(float m, int grid);
 int fp4r_round_sr(float m, int grid, uint32_t u16);
@@ -99,7 +106,9 @@ float fp4r_level(int grid, int k);
 /* Quantize x (rows x cols, leading dimension ld, BF16 bits or FP32).
  * codes: rows_A * W / 2 bytes, scales: rows_A * W / block bytes, where the
  * logical operand A is x (ROW) or x^T (COL) and W its row length.
- * tensor_scale: written (COMPUTE) or read (GIVEN) for NVFP4/UFP4.
+ * tensor_scale (NVFP4/UFP4): one float, written (COMPUTE) or read (GIVEN);
+ * with OUTER128, rows_A * W / 128 floats written, the outer scale of each
+ * 128-element piece of an A-row (W must be a multiple of 128).
  * Returns 0 on success, -1 on invalid arguments. */
 int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
                   int64_t ld, const fp4r_params* p, uint8_t* codes,
