@@ -31,8 +31,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
-KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_quantize.hip", "block_scaled_bit_fp4_amd/csrc/fp4_tiles.h",
-                  "block_scaled_bit_fp4_amd/csrc/fp4_device.h"]
+KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/" + f for f in (
+    "fp4_quantize.h", "fp4_quantize_nvfp4.hip", "fp4_quantize_mxfp4.hip", "fp4_quantize_ufp4.hip",
+    "fp4_quantize_mxfp4_oas.hip", "fp4_tiles.h", "fp4_device.h")]
+MX = ("mxfp4", "mxfp4_oas")
 
 
 def kernel_source_hash() -> str:
@@ -43,12 +45,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int) -> int:
+def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int, outer: bool = False) -> int:
     """Bytes the method must move once: the input, the packed codes, one
-    scale byte per block, and the FP32 tensor scale for two-level formats."""
+    scale byte per block, and for the two-level formats the FP32 tensor
+    scale, or one FP32 outer scale per 128 elements (double block)."""
     n = rows * cols
-    block = 32 if fmt == "mxfp4" else 16
-    return n * in_bytes + n // 2 + n // block + (0 if fmt == "mxfp4" else 4)
+    if fmt in MX:
+        return n * in_bytes + n // 2 + n // 32
+    return n * in_bytes + n // 2 + n // 16 + (4 * (n // 128) if outer else 4)
+
+
+def call_label(c) -> str:
+    return "%s %s %s %s rht=%s%s" % (c.tensor, c.fmt, c.axis, c.rounding, c.rht,
+                                     " outer128" if c.outer else "")
 
 
 def traffic_for(workload: str, call_index: int):
@@ -119,7 +128,7 @@ def cpu_baseline(w, tensors, budget_s=12.0):
         for call in w.calls:
             x = tensors[call.tensor]
             oracle.quantize(x, call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
-                            call.sr_seed)
+                            call.sr_seed, outer=call.outer)
             nbytes += x.size * x.itemsize
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -188,15 +197,15 @@ def main():
         rows, cols = x.shape
         cs, ss = fp4.output_shapes(rows, cols, call.fmt, call.axis)
         p = fp4.make_params(call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
-                            call.sr_seed)
-        nws = fp4.workspace_bytes(rows, cols, p)
+                            call.sr_seed, outer=call.outer)
+        ts_shape = fp4.outer_shape(rows, cols, call.axis) if call.outer else (1,)
         plans.append(dict(
             call=call, x=x,
             codes=torch.empty(cs, dtype=torch.uint8, device=dev),
             scales=torch.empty(ss, dtype=torch.uint8, device=dev),
-            ts=torch.empty(1, dtype=torch.float32, device=dev),
+            ts=torch.empty(ts_shape, dtype=torch.float32, device=dev),
             ws=fp4.new_workspace(rows, cols, p, dev),
-            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size()),
+            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size(), call.outer),
             in_bytes=x.numel() * x.element_size()))
     stream = torch.cuda.current_stream()
 
@@ -204,7 +213,7 @@ def main():
         c = pl["call"]
         fp4.quantize(pl["x"], c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed,
                      codes=pl["codes"], scales=pl["scales"], ts_out=pl["ts"],
-                     workspace=pl["ws"], stream=stream)
+                     workspace=pl["ws"], stream=stream, outer=c.outer)
 
     def step():
         for pl in plans:
@@ -247,8 +256,9 @@ def main():
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload, dom),
-        "kernel": "fp4_quantize call %d (%s %s %s rht=%s): tensor-amax + quantize kernels"
-                  % (dom, c.fmt, c.axis, c.rounding, c.rht),
+        "kernel": "fp4_quantize call %d (%s): %s" % (
+            dom, call_label(c), "quantize kernel" if (c.fmt in MX or c.outer)
+            else "tensor-amax + quantize kernels"),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
 
     if args.copy_mib:
@@ -277,8 +287,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description,
                    "tensors": {k: list(v.shape) for k, v in tensors.items()},
-                   "calls": ["%s %s %s %s rht=%s" % (c.tensor, c.fmt, c.axis, c.rounding, c.rht)
-                             for c in w.calls],
+                   "calls": [call_label(c) for c in w.calls],
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
                    "per_call_us": [round(m * 1e3, 2) for m in per_call],
                    "wall_ms_per_step": round(wall_ms, 4)},

@@ -9,7 +9,11 @@ there is no CPU fallback, and importing the library fails loudly when
 
 Formats: ``"nvfp4"`` (E2M1, 16-element blocks, E4M3 scale, FP32 tensor
 scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
-(uniform 0..7 grid, 16-element blocks, E4M3 scale, FP32 tensor scale).
+(uniform 0..7 grid, 16-element blocks, E4M3 scale, FP32 tensor scale),
+``"mxfp4_oas"`` (MXFP4 with overflow-aware E8M0 scales).  NVFP4 and the
+uniform grid also take double-block scales (``outer=True``): one FP32 outer
+scale per 128 elements of each row of the quantized operand instead of the
+tensor scale.
 """
 from __future__ import annotations
 
@@ -22,8 +26,11 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4.so")
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32}
+MX = ("mxfp4", "mxfp4_oas")
+OUTER = 128  # elements per outer scale (double-block mode)
+TS_COMPUTE, TS_GIVEN, TS_OUTER128 = 0, 1, 2
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
@@ -87,9 +94,10 @@ def load():
 
 
 def make_params(fmt="nvfp4", axis="row", rounding="rtne", rht=False, rht_seed=0, sr_seed=0,
-                ts_given=False) -> Params:
+                ts_given=False, outer=False) -> Params:
+    mode = TS_OUTER128 if outer else (TS_GIVEN if ts_given else TS_COMPUTE)
     return Params(FORMATS[fmt], BLOCK[fmt], AXES[axis], ROUNDINGS[rounding], int(bool(rht)),
-                  1 if ts_given else 0, int(rht_seed) & (2**64 - 1), int(sr_seed) & (2**64 - 1))
+                  mode, int(rht_seed) & (2**64 - 1), int(sr_seed) & (2**64 - 1))
 
 
 def _stream(stream) -> int:
@@ -129,22 +137,31 @@ def output_shapes(rows: int, cols: int, fmt: str, axis: str):
     return (ra, w // 2), (ra, w // BLOCK[fmt])
 
 
+def outer_shape(rows: int, cols: int, axis: str):
+    """Shape of the outer-scale array of the double-block mode."""
+    ra, w = (rows, cols) if axis == "row" else (cols, rows)
+    return (ra, w // OUTER)
+
+
 def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: str = "rtne",
              rht: bool = False, rht_seed: int = 0, sr_seed: int = 0,
              tensor_scale=None, codes: Optional[torch.Tensor] = None,
              scales: Optional[torch.Tensor] = None, ts_out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, stream=None):
+             workspace: Optional[torch.Tensor] = None, stream=None, outer: bool = False):
     """Quantize a BF16/FP32 device matrix.  Returns (codes, scales, tensor_scale).
 
     ``tensor_scale``: None computes the NVFP4/UFP4 tensor scale from the data;
     a float or one-element float32 device tensor supplies it.  The returned
-    tensor scale is a one-element float32 device tensor (None for MXFP4)."""
+    tensor scale is a one-element float32 device tensor (None for the MX
+    formats).  ``outer=True`` selects double-block scales: the third result
+    is then the float32 outer-scale array of shape ``outer_shape()``."""
     _check_2d(x, "x")
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    given = tensor_scale is not None
-    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given)
+    outer = bool(outer) and fmt not in MX
+    given = tensor_scale is not None and not outer
+    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
     cshape, sshape = output_shapes(rows, cols, fmt, axis)
     dev = x.device
     if codes is None:
@@ -152,7 +169,10 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     if scales is None:
         scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
     ts = None
-    if fmt != "mxfp4":
+    if outer:
+        ts = ts_out if ts_out is not None else torch.empty(
+            outer_shape(rows, cols, axis), dtype=torch.float32, device=dev)
+    elif fmt not in MX:
         if given:
             ts = tensor_scale if torch.is_tensor(tensor_scale) else torch.tensor(
                 [float(tensor_scale)], dtype=torch.float32, device=dev)
@@ -174,8 +194,10 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: in
                fmt: str = "nvfp4", axis: str = "row", rht: bool = False, rht_seed: int = 0,
                inverse_rht: bool = False, out_dtype=torch.float32,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Rebuild a rows x cols matrix (x's layout) from codes and scales."""
-    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, True)
+    """Rebuild a rows x cols matrix (x's layout) from codes and scales.  A 2-D
+    ``tensor_scale`` is the outer-scale array of the double-block mode."""
+    outer = torch.is_tensor(tensor_scale) and tensor_scale.dim() == 2
+    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, not outer, outer)
     if out is None:
         out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
     if out.dtype not in DTYPES:

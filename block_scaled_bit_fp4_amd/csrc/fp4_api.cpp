@@ -48,15 +48,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_size(int32_t dt) { return dt == FP4_BF16 ? 2 : 4; }
 
+bool is_mx(int32_t format) { return format == FP4_MXFP4 || format == FP4_MXFP4_OAS; }
+
+bool two_level(const fp4_params* p) { return !is_mx(p->format); }
+
+bool outer_scales(const fp4_params* p) {
+  return two_level(p) && p->ts_mode == FP4_TS_OUTER128;
+}
+
 fp4_status check_params(const fp4_params* p) {
   if (!p) return FP4_ERR_NULL;
-  if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4)
+  if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4 &&
+      p->format != FP4_MXFP4_OAS)
     return FP4_ERR_FORMAT;
-  if (p->block != (p->format == FP4_MXFP4 ? 32 : 16)) return FP4_ERR_FORMAT;
+  if (p->block != (is_mx(p->format) ? 32 : 16)) return FP4_ERR_FORMAT;
   if (p->axis != FP4_AXIS_ROW && p->axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
   if (p->rounding != FP4_RTNE && p->rounding != FP4_SR) return FP4_ERR_FORMAT;
   if (p->rht != 0 && p->rht != 1) return FP4_ERR_FORMAT;
-  if (p->format != FP4_MXFP4 && p->ts_mode != FP4_TS_COMPUTE && p->ts_mode != FP4_TS_GIVEN)
+  if (two_level(p) && p->ts_mode != FP4_TS_COMPUTE && p->ts_mode != FP4_TS_GIVEN &&
+      p->ts_mode != FP4_TS_OUTER128)
     return FP4_ERR_FORMAT;
   return FP4_OK;
 }
@@ -66,10 +76,9 @@ fp4_status check_shape(const fp4_params* p, int64_t rows, int64_t cols, int64_t 
   const int64_t W = p->axis == FP4_AXIS_ROW ? cols : rows;
   if (W % p->block) return FP4_ERR_SHAPE;
   if (p->rht && (W % 16)) return FP4_ERR_SHAPE;
+  if (outer_scales(p) && (W % 128)) return FP4_ERR_SHAPE;
   return FP4_OK;
 }
-
-bool two_level(const fp4_params* p) { return p->format != FP4_MXFP4; }
 
 bool needs_workspace(const fp4_params* p) {
   return two_level(p) && p->ts_mode == FP4_TS_COMPUTE;
@@ -127,7 +136,7 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   q.axis = p->axis;
   q.sr = p->rounding == FP4_SR;
   q.rht = p->rht;
-  q.ts_given = two_level(p) && p->ts_mode == FP4_TS_GIVEN;
+  q.ts_mode = two_level(p) ? p->ts_mode : FP4_TS_COMPUTE;
   q.signs = p->rht ? fp4_rht_signs(p->rht_seed) : 0u;
   q.sr_k0 = (uint32_t)p->sr_seed;
   q.sr_k1 = (uint32_t)(p->sr_seed >> 32);
@@ -163,6 +172,7 @@ fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales,
   q.format = p->format;
   q.axis = p->axis;
   q.inverse_rht = inverse_rht;
+  q.outer = outer_scales(p);
   q.signs = p->rht ? fp4_rht_signs(p->rht_seed) : 0u;
   q.out = out;
   q.out_dtype = out_dtype;
@@ -195,6 +205,19 @@ fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, 
   q.y = y;
   return finish(fp4_launch_rht(q, s), s);
 }
+
+}  // extern "C"
+
+hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
+  switch (q.format) {
+    case FP4_NVFP4: return fp4_launch_quantize_nvfp4(q, s);
+    case FP4_MXFP4: return fp4_launch_quantize_mxfp4(q, s);
+    case FP4_UFP4: return fp4_launch_quantize_ufp4(q, s);
+    default: return fp4_launch_quantize_mxfp4_oas(q, s);
+  }
+}
+
+extern "C" {
 
 const char* fp4_status_str(fp4_status s) {
   switch (s) {

@@ -55,10 +55,10 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) {
   *p = (uint16_t)(u >> 16);
 }
 
-template <int FMT, bool INV, int AXIS, typename T>
+template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ out, DequantArgs a) {
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
-  const float s_t = FMT == kMXFP4 ? 0.0f : a.ts[0];
+  constexpr int B = block_of<FMT>();
+  const float s_t = (is_mx(FMT) || OUTER) ? 0.0f : a.ts[0];
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
   while (w.major < a.n_major) {
@@ -66,8 +66,13 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
     const int64_t b = AXIS == 0 ? w.minor : w.major;
     const uint32_t S = a.scales[ra * (a.W / B) + b];
     float d;
-    if constexpr (FMT == kMXFP4) d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
-    else d = S ? s_t * e4m3_decode(S) : 0.0f;
+    if constexpr (is_mx(FMT)) {
+      d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
+    } else {
+      // outer scales: the 128-piece of the A-row that holds block b
+      const float so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : s_t;
+      d = S ? so * e4m3_decode(S) : 0.0f;
+    }
     const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
     uint32_t words[B / 8];
     if constexpr (B == 16) {
@@ -147,31 +152,36 @@ inline WalkPlan plan_walk(int64_t n_major, int64_t M, int64_t cap) {
   return {(unsigned)g, stride / M, stride % M};
 }
 
-template <int FMT, bool INV, int AXIS, typename T>
+template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 hipError_t launch_dequant_t(const DequantLaunch& q, hipStream_t s) {
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int B = block_of<FMT>();
   const int64_t W = AXIS == 0 ? q.cols : q.rows;
   const int64_t RA = AXIS == 0 ? q.rows : q.cols;
   const int64_t nmaj = AXIS == 0 ? RA : W / B;
   const int64_t M = AXIS == 0 ? W / B : RA;
   const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
   DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, nmaj, M, wp.sq, wp.sr, q.signs};
-  hipLaunchKernelGGL((dequantize_kernel<FMT, INV, AXIS, T>), dim3(wp.grid), dim3(kThreads), 0, s,
-                     static_cast<T*>(q.out), a);
+  hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, AXIS, T>), dim3(wp.grid),
+                     dim3(kThreads), 0, s, static_cast<T*>(q.out), a);
   return hipGetLastError();
 }
-template <int FMT, bool INV, int AXIS>
+template <int FMT, bool OUTER, bool INV, int AXIS>
 hipError_t dq_dtype(const DequantLaunch& q, hipStream_t s) {
-  return q.out_dtype == 0 ? launch_dequant_t<FMT, INV, AXIS, uint16_t>(q, s)
-                          : launch_dequant_t<FMT, INV, AXIS, float>(q, s);
+  return q.out_dtype == 0 ? launch_dequant_t<FMT, OUTER, INV, AXIS, uint16_t>(q, s)
+                          : launch_dequant_t<FMT, OUTER, INV, AXIS, float>(q, s);
 }
-template <int FMT, bool INV>
+template <int FMT, bool OUTER, bool INV>
 hipError_t dq_axis(const DequantLaunch& q, hipStream_t s) {
-  return q.axis == 0 ? dq_dtype<FMT, INV, 0>(q, s) : dq_dtype<FMT, INV, 1>(q, s);
+  return q.axis == 0 ? dq_dtype<FMT, OUTER, INV, 0>(q, s) : dq_dtype<FMT, OUTER, INV, 1>(q, s);
+}
+template <int FMT, bool OUTER>
+hipError_t dq_inv(const DequantLaunch& q, hipStream_t s) {
+  return q.inverse_rht ? dq_axis<FMT, OUTER, true>(q, s) : dq_axis<FMT, OUTER, false>(q, s);
 }
 template <int FMT>
-hipError_t dq_inv(const DequantLaunch& q, hipStream_t s) {
-  return q.inverse_rht ? dq_axis<FMT, true>(q, s) : dq_axis<FMT, false>(q, s);
+hipError_t dq_outer(const DequantLaunch& q, hipStream_t s) {
+  if constexpr (is_mx(FMT)) return dq_inv<FMT, false>(q, s);
+  else return q.outer ? dq_inv<FMT, true>(q, s) : dq_inv<FMT, false>(q, s);
 }
 
 template <bool INV, int AXIS, typename T>
@@ -200,9 +210,10 @@ hipError_t rht_axis(const RhtLaunch& q, hipStream_t s) {
 
 hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
   switch (q.format) {
-    case kNVFP4: return dq_inv<kNVFP4>(q, s);
-    case kMXFP4: return dq_inv<kMXFP4>(q, s);
-    default: return dq_inv<kUFP4>(q, s);
+    case kNVFP4: return dq_outer<kNVFP4>(q, s);
+    case kMXFP4: return dq_outer<kMXFP4>(q, s);
+    case kUFP4: return dq_outer<kUFP4>(q, s);
+    default: return dq_outer<kMXOAS>(q, s);
   }
 }
 

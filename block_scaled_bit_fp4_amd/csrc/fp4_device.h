@@ -17,7 +17,16 @@
 
 namespace fp4dev {
 
-enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2 };
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3 };
+// Tensor-scale modes of the two-level formats: computed from the data,
+// given by the caller, or one outer scale per kOuter elements of an A-row.
+enum : int { kTsCompute = 0, kTsGiven = 1, kTsOuter = 2 };
+constexpr int kOuter = 128;
+
+// E8M0-scaled formats (power-of-two block scales, no tensor scale).
+constexpr bool is_mx(int fmt) { return fmt == kMXFP4 || fmt == kMXOAS; }
+template <int FMT>
+constexpr int block_of() { return is_mx(FMT) ? 32 : 16; }
 
 // ---------------------------------------------------------------- widening
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -133,6 +142,17 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 __device__ __forceinline__ int e8m0_exponent(float amax) {
   const int ex = (int)(__float_as_uint(amax) >> 23);
   const int e = ex - 129;
+  return (ex == 0 || e < -127) ? -127 : e;
+}
+
+// Overflow-aware MX exponent ([MXFP4] 2.A): amax / 2^e in (3.5, 7].  From
+// the standard e, amax / 2^e = 4 * 1.f lies in [4, 8); it exceeds 7 exactly
+// when the significand 1.f exceeds 1.75 (fraction bits above 0x600000), and
+// then e grows by one.  Zero and subnormal amax land on -127.
+__device__ __forceinline__ int e8m0_exponent_oas(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ex = (int)(b >> 23);
+  const int e = ex - 129 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
   return (ex == 0 || e < -127) ? -127 : e;
 }
 

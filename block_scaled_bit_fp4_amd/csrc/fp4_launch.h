@@ -14,7 +14,8 @@ struct QuantLaunch {
   const void* x;
   int in_dtype;  // 0 bf16, 1 f32
   int64_t rows, cols, ld;
-  int format, axis, sr, rht, ts_given;
+  int format, axis, sr, rht;
+  int ts_mode;  // two-level formats: 0 computed, 1 given, 2 outer scales per 128
   uint32_t signs;
   uint32_t sr_k0, sr_k1;
   uint8_t* codes;
@@ -29,6 +30,7 @@ struct DequantLaunch {
   const float* tensor_scale;
   int64_t rows, cols;
   int format, axis, inverse_rht;
+  int outer;  // tensor_scale holds one outer scale per 128 elements of an A-row
   uint32_t signs;
   void* out;
   int out_dtype;  // 0 bf16, 1 f32
@@ -45,6 +47,11 @@ struct RhtLaunch {
 };
 
 hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s);
+// per-format instantiations (fp4_quantize_<format>.hip)
+hipError_t fp4_launch_quantize_nvfp4(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_mxfp4(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_ufp4(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_mxfp4_oas(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s);
 hipError_t fp4_launch_write_scalar(float* p, float v, hipStream_t s);

@@ -1,4 +1,5 @@
-// fp4_quantize.hip -- gfx950 kernels of the quantize path and its launcher.
+// fp4_quantize.h -- gfx950 kernels of the quantize path and their launcher,
+// instantiated per format by fp4_quantize_<format>.hip (parallel builds).
 //
 // Terms: x is the caller's rows x cols tensor (row-major, leading dimension
 // ld).  The logical operand A is x (row axis) or x^T (column axis); W is the
@@ -10,7 +11,9 @@
 // Two-level formats (NVFP4, uniform grid) need the tensor amax of the
 // rotated operand before any block can be coded: a first kernel writes one
 // partial maximum per workgroup, and every workgroup of the quantize kernel
-// reduces them.  MXFP4 and a given tensor scale skip that pass.
+// reduces them.  The MX formats, a given tensor scale and outer scales (one
+// per 128-piece of an A-row, reduced across the lanes that hold the piece)
+// skip that pass.
 //
 // Row axis: a lane owns a 32-element (or 16-element) piece of an A-row,
 // read with 16-byte loads; the next piece's loads are issued before the
@@ -18,6 +21,8 @@
 // (A-rows) and a run of NB consecutive blocks down them; each row of a
 // block is one 2C- or 4C-byte load, so a wave reads one contiguous segment
 // per row, and each lane writes NB*B/2 contiguous code bytes per column.
+#pragma once
+
 #include <mutex>
 #include <type_traits>
 #include <unordered_map>
@@ -89,9 +94,9 @@ struct QuantArgs {
   int64_t col_begin;           // column axis: first column of this launch
   uint8_t* codes;
   uint8_t* scales;
-  const float* ts_in;      // given tensor scale (GIVEN mode)
-  float* ts_out;           // computed tensor scale (COMPUTE mode)
-  const float* partials;   // amax partials (COMPUTE mode)
+  const float* ts_in;      // given tensor scale (kTsGiven)
+  float* ts_out;           // computed tensor scale, or outer scales (kTsOuter)
+  const float* partials;   // amax partials (kTsCompute)
   int npartials;
   uint32_t signs;
   uint32_t sr_k0, sr_k1;
@@ -104,11 +109,13 @@ struct ScaleCtx {
 
 // Tensor scale s_t = amax / (G * 448) and, in LDS, the reciprocal of every
 // decoded block scale: inv[S] = 1 / (s_t * decode(S)), 0 where that is 0.
-template <int FMT, bool GIVEN>
+// Nothing for the MX formats and for outer scales (per 128-piece, coded
+// with the blocks).
+template <int FMT, int TSM>
 __device__ __forceinline__ ScaleCtx scale_prologue(const QuantArgs& a, float* inv_tab) {
   ScaleCtx c{0.0f, 0.0f};
-  if constexpr (FMT != kMXFP4) {
-    if (GIVEN) {
+  if constexpr (!is_mx(FMT) && TSM != kTsOuter) {
+    if (TSM == kTsGiven) {
       c.s_t = a.ts_in[0];
     } else {
       float m = 0.0f;
@@ -211,11 +218,14 @@ __device__ __forceinline__ uint32_t encode8_careful(const float* y, float inv,
 // plain values, amax_t their largest magnitude, n0 the logical index of the
 // first element (SR draws).
 // Two-level formats ([TJ2] 2.A; [NGPT] per-tensor dynamic scaling):
-//   r = amax_b / (s_t * G), S = E4M3(r), d = s_t * decode(S), v = y * (1/d).
-// MXFP4 ([MXFP4] 2): d = 2^e, e = floor(log2 amax_b) - 2.
+//   r = amax_b / (s_t * G), S = E4M3(r), d = s_t * decode(S), v = y * (1/d);
+// with outer scales ([TJ2] 2.A double block) c holds the 128-piece's scale
+// in place of s_t and 1/d is computed here instead of read from the table.
+// MXFP4 ([MXFP4] 2): d = 2^e, e = floor(log2 amax_b) - 2; overflow-aware
+// ([MXFP4] 2.A): e places amax_b / 2^e in (3.5, 7].
 // With BF16 input every RHT partial sum is a multiple of 2^-133, so y = t/4
 // is exact and, while inv >= 2^-124, v = t * (inv / 4) equals y * inv.
-template <int FMT, bool SR, bool RHT, bool BF16IN, int B>
+template <int FMT, bool SR, bool RHT, bool BF16IN, int B, int TSM>
 __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, const ScaleCtx& c,
                                              const float* inv_tab, uint32_t k0, uint32_t k1,
                                              uint64_t n0, uint32_t (&packed)[B / 8],
@@ -223,13 +233,18 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
   constexpr bool kFold = RHT && BF16IN;
   const float amax_b = RHT ? amax_t * 0.25f : amax_t;
   float inv;
-  if constexpr (FMT == kMXFP4) {
-    const int e = e8m0_exponent(amax_b);
+  if constexpr (is_mx(FMT)) {
+    const int e = FMT == kMXOAS ? e8m0_exponent_oas(amax_b) : e8m0_exponent(amax_b);
     sbyte = (uint32_t)(e + 127);
     inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
   } else {
     sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
-    inv = inv_tab[sbyte];
+    if constexpr (TSM == kTsOuter) {
+      const float d = sbyte ? c.s_t * e4m3_decode(sbyte) : 0.0f;
+      inv = d != 0.0f ? 1.0f / d : 0.0f;
+    } else {
+      inv = inv_tab[sbyte];
+    }
   }
   // E2M1 stochastic rounding in encode8_fast needs |v| < 2^126.
   const float limit = (SR && FMT != kUFP4) ? 0x1p126f : __builtin_inff();
@@ -267,10 +282,10 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
 
 // ------------------------------------------------------------- row axis
 // Units: major = A-row, minor = piece of U elements within it.
-template <int FMT, bool SR, bool RHT, bool GIVEN, typename T, int U>
+template <int FMT, bool SR, bool RHT, int TSM, typename T, int U>
 __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restrict__ x,
                                                                 QuantArgs a) {
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int B = block_of<FMT>();
   constexpr int NBU = U / B;  // blocks per unit
   __shared__ float inv_tab[128];
   Walk w;
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
   RowRaw<T, U> cur;
   bool have = w.major < a.n_major;
   if (have) cur.load(x + w.major * a.ld + w.minor * U);  // in flight during the prologue
-  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
   while (have) {
     Walk nw = w;
     nw.advance(a.sq, a.sr, a.M);
@@ -288,10 +303,9 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
 
     uint32_t packed[U / 8];
     uint32_t sb[NBU];
-#pragma unroll
-    for (int bi = 0; bi < NBU; ++bi) {
-      float t[B];
-      float amax_t = 0.0f;
+    // widened (and rotated) block bi of the unit, with its largest magnitude
+    auto block_values = [&](int bi, float (&t)[B], float& amax_t) {
+      amax_t = 0.0f;
 #pragma unroll
       for (int h = 0; h < B / 16; ++h) {
         float g[16];
@@ -303,12 +317,41 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
           amax_t = fmaxf(amax_t, fabsf(g[j]));
         }
       }
+    };
+    auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
       const uint64_t n0 = (uint64_t)w.major * (uint64_t)a.W + (uint64_t)(w.minor * U + bi * B);
       uint32_t pk[B / 8];
-      encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1, n0,
-                                                     pk, sb[bi]);
+      encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
+                                                         a.sr_k1, n0, pk, sb[bi]);
 #pragma unroll
       for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
+    };
+    if constexpr (TSM == kTsOuter) {
+      // kOuter / U consecutive lanes hold one 128-piece of an A-row (the
+      // walk keeps them in step): their maxima combine by lane exchange.
+      constexpr int LPO = kOuter / U;
+      float t[NBU][B], am[NBU];
+      float ao = 0.0f;
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) {
+        block_values(bi, t[bi], am[bi]);
+        ao = fmaxf(ao, am[bi]);
+      }
+#pragma unroll
+      for (int o = 1; o < LPO; o <<= 1) ao = fmaxf(ao, __shfl_xor(ao, o));
+      ScaleCtx co;
+      co.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+      co.den = co.s_t * grid_max<FMT>();
+      if (w.minor % LPO == 0) a.ts_out[w.major * (a.W / kOuter) + w.minor / LPO] = co.s_t;
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) {
+        float t[B], amax_t;
+        block_values(bi, t, amax_t);
+        code(bi, t, amax_t, c);
+      }
     }
     uint8_t* cp = a.codes + w.major * (a.W / 2) + w.minor * (U / 2);
     if constexpr (U >= 32) {
@@ -336,13 +379,13 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
 
 // ---------------------------------------------------------- column axis
 // Units: major = run of NB blocks down the rows, minor = group of C columns.
-template <int FMT, bool SR, bool RHT, bool GIVEN, typename T, int C, int NB>
+template <int FMT, bool SR, bool RHT, int TSM, typename T, int C, int NB>
 __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restrict__ x,
                                                                 QuantArgs a) {
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int B = block_of<FMT>();
   constexpr int WPB = B / 8;  // code words per block
   __shared__ float inv_tab[128];
-  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
   const bool vec_codes = (a.W % 32) == 0;  // 16-byte aligned A-rows of codes
 
   Walk w;
@@ -358,6 +401,38 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
 #pragma unroll
       for (int i = 0; i < (NB + 3) / 4; ++i) sbw[k][i] = 0u;
     const T* base = x + blk0 * B * a.ld + col;
+    // outer scales: the run is one 128-piece of each of the C A-rows; a
+    // first pass over it takes the piece maxima
+    ScaleCtx co[C];
+    if constexpr (TSM == kTsOuter) {
+      static_assert(NB * B == kOuter, "one outer piece per run");
+      float ao[C];
+#pragma unroll
+      for (int k = 0; k < C; ++k) ao[k] = 0.0f;
+#pragma unroll 1
+      for (int j = 0; j < NB; ++j) {
+        ColRaw<T, C> g;
+        g.load(base + (int64_t)j * B * a.ld, a.ld);
+        if (RHT) g.flip_rows(a.signs);
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+          float t[16];
+          g.column(k, t);
+          if (RHT) fwht16(t);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ao[k] = fmaxf(ao[k], fabsf(t[i]));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < C; ++k) {
+        co[k].s_t = (RHT ? ao[k] * 0.25f : ao[k]) / (grid_max<FMT>() * 448.0f);
+        co[k].den = co[k].s_t * grid_max<FMT>();
+        a.ts_out[(col + k) * (a.W / kOuter) + blk0 * B / kOuter] = co[k].s_t;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C; ++k) co[k] = c;
+    }
     ColRaw<T, C> cur[B / 16];
 #pragma unroll
     for (int h = 0; h < B / 16; ++h) cur[h].load(base + (int64_t)h * 16 * a.ld, a.ld);
@@ -388,8 +463,8 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
           const uint64_t n0 = (uint64_t)(col + k) * (uint64_t)a.W + (uint64_t)((blk0 + j) * B);
           uint32_t pk[WPB];
           uint32_t sbyte;
-          encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1,
-                                                         n0, pk, sbyte);
+          encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, co[k], inv_tab, a.sr_k0,
+                                                              a.sr_k1, n0, pk, sbyte);
           sbw[k][j / 4] |= sbyte << (8 * (j % 4));
 #pragma unroll
           for (int q = 0; q < WPB; ++q) codes[k][j * WPB + q] = pk[q];
@@ -458,11 +533,11 @@ struct ColTile {
   }
 };
 
-template <int FMT, bool SR, bool RHT, bool GIVEN, typename T>
+template <int FMT, bool SR, bool RHT, int TSM, typename T>
 __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T* __restrict__ x,
                                                                      QuantArgs a) {
   using Tile = ColTile<T>;
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int B = block_of<FMT>();
   constexpr int TR = Tile::TR, TC = Tile::TC;
   constexpr int kLoads = TR * TC * (int)sizeof(T) / 16 / kThreads;  // 16-byte loads per lane
   constexpr int kUnits = TC * (TR / B) / kThreads;                  // blocks coded per lane
@@ -491,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   bool have = tile < ntile;
   uint4 buf[kLoads];
   if (have) load_tile(tile, buf);  // in flight during the prologue
-  const ScaleCtx c = scale_prologue<FMT, GIVEN>(a, inv_tab);
+  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
   while (have) {
     const int64_t tr = tile / a.M, tc = tile - tr * a.M;
     const int64_t r0 = tr * TR, c0 = tc * TC;
@@ -558,10 +633,21 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
       const int64_t ra = c0 + cl;                 // A-row = column of x
       const int64_t rb = r0 / B + j;              // block index along the A-row
       const uint64_t n0 = (uint64_t)ra * (uint64_t)a.W + (uint64_t)(rb * B);
+      ScaleCtx cc = c;
+      if constexpr (TSM == kTsOuter) {
+        // kOuter / B consecutive lanes hold the blocks of one 128-piece
+        constexpr int LPO = kOuter / B;
+        float ao = amax_t;
+#pragma unroll
+        for (int o = 1; o < LPO; o <<= 1) ao = fmaxf(ao, __shfl_xor(ao, o));
+        cc.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+        cc.den = cc.s_t * grid_max<FMT>();
+        if (j % LPO == 0) a.ts_out[ra * (a.W / kOuter) + rb / LPO] = cc.s_t;
+      }
       uint32_t pk[B / 8];
       uint32_t sbyte;
-      encode_block<FMT, SR, RHT, sizeof(T) == 2, B>(t, amax_t, c, inv_tab, a.sr_k0, a.sr_k1, n0,
-                                                     pk, sbyte);
+      encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
+                                                         a.sr_k1, n0, pk, sbyte);
       uint8_t* cp = a.codes + ra * (a.W / 2) + rb * (B / 2);
       if constexpr (B == 16) *reinterpret_cast<uint2*>(cp) = make_uint2(pk[0], pk[1]);
       else *reinterpret_cast<uint4*>(cp) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
@@ -664,11 +750,11 @@ void launch_amax(const QuantLaunch& q, hipStream_t s) {
   }
 }
 
-template <int FMT, bool SR, bool RHT, bool GIVEN, typename T>
+template <int FMT, bool SR, bool RHT, int TSM, typename T>
 hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
-  constexpr int B = FMT == kMXFP4 ? 32 : 16;
+  constexpr int B = block_of<FMT>();
   const T* x = static_cast<const T*>(q.x);
-  if (FMT != kMXFP4 && !GIVEN) launch_amax<RHT, T>(q, s);
+  if (!is_mx(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
   QuantArgs a{};
   a.ld = q.ld;
   a.codes = q.codes;
@@ -695,11 +781,11 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       hipLaunchKernelGGL(kernel, dim3(wp.grid), dim3(kThreads), 0, s, x, a);
     };
     if (wider)
-      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 64>);
+      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 64>);
     else if (wide)
-      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 32>);
+      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 32>);
     else if constexpr (B == 16)
-      launch(quantize_row_kernel<FMT, SR, RHT, GIVEN, T, 16>);
+      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 16>);
   } else {
     a.W = q.rows;
     a.nblk_axis = q.rows / B;
@@ -717,11 +803,13 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       // more workgroups than fit at once measured faster here than one
       // resident wave
       const unsigned grid = (unsigned)(ntile < kColGrid ? ntile : kColGrid);
-      hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, GIVEN, T>), dim3(grid),
+      hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, TSM, T>), dim3(grid),
                          dim3(kThreads), 0, s, x, t);
     }
     // runs of 128 rows (64 with SR, whose Philox state needs the registers)
-    constexpr int NB = (B == 16 ? kColBlocks : kColBlocks / 2) / (SR ? 2 : 1);
+    // (one 128-piece per run with outer scales)
+    constexpr int NB = TSM == kTsOuter ? kOuter / B
+                                       : (B == 16 ? kColBlocks : kColBlocks / 2) / (SR ? 2 : 1);
     auto run = [&](int64_t blk_begin, int64_t blk_end, int64_t col_begin, int64_t col_end) {
       if (blk_end <= blk_begin || col_end <= col_begin) return;
       QuantArgs r = a;
@@ -735,10 +823,10 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       r.sq = wp.sq;
       r.sr = wp.sr;
       if (C == 2)
-        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, GIVEN, T, 2, NB>), dim3(wp.grid),
+        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 2, NB>), dim3(wp.grid),
                            dim3(kThreads), 0, s, x, r);
       else
-        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, GIVEN, T, 1, NB>), dim3(wp.grid),
+        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 1, NB>), dim3(wp.grid),
                            dim3(kThreads), 0, s, x, r);
     };
     // right strip over the tiled rows, then the bottom strip over all columns
@@ -748,30 +836,30 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, bool SR, bool RHT, bool GIVEN>
+template <int FMT, bool SR, bool RHT, int TSM>
 hipError_t pick_dtype(const QuantLaunch& q, hipStream_t s) {
-  return q.in_dtype == 0 ? launch_quantize_t<FMT, SR, RHT, GIVEN, uint16_t>(q, s)
-                         : launch_quantize_t<FMT, SR, RHT, GIVEN, float>(q, s);
+  return q.in_dtype == 0 ? launch_quantize_t<FMT, SR, RHT, TSM, uint16_t>(q, s)
+                         : launch_quantize_t<FMT, SR, RHT, TSM, float>(q, s);
 }
 template <int FMT, bool SR, bool RHT>
-hipError_t pick_given(const QuantLaunch& q, hipStream_t s) {
-  return q.ts_given ? pick_dtype<FMT, SR, RHT, true>(q, s) : pick_dtype<FMT, SR, RHT, false>(q, s);
+hipError_t pick_tsm(const QuantLaunch& q, hipStream_t s) {
+  if constexpr (is_mx(FMT)) {
+    return pick_dtype<FMT, SR, RHT, kTsCompute>(q, s);  // no tensor scale
+  } else {
+    switch (q.ts_mode) {
+      case kTsGiven: return pick_dtype<FMT, SR, RHT, kTsGiven>(q, s);
+      case kTsOuter: return pick_dtype<FMT, SR, RHT, kTsOuter>(q, s);
+      default: return pick_dtype<FMT, SR, RHT, kTsCompute>(q, s);
+    }
+  }
 }
 template <int FMT, bool SR>
 hipError_t pick_rht(const QuantLaunch& q, hipStream_t s) {
-  return q.rht ? pick_given<FMT, SR, true>(q, s) : pick_given<FMT, SR, false>(q, s);
+  return q.rht ? pick_tsm<FMT, SR, true>(q, s) : pick_tsm<FMT, SR, false>(q, s);
 }
 template <int FMT>
-hipError_t pick_sr(const QuantLaunch& q, hipStream_t s) {
+hipError_t quantize_format(const QuantLaunch& q, hipStream_t s) {
   return q.sr ? pick_rht<FMT, true>(q, s) : pick_rht<FMT, false>(q, s);
 }
 
 }  // namespace
-
-hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
-  switch (q.format) {
-    case kNVFP4: return pick_sr<kNVFP4>(q, s);
-    case kMXFP4: return pick_sr<kMXFP4>(q, s);
-    default: return pick_sr<kUFP4>(q, s);
-  }
-}

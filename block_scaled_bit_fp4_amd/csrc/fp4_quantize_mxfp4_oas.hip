@@ -1,0 +1,7 @@
+// fp4_quantize_mxfp4_oas.hip -- quantize kernels and launcher for one format (the
+// formats build as separate translation units, in parallel).
+#include "fp4_quantize.h"
+
+hipError_t fp4_launch_quantize_mxfp4_oas(const QuantLaunch& q, hipStream_t s) {
+  return quantize_format<kMXOAS>(q, s);
+}

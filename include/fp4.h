@@ -25,7 +25,12 @@
  *    (it/paper/2605.06067), "Enunciato del Problema".
  *  - MXFP4 (32-element blocks, power-of-two E8M0 scale, saturation at the
  *    FP4 limit 6): "Unveiling the Potential of Quantization with MXFP4 ..."
- *    (fr/paper/2603.08713), "2. Methodologie et Analyse" and 2.A.
+ *    (fr/paper/2603.08713), "2. Methodologie et Analyse" and 2.A; its
+ *    overflow-aware scaling (OAS, block amax mapped into (3.5, 7]): same
+ *    page, 2.A.
+ *  - Double-block scaling (an outer scale per 128 elements, inner 16-element
+ *    E4M3 scales, no whole-tensor amax): TetraJet-v2 page, Riepilogo
+ *    Tecnico 2.A.
  *
  * Numerics (one output per input; any launch geometry gives the same bytes):
  *  - A is the logical operand: x (FP4_AXIS_ROW) or x^T (FP4_AXIS_COL); W is
@@ -36,8 +41,11 @@
  *  - NVFP4 (G = 6) / UFP4 (G = 7): s_t = amax|y| / (G * 448) (binary32);
  *    per block S = E4M3_RNE_satfinite(amax_b / (s_t * G)), d = s_t * S;
  *    elements v = y * (1/d) rounded to the grid.  S = 0 or d = 0 gives
- *    signed-zero codes.  MXFP4: d = 2^e, e = floor(log2 amax_b) - 2 clamped
- *    to [-127, 127], scale byte e + 127.
+ *    signed-zero codes.  With FP4_TS_OUTER128, each 128-element piece of an
+ *    A-row has its own s_o = amax_piece / (G * 448), used in place of s_t.
+ *    MXFP4: d = 2^e, e = floor(log2 amax_b) - 2 clamped to [-127, 127],
+ *    scale byte e + 127.  MXFP4_OAS: e is the integer with
+ *    3.5 < amax_b / 2^e <= 7, same clamp and byte.
  *  - Grids: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; UFP4 {0, 1, ..., 7}; values
  *    past the top level saturate.  RTNE ties go to the even code.  SR rounds
  *    up iff u16 < p * 65536, p = (m - L[k]) / (L[k+1] - L[k]); u16 is half of
@@ -51,7 +59,8 @@
  *  - codes: rows_A x (W / 2) bytes; byte (i, j/2) holds A[i][j], even j in
  *    the low nibble.  rows_A = rows (ROW) or cols (COL); W = cols or rows.
  *  - scales: rows_A x (W / B) bytes.
- *  - tensor_scale: one float (NVFP4 / UFP4 only).
+ *  - tensor_scale (NVFP4 / UFP4 only): one float; with FP4_TS_OUTER128,
+ *    rows_A x (W / 128) floats, row-major (requires W % 128 == 0).
  *
  * Ownership and concurrency: the library allocates no memory and keeps no
  * state between calls; all work is enqueued asynchronously on `stream` and
@@ -85,9 +94,10 @@ typedef int32_t fp4_status;
 #define FP4_ERR_WORKSPACE (-6) /* workspace missing or too small */
 #define FP4_ERR_DEVICE (-7)    /* HIP launch failed */
 
-#define FP4_NVFP4 0 /* E2M1, 16-element blocks, E4M3 scale, FP32 tensor scale */
-#define FP4_MXFP4 1 /* E2M1, 32-element blocks, E8M0 scale */
-#define FP4_UFP4 2  /* uniform 0..7 grid, 16-element blocks, E4M3 + FP32 */
+#define FP4_NVFP4 0     /* E2M1, 16-element blocks, E4M3 scale, FP32 tensor scale */
+#define FP4_MXFP4 1     /* E2M1, 32-element blocks, E8M0 scale */
+#define FP4_UFP4 2      /* uniform 0..7 grid, 16-element blocks, E4M3 + FP32 */
+#define FP4_MXFP4_OAS 3 /* MXFP4 with overflow-aware E8M0 scales */
 
 #define FP4_AXIS_ROW 0 /* quantize along rows of x */
 #define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
@@ -98,38 +108,42 @@ typedef int32_t fp4_status;
 #define FP4_BF16 0
 #define FP4_F32 1
 
-#define FP4_TS_COMPUTE 0 /* tensor scale computed from the data, written out */
-#define FP4_TS_GIVEN 1   /* tensor scale read from *tensor_scale */
+#define FP4_TS_COMPUTE 0  /* tensor scale computed from the data, written out */
+#define FP4_TS_GIVEN 1    /* tensor scale read from *tensor_scale */
+#define FP4_TS_OUTER128 2 /* double block: one outer scale per 128 elements */
 
 typedef struct {
-  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 */
-  int32_t block;    /* 16 for NVFP4 and UFP4, 32 for MXFP4 */
+  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 / FP4_MXFP4_OAS */
+  int32_t block;    /* 16 for NVFP4 and UFP4, 32 for MXFP4 and MXFP4_OAS */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4_TS_COMPUTE / FP4_TS_GIVEN (ignored for MXFP4) */
+  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for the MX formats) */
   uint64_t rht_seed;
   uint64_t sr_seed;
 } fp4_params;
 
 /* Bytes of device workspace fp4_quantize needs for this call (0 when none:
- * MXFP4, or a given tensor scale).  Contents need no initialization. */
+ * the MX formats, a given tensor scale, outer scales).  Contents need no
+ * initialization. */
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
 
 /* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
- * scales (layouts above).  tensor_scale is written (COMPUTE) or read
- * (GIVEN) for NVFP4/UFP4 and may be NULL for MXFP4.  workspace must hold
- * fp4_workspace_bytes() bytes.  Requirements: block matches the format; W
- * divisible by the block (and by 16 when rht); ld >= cols; x, codes,
- * scales 16-byte aligned; ld * element size a multiple of 16 bytes.
- * rows == 0 or cols == 0 is valid (COMPUTE writes s_t = 0). */
+ * scales (layouts above).  tensor_scale is written (COMPUTE, OUTER128) or
+ * read (GIVEN) for NVFP4/UFP4 and may be NULL for the MX formats.
+ * workspace must hold fp4_workspace_bytes() bytes.  Requirements: block
+ * matches the format; W divisible by the block (and by 16 when rht, by 128
+ * with OUTER128); ld >= cols; x, codes, scales 16-byte aligned; ld *
+ * element size a multiple of 16 bytes.  rows == 0 or cols == 0 is valid
+ * (COMPUTE writes s_t = 0). */
 fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
                         int64_t ld, const fp4_params* p, uint8_t* codes, uint8_t* scales,
                         float* tensor_scale, void* workspace, size_t ws_bytes,
                         void* stream);
 
 /* Rebuild x from codes, scales and tensor_scale (as produced by
- * fp4_quantize with the same rows, cols and params) into out, in x's
+ * fp4_quantize with the same rows, cols and params, including ts_mode for
+ * the outer-scale layout) into out, in x's
  * layout (rows x cols, leading dimension ld_out), FP32 or BF16 (RNE).
  * inverse_rht = 1 undoes the RHT (requires p->rht).  Each value is
  * sign * L[k] * d, one binary32 product per element. */

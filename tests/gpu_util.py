@@ -44,22 +44,31 @@ def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str):
 
 
 def quantize_both(x: np.ndarray, fmt, axis="row", rounding="rtne", rht=False, rht_seed=0,
-                  sr_seed=0, given=None, poison=0xAA):
+                  sr_seed=0, given=None, poison=0xAA, outer=False):
     """Quantize on the GPU (through the C ABI) and in the oracle; compare
-    codes, scales and the tensor scale byte for byte.  Returns the GPU tensors."""
+    codes, scales and the tensor (or outer) scales byte for byte.  Returns
+    the GPU tensors."""
     xd = to_device(x)
     rows, cols = x.shape
     cshape, sshape = fp4.output_shapes(rows, cols, fmt, axis)
     codes = torch.full(cshape, poison, dtype=torch.uint8, device=DEV)
     scales = torch.full(sshape, poison, dtype=torch.uint8, device=DEV)
+    ts_out = None
+    if outer:
+        ts_out = torch.full(fp4.outer_shape(rows, cols, axis), float("nan"),
+                            dtype=torch.float32, device=DEV)
     c, s, ts = fp4.quantize(xd, fmt, axis, rounding, rht, rht_seed, sr_seed,
-                            tensor_scale=given, codes=codes, scales=scales)
+                            tensor_scale=given, codes=codes, scales=scales, ts_out=ts_out,
+                            outer=outer)
     torch.cuda.synchronize()
     oc, osc, ots = oracle.quantize(x, fmt, axis, rounding, rht, rht_seed, sr_seed,
-                                   tensor_scale=given)
-    tag = "%s %s %s rht=%s %s %s" % (fmt, axis, rounding, rht, x.dtype, x.shape)
+                                   tensor_scale=given, outer=outer)
+    tag = "%s %s %s rht=%s %s %s%s" % (fmt, axis, rounding, rht, x.dtype, x.shape,
+                                       " outer" if outer else "")
     assert_bytes_equal(to_host(s), osc, "scales " + tag)
     assert_bytes_equal(to_host(c), oc, "codes " + tag)
-    if fmt != "mxfp4":
+    if outer:
+        assert_bytes_equal(to_host(ts).view(np.uint32), ots.view(np.uint32), "outer scales " + tag)
+    elif fmt not in fp4.MX:
         assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots), "tensor scale " + tag
     return c, s, ts, (oc, osc, ots)

@@ -50,6 +50,8 @@ def test_workspace_bytes(lib):
     assert fp4.workspace_bytes(64, 64, fp4.make_params("ufp4")) > 0
     assert fp4.workspace_bytes(64, 64, fp4.make_params("mxfp4")) == 0
     assert fp4.workspace_bytes(64, 64, fp4.make_params("nvfp4", ts_given=True)) == 0
+    assert fp4.workspace_bytes(64, 128, fp4.make_params("nvfp4", outer=True)) == 0
+    assert fp4.workspace_bytes(64, 64, fp4.make_params("mxfp4_oas")) == 0
 
 
 # Fake device pointers: validation must reject these calls before touching them.
@@ -78,6 +80,13 @@ def test_quantize_validation(lib):
     assert _q(lib, bad) == -2
     bad = P("nvfp4"); bad.ts_mode = 5
     assert _q(lib, bad) == -2
+    bad = P("mxfp4_oas"); bad.block = 16
+    assert _q(lib, bad) == -2
+    bad = P("nvfp4"); bad.format = 4
+    assert _q(lib, bad) == -2
+    assert _q(lib, P("nvfp4", outer=True), cols=144, ld=144) == -3   # W % 128
+    assert _q(lib, P("ufp4", outer=True, axis="col"), rows=96) == -3
+    assert _q(lib, P("nvfp4", outer=True), cols=128, ld=128, ts=0) == -1
     assert _q(lib, P("nvfp4"), dt=9) == -5
     assert _q(lib, P("nvfp4"), cols=24, ld=24) == -3            # W % 16
     assert _q(lib, P("mxfp4"), cols=48, ld=48) == -3            # W % 32

@@ -24,8 +24,16 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352), (48, 80)]
 KINDS = workloads.SMALL_KINDS
 
-COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4"], ["row", "col"], ["rtne", "sr"],
-                                [False, True], ["bf16", "f32"]))
+COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas"], ["row", "col"],
+                                ["rtne", "sr"], [False, True], ["bf16", "f32"]))
+
+# Double-block (outer scale per 128) shapes: W % 128 == 0 on the axis used.
+# (128, 256) col: no whole column tile (run kernel only); (640, 200) col:
+# tiles plus a right strip of 8 columns and a bottom strip of 128 rows;
+# (384, 1152) row: nine outer pieces per row; (256, 384): whole tiles.
+OUTER_SHAPES = [(128, 256), (640, 200), (384, 1152), (256, 384)]
+OUTER_COMBOS = list(itertools.product(["nvfp4", "ufp4"], ["row", "col"], ["rtne", "sr"],
+                                      [False, True], ["bf16", "f32"]))
 
 
 def _input(kind, shape, seed, dtype):
@@ -55,6 +63,34 @@ def test_quantize_dequantize_parity(fmt, axis, rounding, rht, dtype):
                 if odt == torch.float32:
                     got, want = got.view(np.uint32), want.view(np.uint32)
                 assert_bytes_equal(got, want, "dequant inv=%s %s %s" % (inv, odt, shape))
+
+
+@pytest.mark.parametrize("fmt,axis,rounding,rht,dtype", OUTER_COMBOS,
+                         ids=["-".join(map(str, c)) for c in OUTER_COMBOS])
+def test_outer_scale_parity(fmt, axis, rounding, rht, dtype):
+    for i, shape in enumerate(OUTER_SHAPES):
+        W = shape[1] if axis == "row" else shape[0]
+        if W % 128:
+            continue
+        kind = KINDS[(i + 2 * len(fmt) + (1 if rht else 0) + (2 if axis == "col" else 0))
+                     % len(KINDS)]
+        x = _input(kind, shape, 200 + i, dtype)
+        note("outer %s %s %s rht=%s %s %s %s" % (fmt, axis, rounding, rht, dtype, shape, kind))
+        c, s, ts, (oc, osc, ots) = quantize_both(x, fmt, axis, rounding, rht, 4, 9 + i,
+                                                 outer=True)
+        rows, cols = shape
+        for inv in ([False, True] if rht else [False]):
+            out = fp4.dequantize(c, s, ts, rows, cols, fmt, axis, rht, 4, inv, torch.float32)
+            torch.cuda.synchronize()
+            want = oracle.dequantize(oc, osc, ots, rows, cols, fmt, axis, rht, 4, inv, "f32")
+            assert_bytes_equal(to_host(out).view(np.uint32), want.view(np.uint32),
+                               "outer dequant inv=%s %s" % (inv, shape))
+
+
+def test_outer_scale_rejects_ragged_width():
+    x = to_device(np.zeros((64, 144), dtype=np.float32))
+    with pytest.raises(fp4.FP4Error):
+        fp4.quantize(x, "nvfp4", "row", outer=True)
 
 
 @pytest.mark.parametrize("kind", KINDS)

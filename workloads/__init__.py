@@ -86,6 +86,7 @@ class Call:
     rht: bool = False
     rht_seed: int = 0
     sr_seed: int = 0
+    outer: bool = False   # NVFP4 / uniform: outer scale per 128 elements
 
 
 @dataclass
@@ -156,12 +157,45 @@ def _w_linear_layer() -> Workload:
     return w
 
 
+def _w_activation_outer() -> Workload:
+    w = _w_activation()
+    w.name = "rht_nvfp4_double_block_act_4096x4096"
+    w.description = ("the 4096x4096 activation above, NVFP4 + RHT with double-block scales "
+                     "(FP32 outer scale per 128 elements, no tensor amax pass), RTNE and SR")
+    for c in w.calls:
+        c.outer = True
+    return w
+
+
+def _w_linear_layer_outer() -> Workload:
+    w = _w_linear_layer()
+    w.name = "nvfp4_rht_double_block_linear_h4096_f14336_t16384"
+    w.description = ("the linear-layer operands above with double-block NVFP4 scales (FP32 outer "
+                     "scale per 128 elements of each A-row, no tensor amax pass)")
+    for c in w.calls:
+        c.outer = True
+    return w
+
+
+def _w_mx_weight_oas() -> Workload:
+    w = _w_mx_weight()
+    w.name = "mxfp4_oas_weight_8192x8192"
+    w.description = ("8192x8192 BF16 N(0, 0.02^2): MXFP4 with overflow-aware scales, RTNE, row "
+                     "and column axis, RHT off and on")
+    for c in w.calls:
+        c.fmt = "mxfp4_oas"
+    return w
+
+
 WORKLOADS = {
     "single_fp32": _w_single_fp32,
     "activation": _w_activation,
     "mx_weight": _w_mx_weight,
     "up_proj": _w_up_proj,
     "linear_layer": _w_linear_layer,
+    "activation_outer": _w_activation_outer,
+    "linear_layer_outer": _w_linear_layer_outer,
+    "mx_weight_oas": _w_mx_weight_oas,
 }
 
 
