@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp4dev {
 
 enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3 };
@@ -214,6 +216,23 @@ __device__ __forceinline__ float grid_max() { return FMT == kUFP4 ? 7.0f : 6.0f;
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Max over aligned groups of N consecutive lanes (N = 1, 2, 4 or 8); every
+// lane of a group gets the group's max.  DPP moves inside quads (lane xor 1,
+// lane xor 2) and half rows (mirror of 8 lanes), no LDS round trip.  All
+// lanes of a group must be active.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+  auto move = [](float x, auto ctrl) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (N >= 2) v = fmaxf(v, move(v, std::integral_constant<int, 0xB1>{}));  // [1,0,3,2]
+  if constexpr (N >= 4) v = fmaxf(v, move(v, std::integral_constant<int, 0x4E>{}));  // [2,3,0,1]
+  if constexpr (N >= 8) v = fmaxf(v, move(v, std::integral_constant<int, 0x141>{})); // half mirror
   return v;
 }
 

@@ -337,8 +337,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
         block_values(bi, t[bi], am[bi]);
         ao = fmaxf(ao, am[bi]);
       }
-#pragma unroll
-      for (int o = 1; o < LPO; o <<= 1) ao = fmaxf(ao, __shfl_xor(ao, o));
+      ao = group_max<LPO>(ao);
       ScaleCtx co;
       co.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
       co.den = co.s_t * grid_max<FMT>();
@@ -637,9 +636,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
       if constexpr (TSM == kTsOuter) {
         // kOuter / B consecutive lanes hold the blocks of one 128-piece
         constexpr int LPO = kOuter / B;
-        float ao = amax_t;
-#pragma unroll
-        for (int o = 1; o < LPO; o <<= 1) ao = fmaxf(ao, __shfl_xor(ao, o));
+        const float ao = group_max<LPO>(amax_t);
         cc.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
         cc.den = cc.s_t * grid_max<FMT>();
         if (j % LPO == 0) a.ts_out[ra * (a.W / kOuter) + rb / LPO] = cc.s_t;
