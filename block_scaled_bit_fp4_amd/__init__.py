@@ -42,7 +42,7 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_NULL", -2: "FP4_ERR_FORMAT", -3: "FP4_ERR_SH
 
 # every symbol include/fp4.h declares
 EXPORTS = ("fp4_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_rht",
-           "fp4_rht_signs", "fp4_status_str")
+           "fp4_rht_signs", "fp4_status_str", "fp4_workspace_bytes_dual", "fp4_quantize_dual")
 
 
 class FP4Error(RuntimeError):
@@ -81,6 +81,11 @@ def load():
         L.fp4_workspace_bytes.restype = sz
         L.fp4_quantize.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, sz, vp]
         L.fp4_quantize.restype = i32
+        L.fp4_workspace_bytes_dual.argtypes = [i64, i64, P]
+        L.fp4_workspace_bytes_dual.restype = sz
+        L.fp4_quantize_dual.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, vp, vp, vp,
+                                        sz, vp]
+        L.fp4_quantize_dual.restype = i32
         L.fp4_dequantize.argtypes = [vp, vp, vp, i64, i64, P, i32, vp, i32, i64, vp]
         L.fp4_dequantize.restype = i32
         L.fp4_rht.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_uint64, i32, vp, vp]
@@ -123,6 +128,10 @@ def rht_signs(seed: int) -> int:
 
 def workspace_bytes(rows: int, cols: int, params: Params) -> int:
     return int(load().fp4_workspace_bytes(rows, cols, ctypes.byref(params)))
+
+
+def workspace_bytes_dual(rows: int, cols: int, params: Params) -> int:
+    return int(load().fp4_workspace_bytes_dual(rows, cols, ctypes.byref(params)))
 
 
 def new_workspace(rows: int, cols: int, params: Params, device) -> Optional[torch.Tensor]:
@@ -188,6 +197,54 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize")
     return codes, scales, ts
+
+
+def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", rht: bool = False,
+                  rht_seed: int = 0, sr_seed: int = 0, tensor_scale=None, outer: bool = False,
+                  out_row=None, out_col=None, workspace: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Row-axis and column-axis quantization of x in one call.  Returns
+    ((codes, scales, ts) of the row axis, (codes, scales, ts) of the column
+    axis), each as ``quantize`` would.  ``tensor_scale``: None (computed), or
+    a pair (row, column) of given scales.  ``out_row`` / ``out_col``:
+    optional preallocated (codes, scales, ts) triples."""
+    _check_2d(x, "x")
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    outer = bool(outer) and fmt not in MX
+    given = tensor_scale is not None and not outer
+    p = make_params(fmt, "row", rounding, rht, rht_seed, sr_seed, given, outer)
+    dev = x.device
+    outs = []
+    for axis, pre in (("row", out_row), ("col", out_col)):
+        if pre is not None:
+            outs.append(tuple(pre))
+            continue
+        cshape, sshape = output_shapes(rows, cols, fmt, axis)
+        ts = None
+        if outer:
+            ts = torch.empty(outer_shape(rows, cols, axis), dtype=torch.float32, device=dev)
+        elif fmt not in MX:
+            if given:
+                v = tensor_scale[0 if axis == "row" else 1]
+                ts = v if torch.is_tensor(v) else torch.tensor([float(v)], dtype=torch.float32,
+                                                                device=dev)
+            else:
+                ts = torch.empty(1, dtype=torch.float32, device=dev)
+        outs.append((torch.empty(cshape, dtype=torch.uint8, device=dev),
+                     torch.empty(sshape, dtype=torch.uint8, device=dev), ts))
+    nws = workspace_bytes_dual(rows, cols, p)
+    if nws and workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    (cr, sr_, tr), (cc, sc, tc) = outs
+    st = load().fp4_quantize_dual(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
+                                  ctypes.byref(p), cr.data_ptr(), sr_.data_ptr(), _ptr(tr),
+                                  cc.data_ptr(), sc.data_ptr(), _ptr(tc), _ptr(workspace),
+                                  nws if workspace is not None else 0, _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_quantize_dual")
+    return outs[0], outs[1]
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: int, cols: int,

@@ -147,6 +147,75 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   return finish(fp4_launch_quantize(q, s), s);
 }
 
+size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p) {
+  (void)rows;
+  (void)cols;
+  if (check_params(p) != FP4_OK) return 0;
+  return needs_workspace(p) ? 2 * sizeof(float) * (size_t)kAmaxPartials : 0;
+}
+
+fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                             int64_t ld, const fp4_params* p, uint8_t* codes_row,
+                             uint8_t* scales_row, float* ts_row, uint8_t* codes_col,
+                             uint8_t* scales_col, float* ts_col, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  fp4_status st = check_params(p);
+  if (st != FP4_OK) return st;
+  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  fp4_params pr = *p, pc = *p;
+  pr.axis = FP4_AXIS_ROW;
+  pc.axis = FP4_AXIS_COL;
+  if ((st = check_shape(&pr, rows, cols, ld)) != FP4_OK) return st;
+  if ((st = check_shape(&pc, rows, cols, ld)) != FP4_OK) return st;
+  const bool empty = rows == 0 || cols == 0;
+  if (two_level(p) && (!ts_row || !ts_col)) return FP4_ERR_NULL;
+  if (!empty) {
+    if (!x || !codes_row || !scales_row || !codes_col || !scales_col) return FP4_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes_row) || !aligned16(scales_row) ||
+        !aligned16(codes_col) || !aligned16(scales_col))
+      return FP4_ERR_ALIGN;
+    if ((ld * (int64_t)elem_size(in_dtype)) % 16) return FP4_ERR_ALIGN;
+  }
+  if (needs_workspace(p)) {
+    if (!workspace) return FP4_ERR_WORKSPACE;
+    if (ws_bytes < 2 * sizeof(float) * (size_t)kAmaxPartials) return FP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+  }
+  const bool fused = !empty && in_dtype == FP4_BF16 && !is_mx(p->format) && rows % 128 == 0 &&
+                     cols % 128 == 0;
+  if (!fused) {
+    // the two single-axis calls, one after the other on the stream
+    st = fp4_quantize(x, in_dtype, rows, cols, ld, &pr, codes_row, scales_row, ts_row,
+                      workspace, ws_bytes, stream);
+    if (st != FP4_OK) return st;
+    return fp4_quantize(x, in_dtype, rows, cols, ld, &pc, codes_col, scales_col, ts_col,
+                        workspace, ws_bytes, stream);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DualLaunch q{};
+  q.x = x;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld = ld;
+  q.format = p->format;
+  q.sr = p->rounding == FP4_SR;
+  q.rht = p->rht;
+  q.ts_mode = p->ts_mode;
+  q.signs = p->rht ? fp4_rht_signs(p->rht_seed) : 0u;
+  q.sr_k0 = (uint32_t)p->sr_seed;
+  q.sr_k1 = (uint32_t)(p->sr_seed >> 32);
+  q.codes_row = codes_row;
+  q.scales_row = scales_row;
+  q.ts_row = ts_row;
+  q.codes_col = codes_col;
+  q.scales_col = scales_col;
+  q.ts_col = ts_col;
+  q.workspace = static_cast<float*>(workspace);
+  const hipError_t e = p->format == FP4_NVFP4 ? fp4_launch_quantize_dual_nvfp4(q, s)
+                                              : fp4_launch_quantize_dual_ufp4(q, s);
+  return finish(e, s);
+}
+
 fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                           const float* tensor_scale, int64_t rows, int64_t cols,
                           const fp4_params* p, int32_t inverse_rht, void* out,

@@ -236,6 +236,25 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Max over the 8 lanes of one parity inside each aligned group of 16 lanes
+// (a DPP row): lane xor 2 inside quads, then rotations of the row by 4 and
+// by 8, which keep the parity.  All 16 lanes must be active.
+__device__ __forceinline__ float parity_max16(float v) {
+  auto move = [](float x, auto ctrl) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  v = fmaxf(v, move(v, std::integral_constant<int, 0x4E>{}));   // quad [2,3,0,1]
+  v = fmaxf(v, move(v, std::integral_constant<int, 0x124>{}));  // row_ror:4
+  v = fmaxf(v, move(v, std::integral_constant<int, 0x128>{}));  // row_ror:8
+  return v;
+}
+
+// Swap a 32-bit word with the neighbouring lane (lane xor 1).
+__device__ __forceinline__ uint32_t swap_lane_pair(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
 // Block-wide max over a 256-thread workgroup; every thread gets the result.
 __device__ __forceinline__ float block_max_256(float v) {
   __shared__ float red[4];

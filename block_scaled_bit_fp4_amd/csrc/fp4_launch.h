@@ -24,6 +24,23 @@ struct QuantLaunch {
   float* workspace;
 };
 
+// Row-axis and column-axis quantization of one BF16 x in one pass
+// (16-element-block formats; rows and cols multiples of 128).
+struct DualLaunch {
+  const void* x;
+  int64_t rows, cols, ld;
+  int format, sr, rht, ts_mode;
+  uint32_t signs;
+  uint32_t sr_k0, sr_k1;
+  uint8_t* codes_row;
+  uint8_t* scales_row;
+  float* ts_row;
+  uint8_t* codes_col;
+  uint8_t* scales_col;
+  float* ts_col;
+  float* workspace;  // 2 * kAmaxPartials floats (computed tensor scales)
+};
+
 struct DequantLaunch {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -52,6 +69,8 @@ hipError_t fp4_launch_quantize_nvfp4(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_mxfp4(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_ufp4(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_mxfp4_oas(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_dual_nvfp4(const DualLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_dual_ufp4(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s);
 hipError_t fp4_launch_write_scalar(float* p, float v, hipStream_t s);

@@ -655,6 +655,221 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   }
 }
 
+// ------------------------------------------- dual output (row and column)
+// One read of a BF16 x emits both the row-axis and the column-axis
+// quantization (the forward and the weight-gradient operands), for the
+// 16-element-block formats.  Tiles are kDT x kDT: the column part goes
+// through LDS as in the column tiles; the row part is coded straight from
+// the load registers, where lanes 2m and 2m + 1 of a 16-lane row group hold
+// columns 16m..16m+15 of two adjacent rows and one lane-pair swap gives each
+// a whole 16-column block.  A 128-piece is a whole tile row (row part) or a
+// whole tile column (column part), so outer scales stay inside a tile.  The
+// tensor-amax pass is the same kernel with AMAX = true: it writes one
+// row-axis and one column-axis partial maximum per workgroup.
+constexpr int kDT = 128;          // tile rows and columns
+constexpr int kDP = kDT / 2 + 4;  // LDS words per A-row of the column part
+
+// LDS word of (x column col, row pair pr): XOR-swizzled in 4-word units
+// as in ColTile (conflict-free stores per half wave, conflict-free 128-bit
+// reads by the 8 lanes of one column).
+__device__ __forceinline__ int dual_at(int col, int pr) {
+  return col * kDP + (pr ^ (((col >> 3) & 7) << 2) ^ (((pr >> 5) & 1) << 2));
+}
+
+struct DualArgs {
+  int64_t ld, rows, cols, n_ct, ntile;
+  uint8_t* codes_r;
+  uint8_t* scales_r;
+  uint8_t* codes_c;
+  uint8_t* scales_c;
+  const float* ts_in_r;  // given tensor scales (kTsGiven)
+  const float* ts_in_c;
+  float* ts_out_r;       // computed tensor scales, or outer scales (kTsOuter)
+  float* ts_out_c;
+  float* partials;       // [row-axis maxima | column-axis maxima], npartials each
+  int npartials;
+  uint32_t signs, sr_k0, sr_k1;
+};
+
+// Both axes' tensor scales and reciprocal tables (nothing for outer scales).
+template <int FMT, int TSM>
+__device__ __forceinline__ void dual_prologue(const DualArgs& a, float* inv_r, float* inv_c,
+                                              ScaleCtx& cr, ScaleCtx& cc) {
+  cr = ScaleCtx{0.0f, 0.0f};
+  cc = ScaleCtx{0.0f, 0.0f};
+  if constexpr (TSM != kTsOuter) {
+    if (TSM == kTsGiven) {
+      cr.s_t = a.ts_in_r[0];
+      cc.s_t = a.ts_in_c[0];
+    } else {
+      float mr = 0.0f, mc = 0.0f;
+      for (int i = threadIdx.x; i < a.npartials; i += kThreads) {
+        mr = fmaxf(mr, a.partials[i]);
+        mc = fmaxf(mc, a.partials[a.npartials + i]);
+      }
+      mr = block_max_256(mr);
+      mc = block_max_256(mc);
+      cr.s_t = mr / (grid_max<FMT>() * 448.0f);
+      cc.s_t = mc / (grid_max<FMT>() * 448.0f);
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.ts_out_r[0] = cr.s_t;
+        a.ts_out_c[0] = cc.s_t;
+      }
+    }
+    cr.den = cr.s_t * grid_max<FMT>();
+    cc.den = cc.s_t * grid_max<FMT>();
+    if (threadIdx.x < 128) {
+      const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
+      const float dr = S ? cr.s_t * e4m3_decode(S) : 0.0f;
+      const float dc = S ? cc.s_t * e4m3_decode(S) : 0.0f;
+      inv_r[threadIdx.x] = dr != 0.0f ? 1.0f / dr : 0.0f;
+      inv_c[threadIdx.x] = dc != 0.0f ? 1.0f / dc : 0.0f;
+    }
+    __syncthreads();
+  }
+}
+
+template <int FMT, bool SR, bool RHT, int TSM, bool AMAX>
+__global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* __restrict__ x,
+                                                                DualArgs a) {
+  static_assert(!is_mx(FMT), "16-element blocks");
+  constexpr int kLoads = kDT * kDT * 2 / 16 / kThreads;  // 8 loads of 16 bytes per lane
+  __shared__ float inv_r[128], inv_c[128];
+  __shared__ __align__(16) uint32_t lds[kDT * kDP];
+  const int seg = threadIdx.x & 15;  // 16-byte column segment (8 columns)
+  const int q = threadIdx.x >> 4;    // row pair within a pass
+  // load i: rows 2p and 2p + 1 (p = q + 16 * (i % 4)) are loads i and i + 4
+  auto load_tile = [&](int64_t tile, uint4 (&buf)[kLoads]) {
+    const int64_t tr = tile / a.n_ct, tc = tile - tr * a.n_ct;
+    const uint16_t* base = x + tr * kDT * a.ld + tc * kDT + seg * 8;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int row = 2 * (q + 16 * (i & 3)) + (i >> 2);
+      buf[i] = *reinterpret_cast<const uint4*>(base + row * a.ld);
+    }
+  };
+
+  int64_t tile = blockIdx.x;
+  bool have = tile < a.ntile;
+  uint4 buf[kLoads];
+  if (have) load_tile(tile, buf);  // in flight during the prologue
+  ScaleCtx cr, cc;
+  if constexpr (!AMAX) dual_prologue<FMT, TSM>(a, inv_r, inv_c, cr, cc);
+  float mr = 0.0f, mc = 0.0f;  // AMAX: running maxima of the two axes
+  while (have) {
+    const int64_t tr = tile / a.n_ct, tc = tile - tr * a.n_ct;
+    const int64_t r0 = tr * kDT, c0 = tc * kDT;
+    __syncthreads();  // previous tile's LDS reads are done
+    // ---- registers -> LDS, transposed, for the column part
+#pragma unroll
+    for (int i = 0; i < kLoads / 2; ++i) {
+      const int pr = q + 16 * i;
+      const uint4 e = buf[i], o = buf[i + kLoads / 2];
+      const uint32_t ev[4] = {e.x, e.y, e.z, e.w}, od[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int col = seg * 8 + 2 * k;
+        lds[dual_at(col, pr)] = (ev[k] & 0xFFFFu) | (od[k] << 16);
+        lds[dual_at(col + 1, pr)] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
+      }
+    }
+    // ---- row part, from the registers
+    const bool odd = seg & 1;
+#pragma unroll
+    for (int i = 0; i < kLoads / 2; ++i) {
+      const uint4 send = odd ? buf[i] : buf[i + kLoads / 2];
+      uint4 recv;
+      recv.x = swap_lane_pair(send.x);
+      recv.y = swap_lane_pair(send.y);
+      recv.z = swap_lane_pair(send.z);
+      recv.w = swap_lane_pair(send.w);
+      const uint4 lo = odd ? recv : buf[i];
+      const uint4 hi = odd ? buf[i + kLoads / 2] : recv;
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float t[16];
+      widen_bf16_group<RHT>(w, a.signs, t);
+      if (RHT) fwht16(t);
+      float amax_t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax_t = fmaxf(amax_t, fabsf(t[j]));
+      if constexpr (AMAX) {
+        mr = fmaxf(mr, amax_t);
+      } else {
+        const int64_t row = r0 + 2 * (q + 16 * i) + (odd ? 1 : 0);
+        const int64_t b = c0 / 16 + (seg >> 1);  // block along the row
+        ScaleCtx c = cr;
+        if constexpr (TSM == kTsOuter) {
+          // the 8 lanes of this parity hold the row's 128-piece
+          const float ao = parity_max16(amax_t);
+          c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+          c.den = c.s_t * grid_max<FMT>();
+          if (seg < 2) a.ts_out_r[row * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
+        }
+        uint32_t pk[2];
+        uint32_t sbyte;
+        encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_r, a.sr_k0, a.sr_k1,
+                                                  (uint64_t)row * (uint64_t)a.cols +
+                                                      (uint64_t)(b * 16),
+                                                  pk, sbyte);
+        *reinterpret_cast<uint2*>(a.codes_r + row * (a.cols / 2) + b * 8) = make_uint2(pk[0], pk[1]);
+        a.scales_r[row * (a.cols / 16) + b] = (uint8_t)sbyte;
+      }
+    }
+    __syncthreads();
+    // ---- the next tile's loads fly while the column part is coded
+    const int64_t next = tile + gridDim.x;
+    const bool have_next = next < a.ntile;
+    if (have_next) load_tile(next, buf);
+    // ---- column part: unit u -> (x column cl, block j of 16 rows), j fastest
+#pragma unroll
+    for (int i = 0; i < kDT * (kDT / 16) / kThreads; ++i) {
+      const int u = threadIdx.x + i * kThreads;
+      const int cl = u >> 3, j = u & 7;
+      const uint4 lo = *reinterpret_cast<const uint4*>(lds + dual_at(cl, 8 * j));
+      const uint4 hi = *reinterpret_cast<const uint4*>(lds + dual_at(cl, 8 * j + 4));
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float t[16];
+      widen_bf16_group<RHT>(w, a.signs, t);
+      if (RHT) fwht16(t);
+      float amax_t = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) amax_t = fmaxf(amax_t, fabsf(t[e]));
+      if constexpr (AMAX) {
+        mc = fmaxf(mc, amax_t);
+      } else {
+        const int64_t ra = c0 + cl;     // A-row = column of x
+        const int64_t rb = r0 / 16 + j;  // block down the column
+        ScaleCtx c = cc;
+        if constexpr (TSM == kTsOuter) {
+          const float ao = group_max<8>(amax_t);
+          c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+          c.den = c.s_t * grid_max<FMT>();
+          if (j == 0) a.ts_out_c[ra * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
+        }
+        uint32_t pk[2];
+        uint32_t sbyte;
+        encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_c, a.sr_k0, a.sr_k1,
+                                                  (uint64_t)ra * (uint64_t)a.rows +
+                                                      (uint64_t)(rb * 16),
+                                                  pk, sbyte);
+        *reinterpret_cast<uint2*>(a.codes_c + ra * (a.rows / 2) + rb * 8) =
+            make_uint2(pk[0], pk[1]);
+        a.scales_c[ra * (a.rows / 16) + rb] = (uint8_t)sbyte;
+      }
+    }
+    tile = next;
+    have = have_next;
+  }
+  if constexpr (AMAX) {
+    mr = block_max_256(mr);
+    mc = block_max_256(mc);
+    if (threadIdx.x == 0) {
+      a.partials[blockIdx.x] = RHT ? mr * 0.25f : mr;
+      a.partials[a.npartials + blockIdx.x] = RHT ? mc * 0.25f : mc;
+    }
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 // Launch geometry (measured on MI355X; overridable at build time for sweeps).
 #ifndef FP4_ROW_GRID
@@ -857,6 +1072,54 @@ hipError_t pick_rht(const QuantLaunch& q, hipStream_t s) {
 template <int FMT>
 hipError_t quantize_format(const QuantLaunch& q, hipStream_t s) {
   return q.sr ? pick_rht<FMT, true>(q, s) : pick_rht<FMT, false>(q, s);
+}
+
+// Dual output: BF16, rows and cols multiples of kDT (checked by the caller).
+template <int FMT, bool SR, bool RHT, int TSM>
+hipError_t launch_dual_t(const DualLaunch& q, hipStream_t s) {
+  DualArgs a{};
+  a.ld = q.ld;
+  a.rows = q.rows;
+  a.cols = q.cols;
+  a.n_ct = q.cols / kDT;
+  a.ntile = (q.rows / kDT) * a.n_ct;
+  a.codes_r = q.codes_row;
+  a.scales_r = q.scales_row;
+  a.codes_c = q.codes_col;
+  a.scales_c = q.scales_col;
+  a.ts_in_r = q.ts_row;
+  a.ts_in_c = q.ts_col;
+  a.ts_out_r = q.ts_row;
+  a.ts_out_c = q.ts_col;
+  a.partials = q.workspace;
+  a.npartials = kAmaxPartials;
+  a.signs = q.signs;
+  a.sr_k0 = q.sr_k0;
+  a.sr_k1 = q.sr_k1;
+  const uint16_t* x = static_cast<const uint16_t*>(q.x);
+  if constexpr (TSM == kTsCompute)  // every partial slot is written
+    hipLaunchKernelGGL((dual_tile_kernel<FMT, false, RHT, kTsCompute, true>),
+                       dim3(kAmaxPartials), dim3(kThreads), 0, s, x, a);
+  const unsigned grid = (unsigned)(a.ntile < kColGrid ? a.ntile : kColGrid);
+  hipLaunchKernelGGL((dual_tile_kernel<FMT, SR, RHT, TSM, false>), dim3(grid), dim3(kThreads), 0,
+                     s, x, a);
+  return hipGetLastError();
+}
+template <int FMT, bool SR, bool RHT>
+hipError_t dual_pick_tsm(const DualLaunch& q, hipStream_t s) {
+  switch (q.ts_mode) {
+    case kTsGiven: return launch_dual_t<FMT, SR, RHT, kTsGiven>(q, s);
+    case kTsOuter: return launch_dual_t<FMT, SR, RHT, kTsOuter>(q, s);
+    default: return launch_dual_t<FMT, SR, RHT, kTsCompute>(q, s);
+  }
+}
+template <int FMT, bool SR>
+hipError_t dual_pick_rht(const DualLaunch& q, hipStream_t s) {
+  return q.rht ? dual_pick_tsm<FMT, SR, true>(q, s) : dual_pick_tsm<FMT, SR, false>(q, s);
+}
+template <int FMT>
+hipError_t quantize_dual_format(const DualLaunch& q, hipStream_t s) {
+  return q.sr ? dual_pick_rht<FMT, true>(q, s) : dual_pick_rht<FMT, false>(q, s);
 }
 
 }  // namespace

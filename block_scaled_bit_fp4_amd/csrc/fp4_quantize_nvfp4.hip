@@ -5,3 +5,7 @@
 hipError_t fp4_launch_quantize_nvfp4(const QuantLaunch& q, hipStream_t s) {
   return quantize_format<kNVFP4>(q, s);
 }
+
+hipError_t fp4_launch_quantize_dual_nvfp4(const DualLaunch& q, hipStream_t s) {
+  return quantize_dual_format<kNVFP4>(q, s);
+}

@@ -141,6 +141,30 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
                         float* tensor_scale, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* Bytes of device workspace fp4_quantize_dual needs (0 when none). */
+size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p);
+
+/* Both quantizations of x in one call: the row axis (codes_row, scales_row,
+ * ts_row, as fp4_quantize with p->axis = FP4_AXIS_ROW) and the column axis
+ * (codes_col, scales_col, ts_col, as with FP4_AXIS_COL); p->axis is
+ * ignored.  The outputs are byte for byte those of the two single calls.
+ * The forward and the weight-gradient GEMM both need an operand this way
+ * (TetraJet-v2 page, Riepilogo Tecnico 2.A: the 1x16 groups realigned for
+ * the transposed matrix; the [UFP4] page, Metodologia 2: quantized
+ * operands of all three GEMMs).  With BF16 input, the NVFP4 or uniform
+ * grid format and rows and cols multiples of 128, x is read once per pass
+ * (once in all with a given tensor scale or outer scales, twice with
+ * computed tensor scales instead of four times); otherwise the call runs
+ * the two single-axis quantizations in turn.  ts_row / ts_col follow the
+ * tensor_scale rules of fp4_quantize for their axis; workspace must hold
+ * fp4_workspace_bytes_dual() bytes.  Same alignment rules and errors as
+ * fp4_quantize, checked for both axes. */
+fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                             int64_t ld, const fp4_params* p, uint8_t* codes_row,
+                             uint8_t* scales_row, float* ts_row, uint8_t* codes_col,
+                             uint8_t* scales_col, float* ts_col, void* workspace,
+                             size_t ws_bytes, void* stream);
+
 /* Rebuild x from codes, scales and tensor_scale (as produced by
  * fp4_quantize with the same rows, cols and params, including ts_mode for
  * the outer-scale layout) into out, in x's

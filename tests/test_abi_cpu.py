@@ -135,3 +135,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fp4, "_lib", None)
     with pytest.raises(RuntimeError):
         fp4.load()
+
+
+def test_dual_validation(lib):
+    P = fp4.make_params
+    def dq(p, **k):
+        return lib.fp4_quantize_dual(k.get("x", A), k.get("dt", 0), k.get("rows", 128),
+                                     k.get("cols", 128), k.get("ld", 128),
+                                     ctypes.byref(p) if p is not None else None,
+                                     k.get("cr", A), k.get("sr", A), k.get("tr", A),
+                                     k.get("cc", A), k.get("sc", A), k.get("tc", A),
+                                     k.get("ws", A), k.get("nws", 8192), None)
+    assert fp4.workspace_bytes_dual(128, 128, P("nvfp4")) == 2 * fp4.workspace_bytes(128, 128, P("nvfp4"))
+    assert fp4.workspace_bytes_dual(128, 128, P("nvfp4", outer=True)) == 0
+    assert dq(None) == -1
+    assert dq(P("nvfp4"), dt=7) == -5
+    assert dq(P("nvfp4"), rows=120) == -3          # column axis: W = rows % 16
+    assert dq(P("nvfp4"), cols=120, ld=120) == -3  # row axis
+    assert dq(P("nvfp4", outer=True), rows=144) == -3
+    assert dq(P("nvfp4"), tr=0) == -1
+    assert dq(P("nvfp4"), tc=0) == -1
+    assert dq(P("nvfp4"), cc=MIS) == -4
+    assert dq(P("nvfp4"), sc=0) == -1
+    assert dq(P("nvfp4"), nws=4096) == -6           # needs two partial arrays
+    assert dq(P("nvfp4"), ws=0) == -6
