@@ -195,8 +195,13 @@ int fp4r_e8m0_exponent_oas(float amax) {
  * L[k] <= m < L[k+1]; m >= L[7] saturates at 7 ([MXFP4] 2.A: saturation at
  * the FP4 limit).  RTNE compares m with the exact midpoint, ties to the even
  * code ([UFP4] Metodologia 1: RTNE bins).  SR rounds up with probability
- * (m - L[k]) / (L[k+1] - L[k]) using a 16-bit draw ([TJ2] 2.A: stochastic
- * rounding so that E[round(x)] = x; [UFP4] Metodologia 2: SR on dY).
+ * p = (m - L[k]) / (L[k+1] - L[k]) using a 16-bit draw ([TJ2] 2.A:
+ * stochastic rounding so that E[round(x)] = x; [UFP4] Metodologia 2: SR on
+ * dY): up iff p * 2^22 >= 64 * u16 + 1, i.e. iff the draw, read as the
+ * fixed-point number (u16 + 2^-6) * 2^-16, does not exceed p.  Of the 2^16
+ * draws, min(2^16, floor((p * 2^22 - 1) / 64) + 1) round up (none when
+ * p * 2^22 < 1), which is within one of p * 2^16: E[round(m)] equals m to
+ * within 2^-16 of a bin width.
  * ---------------------------------------------------------------------- */
 static int bin_below(double m, const double* L) {
   int k = 0;
@@ -221,7 +226,8 @@ int fp4r_round_sr(float mf, int grid, uint32_t u16) {
   if (m >= L[7]) return 7;
   int k = bin_below(m, L);
   double p = (m - L[k]) / (L[k + 1] - L[k]);
-  return ((double)(u16 & 0xFFFFu) < p * 65536.0) ? k + 1 : k;
+  /* p * 2^22 and 64 * u16 + 1 are exact in binary64 */
+  return (p * 4194304.0 >= 64.0 * (double)(u16 & 0xFFFFu) + 1.0) ? k + 1 : k;
 }
 
 /* ------------------------------------------------------------------------

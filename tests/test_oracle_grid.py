@@ -92,9 +92,10 @@ def test_saturation_and_infinity():
 @pytest.mark.parametrize("grid,fixture", [("e2m1", "e2m1_levels.txt"),
                                           ("uniform", "uniform_levels.txt")])
 def test_sr_exhaustive_over_draws(grid, fixture):
-    """For each m, the number of 16-bit draws that round up is exactly
-    ceil(p * 2^16) with p = (m - L[k]) / (L[k+1] - L[k]) in exact rationals,
-    so E[q] is within one part in 2^16 of a bin width of m (unbiased up to the
+    """For each m, the draws that round up are exactly those with
+    64 * u16 + 1 <= p * 2^22, p = (m - L[k]) / (L[k+1] - L[k]) in exact
+    rationals: their number is min(2^16, floor((p * 2^22 - 1) / 64) + 1), so
+    E[q] is within one part in 2^16 of a bin width of m (unbiased up to the
     draw resolution: TetraJet-v2 page, 2.A)."""
     levels = _levels(fixture)
     rng = np.random.default_rng(3)
@@ -112,8 +113,13 @@ def test_sr_exhaustive_over_draws(grid, fixture):
         lo, hi = Fraction(levels[k]), Fraction(levels[k + 1])
         p = (m - lo) / (hi - lo)
         n_up = int(np.count_nonzero(k_all == k + 1))
-        want = -((-p * 65536).numerator // (-p * 65536).denominator) if p else 0
+        X = p * (1 << 22)
+        want = 0 if X < 1 else min(65536, int((X - 1) // 64) + 1)
         assert n_up == want, (float(mf), n_up, want)
+        up = np.nonzero(k_all == k + 1)[0]
+        assert (64 * up.astype(np.int64) + 1 <= X).all()   # exactly the small draws
+        if up.size:
+            assert up.max() == up.size - 1
         assert set(np.unique(k_all)) <= {k, k + 1}
         mean = lo + (hi - lo) * Fraction(n_up, 65536)
         assert abs(mean - m) <= (hi - lo) / 65536
