@@ -45,14 +45,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int, outer: bool = False) -> int:
+def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int, outer: bool = False,
+                      outputs: int = 1) -> int:
     """Bytes the method must move once: the input, the packed codes, one
     scale byte per block, and for the two-level formats the FP32 tensor
-    scale, or one FP32 outer scale per 128 elements (double block)."""
+    scale, or one FP32 outer scale per 128 elements (double block); a
+    dual-output call reads the input once and writes two sets."""
     n = rows * cols
     if fmt in MX:
-        return n * in_bytes + n // 2 + n // 32
-    return n * in_bytes + n // 2 + n // 16 + (4 * (n // 128) if outer else 4)
+        return n * in_bytes + outputs * (n // 2 + n // 32)
+    return n * in_bytes + outputs * (n // 2 + n // 16 + (4 * (n // 128) if outer else 4))
 
 
 def call_label(c) -> str:
@@ -127,8 +129,9 @@ def cpu_baseline(w, tensors, budget_s=12.0):
     while True:
         for call in w.calls:
             x = tensors[call.tensor]
-            oracle.quantize(x, call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
-                            call.sr_seed, outer=call.outer)
+            for axis in (("row", "col") if call.axis == "both" else (call.axis,)):
+                oracle.quantize(x, call.fmt, axis, call.rounding, call.rht, call.rht_seed,
+                                call.sr_seed, outer=call.outer)
             nbytes += x.size * x.itemsize
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -195,25 +198,37 @@ def main():
     for call in w.calls:
         x = dtensors[call.tensor]
         rows, cols = x.shape
-        cs, ss = fp4.output_shapes(rows, cols, call.fmt, call.axis)
-        p = fp4.make_params(call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
+        dual = call.axis == "both"
+        axes = ("row", "col") if dual else (call.axis,)
+        p = fp4.make_params(call.fmt, axes[0], call.rounding, call.rht, call.rht_seed,
                             call.sr_seed, outer=call.outer)
-        ts_shape = fp4.outer_shape(rows, cols, call.axis) if call.outer else (1,)
+        outs = []
+        for axis in axes:
+            cs, ss = fp4.output_shapes(rows, cols, call.fmt, axis)
+            ts_shape = fp4.outer_shape(rows, cols, axis) if call.outer else (1,)
+            outs.append((torch.empty(cs, dtype=torch.uint8, device=dev),
+                         torch.empty(ss, dtype=torch.uint8, device=dev),
+                         torch.empty(ts_shape, dtype=torch.float32, device=dev)))
+        nws = (fp4.workspace_bytes_dual if dual else fp4.workspace_bytes)(rows, cols, p)
         plans.append(dict(
-            call=call, x=x,
-            codes=torch.empty(cs, dtype=torch.uint8, device=dev),
-            scales=torch.empty(ss, dtype=torch.uint8, device=dev),
-            ts=torch.empty(ts_shape, dtype=torch.float32, device=dev),
-            ws=fp4.new_workspace(rows, cols, p, dev),
-            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size(), call.outer),
+            call=call, x=x, outs=outs,
+            ws=torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None,
+            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size(), call.outer,
+                                  len(axes)),
             in_bytes=x.numel() * x.element_size()))
     stream = torch.cuda.current_stream()
 
     def run(pl):
         c = pl["call"]
-        fp4.quantize(pl["x"], c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed,
-                     codes=pl["codes"], scales=pl["scales"], ts_out=pl["ts"],
-                     workspace=pl["ws"], stream=stream, outer=c.outer)
+        if c.axis == "both":
+            fp4.quantize_dual(pl["x"], c.fmt, c.rounding, c.rht, c.rht_seed, c.sr_seed,
+                              outer=c.outer, out_row=pl["outs"][0], out_col=pl["outs"][1],
+                              workspace=pl["ws"], stream=stream)
+        else:
+            codes, scales, ts = pl["outs"][0]
+            fp4.quantize(pl["x"], c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed,
+                         codes=codes, scales=scales, ts_out=ts, workspace=pl["ws"],
+                         stream=stream, outer=c.outer)
 
     def step():
         for pl in plans:

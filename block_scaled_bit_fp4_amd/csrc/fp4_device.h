@@ -190,8 +190,9 @@ __device__ __forceinline__ uint32_t round_rtne_sw(float m) {
 }
 
 // Stochastic rounding ([TJ2] 2.A; [UFP4] Metodologia 2): with L[k] <= m <
-// L[k+1], round up iff u16 < p * 2^16, p = (m - L[k]) / (L[k+1] - L[k]),
-// which is the (exact) fractional part of m / spacing.
+// L[k+1], round up iff p * 2^22 >= 64 * u16 + 1, p = (m - L[k]) /
+// (L[k+1] - L[k]), which is the (exact) fractional part of m / spacing;
+// both sides of the comparison are exact in binary32.
 template <int FMT>
 __device__ __forceinline__ uint32_t round_sr_sw(float m, uint32_t u16) {
   float q, off;
@@ -204,7 +205,7 @@ __device__ __forceinline__ uint32_t round_sr_sw(float m, uint32_t u16) {
     off = lo ? 0.0f : (mid ? 2.0f : 4.0f);
   }
   const float fl = __builtin_floorf(q);
-  const float up = (float)u16 < (q - fl) * 65536.0f ? 1.0f : 0.0f;
+  const float up = (q - fl) * 4194304.0f >= (float)(u16 * 64u + 1u) ? 1.0f : 0.0f;
   return (uint32_t)fminf(fl + off + up, 7.0f);
 }
 

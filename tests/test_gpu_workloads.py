@@ -14,6 +14,23 @@ from tests.gpu_util import assert_bytes_equal, note, quantize_both, to_device, t
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
+def _dual_full(x, call):
+    """A dual-output call against the oracle's two single-axis quantizations."""
+    (cr, sr_, tr), (cc, sc, tc) = fp4.quantize_dual(to_device(x), call.fmt, call.rounding,
+                                                    call.rht, call.rht_seed, call.sr_seed,
+                                                    outer=call.outer)
+    torch.cuda.synchronize()
+    for axis, (c, s, t) in (("row", (cr, sr_, tr)), ("col", (cc, sc, tc))):
+        oc, osc, ots = oracle.quantize(x, call.fmt, axis, call.rounding, call.rht, call.rht_seed,
+                                       call.sr_seed, outer=call.outer)
+        assert_bytes_equal(to_host(s), osc, "dual scales " + axis)
+        assert_bytes_equal(to_host(c), oc, "dual codes " + axis)
+        if call.outer:
+            assert_bytes_equal(to_host(t).view(np.uint32), ots.view(np.uint32), "dual outer")
+        elif call.fmt not in fp4.MX:
+            assert to_host(t).view(np.uint32)[0] == np.float32(ots).view(np.uint32)
+
+
 @pytest.mark.parametrize("key", list(workloads.WORKLOADS))
 def test_workload_full_size(key):
     w = workloads.workload(key)
@@ -24,6 +41,9 @@ def test_workload_full_size(key):
             cache[call.tensor] = w.make(call.tensor)
         x = cache[call.tensor]
         note("workload %s: %s" % (key, call))
+        if call.axis == "both":
+            _dual_full(x, call)
+            continue
         c, s, ts, (oc, osc, ots) = quantize_both(x, call.fmt, call.axis, call.rounding, call.rht,
                                                  call.rht_seed, call.sr_seed, outer=call.outer)
         if key == "single_fp32":

@@ -81,7 +81,7 @@ class Call:
     """One quantize call of a workload."""
     tensor: str
     fmt: str
-    axis: str = "row"
+    axis: str = "row"     # "row", "col", or "both" (one dual-output call)
     rounding: str = "rtne"
     rht: bool = False
     rht_seed: int = 0
@@ -187,6 +187,29 @@ def _w_mx_weight_oas() -> Workload:
     return w
 
 
+def _w_linear_layer_dual() -> Workload:
+    w = _w_linear_layer()
+    w.name = "nvfp4_rht_dual_linear_h4096_f14336_t16384"
+    w.description = ("the linear-layer operands above; X quantized along rows and columns by one "
+                     "dual-output call (same outputs as the separate X row and X column calls)")
+    w.calls = [Call("X", "nvfp4", "both", "rtne", True, 0, 0),
+               Call("W", "nvfp4", "row", "rtne", True, 0, 0),
+               Call("dY", "nvfp4", "col", "sr", True, 0, 1)]
+    return w
+
+
+def _w_training_operands() -> Workload:
+    w = _w_linear_layer()
+    w.name = "nvfp4_rht_all_gemm_operands_h4096_f14336_t16384"
+    w.description = ("every quantized operand of the three GEMMs of one linear layer (forward, "
+                     "input gradient, weight gradient): X, W and dY each along rows and columns "
+                     "by dual-output calls; NVFP4 + RHT, SR on dY")
+    w.calls = [Call("X", "nvfp4", "both", "rtne", True, 0, 0),
+               Call("W", "nvfp4", "both", "rtne", True, 0, 0),
+               Call("dY", "nvfp4", "both", "sr", True, 0, 1)]
+    return w
+
+
 WORKLOADS = {
     "single_fp32": _w_single_fp32,
     "activation": _w_activation,
@@ -196,6 +219,8 @@ WORKLOADS = {
     "activation_outer": _w_activation_outer,
     "linear_layer_outer": _w_linear_layer_outer,
     "mx_weight_oas": _w_mx_weight_oas,
+    "linear_layer_dual": _w_linear_layer_dual,
+    "training_operands": _w_training_operands,
 }
 
 
