@@ -58,8 +58,23 @@ def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int, outer: bool
 
 
 def call_label(c) -> str:
-    return "%s %s %s %s rht=%s%s" % (c.tensor, c.fmt, c.axis, c.rounding, c.rht,
-                                     " outer128" if c.outer else "")
+    if c.op == "rht":
+        return "%s rht %s" % (c.tensor, c.axis)
+    lab = "%s %s %s %s rht=%s%s" % (c.tensor, c.fmt, c.axis, c.rounding, c.rht,
+                                    " outer128" if c.outer else "")
+    return lab if c.op == "quantize" else "%s dequantize to %s%s" % (
+        lab, c.out_dtype, " (inverse RHT)" if c.rht else "")
+
+
+def op_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
+    """Algorithmic bytes of one call of any operation."""
+    n = rows * cols
+    if c.op == "rht":
+        return n * in_bytes + n * 4
+    if c.op == "dequantize":
+        q = algorithmic_bytes(rows, cols, c.fmt, 0, c.outer)  # codes, scales, tensor scale
+        return q + n * (2 if c.out_dtype == "bf16" else 4)
+    return algorithmic_bytes(rows, cols, c.fmt, in_bytes, c.outer, 2 if c.axis == "both" else 1)
 
 
 def traffic_for(workload: str, call_index: int):
@@ -129,9 +144,16 @@ def cpu_baseline(w, tensors, budget_s=12.0):
     while True:
         for call in w.calls:
             x = tensors[call.tensor]
-            for axis in (("row", "col") if call.axis == "both" else (call.axis,)):
-                oracle.quantize(x, call.fmt, axis, call.rounding, call.rht, call.rht_seed,
-                                call.sr_seed, outer=call.outer)
+            if call.op == "rht":
+                oracle.rht(x, call.axis, call.rht_seed)
+            else:
+                for axis in (("row", "col") if call.axis == "both" else (call.axis,)):
+                    q = oracle.quantize(x, call.fmt, axis, call.rounding, call.rht,
+                                        call.rht_seed, call.sr_seed, outer=call.outer)
+                    if call.op == "dequantize":
+                        oracle.dequantize(q[0], q[1], q[2], x.shape[0], x.shape[1], call.fmt,
+                                          axis, call.rht, call.rht_seed, call.rht,
+                                          "f32" if call.out_dtype == "f32" else "bf16")
             nbytes += x.size * x.itemsize
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -210,17 +232,32 @@ def main():
                          torch.empty(ss, dtype=torch.uint8, device=dev),
                          torch.empty(ts_shape, dtype=torch.float32, device=dev)))
         nws = (fp4.workspace_bytes_dual if dual else fp4.workspace_bytes)(rows, cols, p)
-        plans.append(dict(
-            call=call, x=x, outs=outs,
-            ws=torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None,
-            alg=algorithmic_bytes(rows, cols, call.fmt, x.element_size(), call.outer,
-                                  len(axes)),
-            in_bytes=x.numel() * x.element_size()))
+        pl = dict(call=call, x=x, outs=outs,
+                  ws=torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None,
+                  alg=op_bytes(call, rows, cols, x.element_size()),
+                  in_bytes=x.numel() * x.element_size())
+        if call.op == "dequantize":   # this call's codes, made once outside the timed region
+            codes, scales, ts = outs[0]
+            fp4.quantize(x, call.fmt, call.axis, call.rounding, call.rht, call.rht_seed,
+                         call.sr_seed, codes=codes, scales=scales, ts_out=ts, workspace=pl["ws"],
+                         outer=call.outer)
+            pl["y"] = torch.empty((rows, cols), device=dev, dtype=torch.bfloat16
+                                  if call.out_dtype == "bf16" else torch.float32)
+        elif call.op == "rht":
+            pl["y"] = torch.empty((rows, cols), device=dev, dtype=torch.float32)
+        plans.append(pl)
     stream = torch.cuda.current_stream()
 
     def run(pl):
         c = pl["call"]
-        if c.axis == "both":
+        if c.op == "rht":
+            fp4.rht(pl["x"], c.axis, c.rht_seed, out=pl["y"], stream=stream)
+        elif c.op == "dequantize":
+            codes, scales, ts = pl["outs"][0]
+            rows, cols = pl["x"].shape
+            fp4.dequantize(codes, scales, ts, rows, cols, c.fmt, c.axis, c.rht, c.rht_seed,
+                           c.rht, pl["y"].dtype, out=pl["y"], stream=stream)
+        elif c.axis == "both":
             fp4.quantize_dual(pl["x"], c.fmt, c.rounding, c.rht, c.rht_seed, c.sr_seed,
                               outer=c.outer, out_row=pl["outs"][0], out_col=pl["outs"][1],
                               workspace=pl["ws"], stream=stream)
@@ -271,9 +308,10 @@ def main():
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_for(args.workload, dom),
-        "kernel": "fp4_quantize call %d (%s): %s" % (
-            dom, call_label(c), "quantize kernel" if (c.fmt in MX or c.outer)
-            else "tensor-amax + quantize kernels"),
+        "kernel": "call %d (%s): %s" % (
+            dom, call_label(c), "fp4_rht" if c.op == "rht" else "fp4_dequantize"
+            if c.op == "dequantize" else "fp4_quantize, quantize kernel"
+            if (c.fmt in MX or c.outer) else "fp4_quantize, tensor-amax + quantize kernels"),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
 
     if args.copy_mib:

@@ -44,16 +44,15 @@ struct DequantArgs {
   uint32_t signs;
 };
 
-__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_elem(uint16_t* p, float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
-    *p = (uint16_t)((u >> 16) | 0x0040u);
-    return;
-  }
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  *p = (uint16_t)(u >> 16);
+// BF16 bits of v, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x0040u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
+
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = (uint16_t)bf16_rne(v); }
 
 template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ out, DequantArgs a) {
@@ -97,6 +96,14 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
         float4* o = reinterpret_cast<float4*>(out + ra * a.ld_out + j0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = make_float4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
+      } else if (AXIS == 0) {
+        // 16 BF16 values: two 16-byte stores (rows are 16-byte aligned)
+        uint32_t pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pk[i] = bf16_rne(t[2 * i]) | (bf16_rne(t[2 * i + 1]) << 16);
+        uint4* o = reinterpret_cast<uint4*>(out + ra * a.ld_out + j0);
+        o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        o[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {

@@ -44,15 +44,26 @@ def test_workload_full_size(key):
         if call.axis == "both":
             _dual_full(x, call)
             continue
+        if call.op == "rht":
+            y = fp4.rht(to_device(x), call.axis, call.rht_seed)
+            torch.cuda.synchronize()
+            want = oracle.rht(x, call.axis, call.rht_seed)
+            assert_bytes_equal(to_host(y).view(np.uint32), want.view(np.uint32), "rht")
+            continue
         c, s, ts, (oc, osc, ots) = quantize_both(x, call.fmt, call.axis, call.rounding, call.rht,
                                                  call.rht_seed, call.sr_seed, outer=call.outer)
-        if key == "single_fp32":
+        if key == "single_fp32" or call.op == "dequantize":
             rows, cols = x.shape
+            bf16 = call.op == "dequantize" and call.out_dtype == "bf16"
             out = fp4.dequantize(c, s, ts, rows, cols, call.fmt, call.axis, call.rht,
-                                 call.rht_seed, call.rht)
+                                 call.rht_seed, call.rht,
+                                 torch.bfloat16 if bf16 else torch.float32)
             torch.cuda.synchronize()
             want = oracle.dequantize(oc, osc, ots, rows, cols, call.fmt, call.axis, call.rht,
-                                     call.rht_seed, call.rht)
-            assert_bytes_equal(to_host(out).view(np.uint32), want.view(np.uint32), "dequant")
+                                     call.rht_seed, call.rht, "bf16" if bf16 else "f32")
+            got = to_host(out)
+            if not bf16:
+                got, want = got.view(np.uint32), want.view(np.uint32)
+            assert_bytes_equal(got, want, "dequant")
         del c, s, ts, oc, osc
     cache.clear()

@@ -87,6 +87,8 @@ class Call:
     rht_seed: int = 0
     sr_seed: int = 0
     outer: bool = False   # NVFP4 / uniform: outer scale per 128 elements
+    op: str = "quantize"  # "quantize", "dequantize" (of this call's own codes) or "rht"
+    out_dtype: str = "bf16"  # dequantize output
 
 
 @dataclass
@@ -210,6 +212,23 @@ def _w_training_operands() -> Workload:
     return w
 
 
+def _w_dequant() -> Workload:
+    w = _w_linear_layer()
+    w.name = "nvfp4_rht_dequant_and_rht_h4096_t16384"
+    w.description = ("the 16384x4096 linear-layer activation X: NVFP4 + RHT codes (quantized once, "
+                     "outside the timed region) dequantized with the inverse RHT to BF16 along "
+                     "rows and along columns, double-block codes dequantized to FP32, and the "
+                     "standalone forward RHT along rows (FP32 out); value counts the BF16 bytes "
+                     "of X per call")
+    w.tensors = {"X": w.tensors["X"]}
+    w.calls = [Call("X", "nvfp4", "row", "rtne", True, 0, 0, op="dequantize"),
+               Call("X", "nvfp4", "col", "rtne", True, 0, 0, op="dequantize"),
+               Call("X", "nvfp4", "row", "rtne", True, 0, 0, outer=True, op="dequantize",
+                    out_dtype="f32"),
+               Call("X", "nvfp4", "row", op="rht")]
+    return w
+
+
 WORKLOADS = {
     "single_fp32": _w_single_fp32,
     "activation": _w_activation,
@@ -221,6 +240,7 @@ WORKLOADS = {
     "mx_weight_oas": _w_mx_weight_oas,
     "linear_layer_dual": _w_linear_layer_dual,
     "training_operands": _w_training_operands,
+    "dequant": _w_dequant,
 }
 
 
