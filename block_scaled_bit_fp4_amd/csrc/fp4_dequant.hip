@@ -93,17 +93,19 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
       if (INV) rht16_inverse(t, a.signs);
       const int64_t j0 = b * B + h * 16;
       if (AXIS == 0 && sizeof(T) == 4) {
-        float4* o = reinterpret_cast<float4*>(out + ra * a.ld_out + j0);
+        T* o = out + ra * a.ld_out + j0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = make_float4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
+        for (int i = 0; i < 4; ++i)
+          store16<false>(o + 4 * i, __float_as_uint(t[4 * i]), __float_as_uint(t[4 * i + 1]),
+                  __float_as_uint(t[4 * i + 2]), __float_as_uint(t[4 * i + 3]));
       } else if (AXIS == 0) {
         // 16 BF16 values: two 16-byte stores (rows are 16-byte aligned)
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pk[i] = bf16_rne(t[2 * i]) | (bf16_rne(t[2 * i + 1]) << 16);
-        uint4* o = reinterpret_cast<uint4*>(out + ra * a.ld_out + j0);
-        o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        o[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        T* o = out + ra * a.ld_out + j0;
+        store16<false>(o, pk[0], pk[1], pk[2], pk[3]);
+        store16<false>(o + 8, pk[4], pk[5], pk[6], pk[7]);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -132,9 +134,11 @@ __global__ __launch_bounds__(kThreads) void rht_kernel(const T* __restrict__ x, 
     if (INV) rht16_inverse(t, signs);
     else rht16_forward(t, signs);
     if (AXIS == 0) {
-      float4* o = reinterpret_cast<float4*>(y + ra * cols + g * 16);
+      float* o = y + ra * cols + g * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = make_float4(t[4 * i], t[4 * i + 1], t[4 * i + 2], t[4 * i + 3]);
+      for (int i = 0; i < 4; ++i)
+        store16<false>(o + 4 * i, __float_as_uint(t[4 * i]), __float_as_uint(t[4 * i + 1]),
+                __float_as_uint(t[4 * i + 2]), __float_as_uint(t[4 * i + 3]));
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) y[(g * 16 + j) * cols + ra] = t[j];

@@ -369,10 +369,10 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
     if constexpr (U >= 32) {
 #pragma unroll
       for (int i = 0; i < U / 32; ++i)
-        reinterpret_cast<uint4*>(cp)[i] =
-            make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+        store16<true>(cp + 16 * i, packed[4 * i], packed[4 * i + 1], packed[4 * i + 2],
+                packed[4 * i + 3]);
     } else {
-      *reinterpret_cast<uint2*>(cp) = make_uint2(packed[0], packed[1]);
+      store8<true>(cp, packed[0], packed[1]);
     }
     uint8_t* sp = a.scales + w.major * (a.W / B) + w.minor * NBU;
     if constexpr (NBU == 4)
@@ -493,16 +493,16 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
       if (nb == NB && vec_codes) {
 #pragma unroll
         for (int q = 0; q < NB * WPB; q += 4)
-          *reinterpret_cast<uint4*>(cp + 4 * q) =
-              make_uint4(codes[k][q], codes[k][q + 1], codes[k][q + 2], codes[k][q + 3]);
+          store16<true>(cp + 4 * q, codes[k][q], codes[k][q + 1], codes[k][q + 2],
+                        codes[k][q + 3]);
       } else {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if (j < nb) {
 #pragma unroll
             for (int q = 0; q < WPB; q += 2)
-              *reinterpret_cast<uint2*>(cp + 4 * (j * WPB + q)) =
-                  make_uint2(codes[k][j * WPB + q], codes[k][j * WPB + q + 1]);
+              store8<true>(cp + 4 * (j * WPB + q), codes[k][j * WPB + q],
+                           codes[k][j * WPB + q + 1]);
           }
         }
       }
@@ -659,8 +659,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
       encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
                                                          a.sr_k1, n0, pk, sbyte);
       uint8_t* cp = a.codes + ra * (a.W / 2) + rb * (B / 2);
-      if constexpr (B == 16) *reinterpret_cast<uint2*>(cp) = make_uint2(pk[0], pk[1]);
-      else *reinterpret_cast<uint4*>(cp) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      if constexpr (B == 16) store8<true>(cp, pk[0], pk[1]);
+      else store16<true>(cp, pk[0], pk[1], pk[2], pk[3]);
       a.scales[ra * a.nblk_axis + rb] = (uint8_t)sbyte;
     }
     tile = next;
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
                                                   (uint64_t)row * (uint64_t)a.cols +
                                                       (uint64_t)(b * 16),
                                                   pk, sbyte);
-        *reinterpret_cast<uint2*>(a.codes_r + row * (a.cols / 2) + b * 8) = make_uint2(pk[0], pk[1]);
+        store8<true>(a.codes_r + row * (a.cols / 2) + b * 8, pk[0], pk[1]);
         a.scales_r[row * (a.cols / 16) + b] = (uint8_t)sbyte;
       }
     }
@@ -865,8 +865,7 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
                                                   (uint64_t)ra * (uint64_t)a.rows +
                                                       (uint64_t)(rb * 16),
                                                   pk, sbyte);
-        *reinterpret_cast<uint2*>(a.codes_c + ra * (a.rows / 2) + rb * 8) =
-            make_uint2(pk[0], pk[1]);
+        store8<true>(a.codes_c + ra * (a.rows / 2) + rb * 8, pk[0], pk[1]);
         a.scales_c[ra * (a.rows / 16) + rb] = (uint8_t)sbyte;
       }
     }

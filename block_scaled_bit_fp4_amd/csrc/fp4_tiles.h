@@ -14,6 +14,25 @@ namespace fp4dev {
 
 constexpr int kThreads = 256;
 
+// 16- and 8-byte stores of outputs the kernel does not read again.  NT:
+// with the nontemporal hint, measured faster for the code bytes of the
+// quantize kernels and much slower (about 2x) for the FP32 outputs of the
+// dequantize and RHT kernels, which therefore use plain stores.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ void store16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4_t v = {a, b, c, d};
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+  else *reinterpret_cast<u32x4_t*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ void store8(void* p, uint32_t a, uint32_t b) {
+  const u32x2_t v = {a, b};
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+  else *reinterpret_cast<u32x2_t*>(p) = v;
+}
+
 // ---------------------------------------------------------------- rows
 // Raw bytes of N consecutive elements of a row (16-byte aligned).
 template <typename T, int N>
