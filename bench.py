@@ -12,10 +12,14 @@ between device synchronizations, timed with HIP events on the stream the
 kernels run on.  Prints one JSON line.
 
 `value` is input GB/s over the whole step (bytes of BF16 input of every call
-/ step time).  `roofline` covers the dominant call: its algorithmic bytes
-(input + codes + scale bytes + 4-byte tensor scale) over its mean duration,
-against the 8 TB/s HBM peak.  `cpu_baseline` times the scalar oracle on the
-host on a bounded sample of the same workload.
+/ step time), warm: the same tensors are quantized every step, so inputs of
+up to 256 MB may be partly served from the MALL.  `config.cold_per_call_us`
+times each call after reading a 512 MiB buffer, which evicts L2 and MALL
+(`cold_input_gbs` is the step rate from those times).  `roofline` covers the
+dominant call: its algorithmic bytes (input + codes + scale bytes + 4-byte
+tensor scale) over its mean duration, against the 8 TB/s HBM peak.
+`cpu_baseline` times the scalar oracle on the host on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -172,6 +176,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="activation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache per-call timing (512 MiB eviction before each call)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one device-to-device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -301,6 +307,26 @@ def main():
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in evs) / reps
         per_call.append(ms)
+    # cold caches: before each call, reading a 512 MiB buffer evicts the
+    # inputs from L2 and the 256 MB MALL (a read leaves no dirty lines to
+    # write back during the call); only the call itself is timed
+    cold_per_call = []
+    if not args.no_cold:
+        scratch = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+        creps = max(10, args.steps // 10)
+        for pl in plans:
+            tot = 0.0
+            for r in range(creps):
+                torch.sum(scratch, dim=0, out=sink)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                run(pl)
+                b.record(stream)
+                b.synchronize()
+                tot += a.elapsed_time(b)
+            cold_per_call.append(tot / creps)
+        del scratch
     dom = max(range(len(plans)), key=lambda i: per_call[i])
     pl = plans[dom]
     achieved = pl["alg"] / (per_call[dom] * 1e-3) / 1e9
@@ -343,7 +369,10 @@ def main():
                    "calls": [call_label(c) for c in w.calls],
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
                    "per_call_us": [round(m * 1e3, 2) for m in per_call],
-                   "wall_ms_per_step": round(wall_ms, 4)},
+                   "wall_ms_per_step": round(wall_ms, 4),
+                   "cold_per_call_us": [round(m * 1e3, 2) for m in cold_per_call] or None,
+                   "cold_input_gbs": round(in_bytes / (sum(cold_per_call) * 1e-3) / 1e9, 2)
+                   if cold_per_call else None},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
