@@ -54,67 +54,146 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
 __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = (uint16_t)bf16_rne(v); }
 
+// Row-axis output staging.  A lane's unit is WORDS contiguous 32-bit words
+// of output, and consecutive lanes hold consecutive units; writing them
+// straight out would make every store instruction touch 64 separate
+// 16-byte pieces.  Instead each lane parks its words in LDS, and the
+// workgroup then stores 16-byte chunks so that consecutive lanes write
+// consecutive chunks (whole 64-byte segments and more per instruction).
+template <int WORDS>
+struct RowStage {
+  static constexpr int P = WORDS + 4;  // word pitch: 16-byte aligned, banks spread
+  static constexpr int kChunks = WORDS / 4;
+  uint32_t* buf;  // [kThreads][P]
+  uint32_t** dst;  // [kThreads] destination of each lane's unit (null: none)
+  __device__ __forceinline__ void put(const uint32_t (&v)[WORDS], uint32_t* to) const {
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q)
+      *reinterpret_cast<uint4*>(buf + threadIdx.x * P + 4 * q) =
+          make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    dst[threadIdx.x] = to;
+  }
+  // after a barrier: chunk k = i * kThreads + lane of the workgroup's units
+  __device__ __forceinline__ void flush() const {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int k = i * kThreads + threadIdx.x;
+      const int u = k / kChunks, part = k % kChunks;
+      uint32_t* to = dst[u];
+      if (to) {
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + u * P + 4 * part);
+        store16<false>(to + 4 * part, v.x, v.y, v.z, v.w);
+      }
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void pack_out(const float* t, uint32_t* w, int n);
+template <>
+__device__ __forceinline__ void pack_out<float>(const float* t, uint32_t* w, int n) {
+  for (int j = 0; j < n; ++j) w[j] = __float_as_uint(t[j]);
+}
+template <>
+__device__ __forceinline__ void pack_out<uint16_t>(const float* t, uint32_t* w, int n) {
+  for (int j = 0; j < n / 2; ++j) w[j] = bf16_rne(t[2 * j]) | (bf16_rne(t[2 * j + 1]) << 16);
+}
+
+// Values of block (ra, b): sign * L[k] * d, optionally through the inverse
+// RHT; t holds B values.
+template <int FMT, bool OUTER, bool INV>
+__device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t, int64_t ra,
+                                              int64_t b, float* t) {
+  constexpr int B = block_of<FMT>();
+  const uint32_t S = a.scales[ra * (a.W / B) + b];
+  float d;
+  if constexpr (is_mx(FMT)) {
+    d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
+  } else {
+    // outer scales: the 128-piece of the A-row that holds block b
+    const float so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : s_t;
+    d = S ? so * e4m3_decode(S) : 0.0f;
+  }
+  const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
+  uint32_t words[B / 8];
+  if constexpr (B == 16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(cp);
+    words[0] = v.x; words[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(cp);
+    words[0] = v.x; words[1] = v.y; words[2] = v.z; words[3] = v.w;
+  }
+#pragma unroll
+  for (int h = 0; h < B / 16; ++h) {
+    float g[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
+      const float mag = grid_level<FMT>(c & 7u) * d;
+      g[j] = (c & 8u) ? -mag : mag;
+    }
+    if (INV) rht16_inverse(g, a.signs);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t[16 * h + j] = g[j];
+  }
+}
+
 template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ out, DequantArgs a) {
   constexpr int B = block_of<FMT>();
   const float s_t = (is_mx(FMT) || OUTER) ? 0.0f : a.ts[0];
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
-  while (w.major < a.n_major) {
-    const int64_t ra = AXIS == 0 ? w.major : w.minor;
-    const int64_t b = AXIS == 0 ? w.minor : w.major;
-    const uint32_t S = a.scales[ra * (a.W / B) + b];
-    float d;
-    if constexpr (is_mx(FMT)) {
-      d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
-    } else {
-      // outer scales: the 128-piece of the A-row that holds block b
-      const float so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : s_t;
-      d = S ? so * e4m3_decode(S) : 0.0f;
+  if constexpr (AXIS == 0 && sizeof(T) == 2) {
+    // BF16 rows: 2 bytes per value, a lane's 16-value group is two 16-byte
+    // stores (staging measured slower here)
+    while (w.major < a.n_major) {
+      float t[B];
+      dequant_block<FMT, OUTER, INV>(a, s_t, w.major, w.minor, t);
+      uint32_t v[B / 2];
+      pack_out<T>(t, v, B);
+      uint32_t* to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
+#pragma unroll
+      for (int q = 0; q < B / 8; ++q) store16<false>(to + 4 * q, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      w.advance(a.sq, a.sr, a.M);
     }
-    const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
-    uint32_t words[B / 8];
-    if constexpr (B == 16) {
-      const uint2 v = *reinterpret_cast<const uint2*>(cp);
-      words[0] = v.x; words[1] = v.y;
-    } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(cp);
-      words[0] = v.x; words[1] = v.y; words[2] = v.z; words[3] = v.w;
-    }
-#pragma unroll
-    for (int h = 0; h < B / 16; ++h) {
-      float t[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
-        const float mag = grid_level<FMT>(c & 7u) * d;
-        t[j] = (c & 8u) ? -mag : mag;
-      }
-      if (INV) rht16_inverse(t, a.signs);
-      const int64_t j0 = b * B + h * 16;
-      if (AXIS == 0 && sizeof(T) == 4) {
-        T* o = out + ra * a.ld_out + j0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store16<false>(o + 4 * i, __float_as_uint(t[4 * i]), __float_as_uint(t[4 * i + 1]),
-                  __float_as_uint(t[4 * i + 2]), __float_as_uint(t[4 * i + 3]));
-      } else if (AXIS == 0) {
-        // 16 BF16 values: two 16-byte stores (rows are 16-byte aligned)
-        uint32_t pk[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pk[i] = bf16_rne(t[2 * i]) | (bf16_rne(t[2 * i + 1]) << 16);
-        T* o = out + ra * a.ld_out + j0;
-        store16<false>(o, pk[0], pk[1], pk[2], pk[3]);
-        store16<false>(o + 8, pk[4], pk[5], pk[6], pk[7]);
+  } else if constexpr (AXIS == 0) {
+    // FP32 rows: units (A-row, block), block fastest; the whole workgroup
+    // steps together so that it can stage its outputs
+    constexpr int WORDS = B * (int)sizeof(T) / 4;
+    using Stage = RowStage<WORDS>;
+    __shared__ __align__(16) uint32_t sbuf[kThreads * Stage::P];
+    __shared__ uint32_t* sdst[kThreads];
+    const Stage st{sbuf, sdst};
+    const int64_t units = a.n_major * a.M;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < units;
+         base += (int64_t)gridDim.x * kThreads) {
+      uint32_t v[WORDS];
+      uint32_t* to = nullptr;
+      if (w.major < a.n_major) {
+        float t[B];
+        dequant_block<FMT, OUTER, INV>(a, s_t, w.major, w.minor, t);
+        pack_out<T>(t, v, B);
+        to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          T* p = AXIS == 0 ? out + ra * a.ld_out + j0 + j : out + (j0 + j) * a.ld_out + ra;
-          store_elem(p, t[j]);
-        }
+        for (int j = 0; j < WORDS; ++j) v[j] = 0u;
       }
+      st.put(v, to);
+      __syncthreads();
+      st.flush();
+      __syncthreads();
+      w.advance(a.sq, a.sr, a.M);
     }
-    w.advance(a.sq, a.sr, a.M);
+  } else {
+    while (w.major < a.n_major) {
+      const int64_t ra = w.minor, b = w.major;
+      float t[B];
+      dequant_block<FMT, OUTER, INV>(a, s_t, ra, b, t);
+#pragma unroll
+      for (int j = 0; j < B; ++j) store_elem(out + (b * B + j) * a.ld_out + ra, t[j]);
+      w.advance(a.sq, a.sr, a.M);
+    }
   }
 }
 
@@ -126,24 +205,44 @@ __global__ __launch_bounds__(kThreads) void rht_kernel(const T* __restrict__ x, 
                                                        float* __restrict__ y) {
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, M);
-  while (w.major < n_major) {
-    const int64_t ra = AXIS == 0 ? w.major : w.minor;
-    const int64_t g = AXIS == 0 ? w.minor : w.major;
-    float t[16];
-    load_group<AXIS>(x, ld, ra, g * 16, t);
-    if (INV) rht16_inverse(t, signs);
-    else rht16_forward(t, signs);
-    if (AXIS == 0) {
-      float* o = y + ra * cols + g * 16;
+  if constexpr (AXIS == 0) {
+    using Stage = RowStage<16>;
+    __shared__ __align__(16) uint32_t sbuf[kThreads * Stage::P];
+    __shared__ uint32_t* sdst[kThreads];
+    const Stage st{sbuf, sdst};
+    const int64_t units = n_major * M;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < units;
+         base += (int64_t)gridDim.x * kThreads) {
+      uint32_t v[16];
+      uint32_t* to = nullptr;
+      if (w.major < n_major) {
+        float t[16];
+        load_group<0>(x, ld, w.major, w.minor * 16, t);
+        if (INV) rht16_inverse(t, signs);
+        else rht16_forward(t, signs);
+        pack_out<float>(t, v, 16);
+        to = reinterpret_cast<uint32_t*>(y + w.major * cols + w.minor * 16);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store16<false>(o + 4 * i, __float_as_uint(t[4 * i]), __float_as_uint(t[4 * i + 1]),
-                __float_as_uint(t[4 * i + 2]), __float_as_uint(t[4 * i + 3]));
-    } else {
+        for (int j = 0; j < 16; ++j) v[j] = 0u;
+      }
+      st.put(v, to);
+      __syncthreads();
+      st.flush();
+      __syncthreads();
+      w.advance(sq, sr, M);
+    }
+  } else {
+    while (w.major < n_major) {
+      const int64_t ra = w.minor, g = w.major;
+      float t[16];
+      load_group<1>(x, ld, ra, g * 16, t);
+      if (INV) rht16_inverse(t, signs);
+      else rht16_forward(t, signs);
 #pragma unroll
       for (int j = 0; j < 16; ++j) y[(g * 16 + j) * cols + ra] = t[j];
+      w.advance(sq, sr, M);
     }
-    w.advance(sq, sr, M);
   }
 }
 
