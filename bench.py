@@ -81,6 +81,14 @@ def op_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
     return algorithmic_bytes(rows, cols, c.fmt, in_bytes, c.outer, 2 if c.axis == "both" else 1)
 
 
+def moved_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
+    """Bytes the chosen algorithm moves: the algorithmic bytes plus, for a
+    quantize call with a computed tensor scale (two-level formats without
+    outer scales), the tensor-amax pass's second read of the input."""
+    extra = (c.op == "quantize" and c.fmt not in MX and not c.outer)
+    return op_bytes(c, rows, cols, in_bytes) + (rows * cols * in_bytes if extra else 0)
+
+
 def traffic_for(workload: str, call_index: int):
     """HBM bytes per launch from committed rocprofv3 counters, if they were
     taken on the current kernel sources; else None."""
@@ -241,6 +249,7 @@ def main():
         pl = dict(call=call, x=x, outs=outs,
                   ws=torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None,
                   alg=op_bytes(call, rows, cols, x.element_size()),
+                  moved=moved_bytes(call, rows, cols, x.element_size()),
                   in_bytes=x.numel() * x.element_size())
         if call.op == "dequantize":   # this call's codes, made once outside the timed region
             codes, scales, ts = outs[0]
@@ -327,6 +336,15 @@ def main():
                 tot += a.elapsed_time(b)
             cold_per_call.append(tot / creps)
         del scratch
+    # per call: algorithmic (single-read) bytes, bytes as moved (with the
+    # amax pass's re-read) and counter-measured HBM bytes, each over the
+    # call's mean duration, as fractions of the 8 TB/s peak
+    def frac(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    frac_alg = [frac(pl["alg"], m) for pl, m in zip(plans, per_call)]
+    frac_moved = [frac(pl["moved"], m) for pl, m in zip(plans, per_call)]
+    measured = [traffic_for(args.workload, i) for i in range(len(plans))]
+    frac_rocprof = [frac(t, m) if t else None for t, m in zip(measured, per_call)]
     dom = max(range(len(plans)), key=lambda i: per_call[i])
     pl = plans[dom]
     achieved = pl["alg"] / (per_call[dom] * 1e-3) / 1e9
@@ -369,6 +387,8 @@ def main():
                    "calls": [call_label(c) for c in w.calls],
                    "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
                    "per_call_us": [round(m * 1e3, 2) for m in per_call],
+                   "frac_alg": frac_alg, "frac_moved": frac_moved,
+                   "frac_rocprof": frac_rocprof if any(frac_rocprof) else None,
                    "wall_ms_per_step": round(wall_ms, 4),
                    "cold_per_call_us": [round(m * 1e3, 2) for m in cold_per_call] or None,
                    "cold_input_gbs": round(in_bytes / (sum(cold_per_call) * 1e-3) / 1e9, 2)

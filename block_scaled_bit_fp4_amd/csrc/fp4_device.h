@@ -41,15 +41,39 @@ __device__ __forceinline__ uint32_t pair_sign_mask(uint32_t signs, int e) {
   return (((signs >> (2 * e)) & 1u) << 15) | (((signs >> (2 * e + 1)) & 1u) << 31);
 }
 
-// Widen the 8 words of a BF16 16-group, flipping signs when SIGN.
+// Half H (0 low, 1 high) of w xor the same half of the wave-uniform m,
+// moved to bits 31..16 of a word whose low half is zero: one BF16 element
+// with its sign flipped, widened exactly to binary32, in one SDWA
+// instruction that reads m from a scalar register.  (Written out as C, the
+// high half compiles to a three-input op that needs m copied to a vector
+// register first.)
+template <int H>
+__device__ __forceinline__ uint32_t xor_widen_bf16(uint32_t w, uint32_t m) {
+  uint32_t r;
+  if constexpr (H == 0)
+    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_0 "
+        "src1_sel:WORD_0" : "=v"(r) : "v"(w), "s"(m));
+  else
+    asm("v_xor_b32_sdwa %0, %1, %2 dst_sel:WORD_1 dst_unused:UNUSED_PAD src0_sel:WORD_1 "
+        "src1_sel:WORD_1" : "=v"(r) : "v"(w), "s"(m));
+  return r;
+}
+
+// Widen the 8 words of a BF16 16-group, flipping signs when SIGN (signs is
+// wave-uniform: the RHT's one sign vector).
 template <bool SIGN>
 __device__ __forceinline__ void widen_bf16_group(const uint32_t (&w)[8], uint32_t signs,
                                                  float (&t)[16]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t v = SIGN ? w[e] ^ pair_sign_mask(signs, e) : w[e];
-    t[2 * e] = bf16_lo(v);
-    t[2 * e + 1] = bf16_hi(v);
+    if constexpr (SIGN) {
+      const uint32_t m = pair_sign_mask(signs, e);
+      t[2 * e] = __uint_as_float(xor_widen_bf16<0>(w[e], m));
+      t[2 * e + 1] = __uint_as_float(xor_widen_bf16<1>(w[e], m));
+    } else {
+      t[2 * e] = bf16_lo(w[e]);
+      t[2 * e + 1] = bf16_hi(w[e]);
+    }
   }
 }
 

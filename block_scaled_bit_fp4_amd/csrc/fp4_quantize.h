@@ -137,24 +137,28 @@ __device__ __forceinline__ ScaleCtx scale_prologue(const QuantArgs& a, float* in
 
 // Elements 2j and 2j + 1 of v, stochastically rounded in hardware with the
 // draws of Philox word w (element 2j its low half, 2j + 1 its high half).
-// Both converts take the pair; the first uses element 2j's draw and is kept
-// for the low nibble, the second element 2j + 1's draw and is kept for the
-// high nibble.  Only byte 0 of each result is defined (the compiler does
-// not carry the convert's other destination bytes through); the caller
-// gathers and merges the bytes.
-__device__ __forceinline__ void sr_pair_e2m1(float ve, float vo, uint32_t w, uint32_t& lo,
-                                             uint32_t& hi) {
+// Both converts take the pair (odd element first); the first uses the odd
+// element's draw and keeps its code in the low nibble, the second the even
+// element's draw and keeps its code in the high nibble.  Only byte 0 of each
+// result is defined (the compiler does not carry the convert's other
+// destination bytes through); the caller gathers and swaps the nibbles.
+__device__ __forceinline__ void sr_pair_e2m1(float ve, float vo, uint32_t w, uint32_t& odd,
+                                             uint32_t& even) {
   typedef float f2 __attribute__((ext_vector_type(2)));
-  const uint32_t nw = ~w;
-  // first slot: random bits 31..10 = (~u16 << 6) | 0b111111
-  const uint32_t r0 = __builtin_amdgcn_alignbit(nw, 0xFFFFFFFFu, 16);  // (~w << 16) | 0xFFFF
-  // second slot: random bits 30..9 = (~u16 << 6) | 0b111111
-  const uint32_t r1 = (nw >> 1) | 0x7E00u;
+  // first slot, bits 31..10: ~(high half) then six ones = ~w | 0xFFFF
+  // (three-input op, truth table 0xCF = ~a | b)
+  const uint32_t r0 = __builtin_amdgcn_bitop3_b32(w, 0xFFFFu, 0u, 0xCF);
+  // second slot, bits 30..9: ~(low half) then six ones = ~(w << 15)
+  // = w * -2^15 - 1 in 24-bit signed multiply-add (only w's low 17 bits
+  // reach bits 31..15), one instruction where the compiler would emit a
+  // shift and a not
+  uint32_t r1;
+  asm("v_mad_i32_i24 %0, %1, %2, -1" : "=v"(r1) : "v"(w), "s"(-32768));
   f2 p;
-  p.x = ve;
-  p.y = vo;
-  lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r0, 1.0f, 0);
-  hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r1, 1.0f, 0);
+  p.x = vo;
+  p.y = ve;
+  odd = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r0, 1.0f, 0);
+  even = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r1, 1.0f, 0);
 }
 
 // Bytes 0 of a, b, c, d as one word (selector 0x0C gives a zero byte).
@@ -193,12 +197,14 @@ __device__ __forceinline__ uint32_t encode8_fast(const float* v, const uint32_t 
     // 64 * u16 + 1, the rounding rule.  The two elements of a byte need
     // independent draws, so each pair is converted twice, once with each
     // element's draw, and each element's nibble is taken from its convert.
-    uint32_t lo[4], hi[4];
+    // The pair enters odd element first: each slot then takes its draw from
+    // w in one instruction (above), and the nibbles swap back in the merge.
+    uint32_t od[4], ev[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sr_pair_e2m1(v[2 * j], v[2 * j + 1], r[j], lo[j], hi[j]);
-    const uint32_t wl = gather_low_bytes(lo[0], lo[1], lo[2], lo[3]);
-    const uint32_t wh = gather_low_bytes(hi[0], hi[1], hi[2], hi[3]);
-    word = (wl & 0x0F0F0F0Fu) | (wh & 0xF0F0F0F0u);
+    for (int j = 0; j < 4; ++j) sr_pair_e2m1(v[2 * j], v[2 * j + 1], r[j], od[j], ev[j]);
+    const uint32_t wo = gather_low_bytes(od[0], od[1], od[2], od[3]);  // odd codes, low nibbles
+    const uint32_t we = gather_low_bytes(ev[0], ev[1], ev[2], ev[3]);  // even codes, high nibbles
+    word = ((we >> 4) & 0x0F0F0F0Fu) | ((wo << 4) & 0xF0F0F0F0u);
   } else {
 #pragma unroll
     for (int l = 0; l < 8; ++l) {
@@ -558,54 +564,63 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   constexpr int TR = Tile::TR, TC = Tile::TC;
   constexpr int kLoads = TR * TC * (int)sizeof(T) / 16 / kThreads;  // 16-byte loads per lane
   constexpr int kUnits = TC * (TR / B) / kThreads;                  // blocks coded per lane
+  constexpr int LPR = TR / B;              // lanes per A-row of a tile (its blocks)
+  constexpr int kRowStep = kThreads / LPR;  // A-rows between a lane's units
   __shared__ float inv_tab[128];
   __shared__ __align__(16) uint32_t lds[Tile::kWords];
   const int64_t ntile = a.n_major * a.M;  // row tiles x column tiles, column tile fastest
 
-  // load i: segment threadIdx % 8 of row tile_row(i); for BF16, loads i and
-  // i + kLoads/2 are the two rows of one pair
-  auto load_tile = [&](int64_t tile, uint4 (&buf)[kLoads]) {
-    const int64_t tr = tile / a.M, tc = tile - tr * a.M;
-    const T* base = x + tr * TR * a.ld + tc * TC;
+  // Load i of a lane reads 16 bytes of tile row lane_row + row_i at byte
+  // lane_col: lane_row and lane_col depend on the lane only, row_i on i
+  // only, so every address is a wave-uniform base plus one per-lane 32-bit
+  // offset (the launcher keeps a tile's extent below 2^31 bytes).  For BF16,
+  // loads i and i + kLoads/2 are the two rows of one pair.
+  const int seg = threadIdx.x & 7;
+  const uint32_t lane_off = (uint32_t)(((sizeof(T) == 2 ? 2 : 1) * (threadIdx.x >> 3)) * a.ld +
+                                       seg * (16 / (int)sizeof(T))) * (uint32_t)sizeof(T);
+  auto load_tile = [&](int64_t tr, int64_t tc, uint4 (&buf)[kLoads]) {
+    const char* base = reinterpret_cast<const char*>(x + tr * TR * a.ld + tc * TC);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      int row;
-      if constexpr (sizeof(T) == 2)
-        row = 2 * ((threadIdx.x >> 3) + 32 * (i % (kLoads / 2))) + (i >= kLoads / 2 ? 1 : 0);
-      else
-        row = (threadIdx.x >> 3) + 32 * i;
-      const int seg = threadIdx.x & 7;
-      buf[i] = *reinterpret_cast<const uint4*>(base + row * a.ld + seg * (16 / (int)sizeof(T)));
+      const int row_i = sizeof(T) == 2 ? 64 * (i % (kLoads / 2)) + (i >= kLoads / 2 ? 1 : 0)
+                                       : 32 * i;
+      const char* p = base + (int64_t)row_i * a.ld * (int64_t)sizeof(T);
+      buf[i] = *reinterpret_cast<const uint4*>(p + lane_off);
     }
   };
 
+  // (row tile, column tile) walk with a grid stride, no division in the loop
+  const int64_t step_r = gridDim.x / a.M, step_c = gridDim.x - step_r * a.M;
   int64_t tile = blockIdx.x;
+  int64_t tr = tile / a.M, tc = tile - tr * a.M;
   bool have = tile < ntile;
   uint4 buf[kLoads];
-  if (have) load_tile(tile, buf);  // in flight during the prologue
+  if (have) load_tile(tr, tc, buf);  // in flight during the prologue
   const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
+  // a lane's units: A-rows lane_ra + kRowStep * i of the tile, block j
+  const int lane_ra = threadIdx.x / LPR, j = threadIdx.x % LPR;
   while (have) {
-    const int64_t tr = tile / a.M, tc = tile - tr * a.M;
     const int64_t r0 = tr * TR, c0 = tc * TC;
     __syncthreads();  // previous tile's LDS reads are done
     // ---- registers -> LDS, transposed
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < kLoads / 2; ++i) {
-        const int pr = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;  // row pair, segment
+        const int pr = (threadIdx.x >> 3) + 32 * i;  // row pair
         const uint4 e = buf[i], o = buf[i + kLoads / 2];
         const uint32_t ev[4] = {e.x, e.y, e.z, e.w}, od[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int col = seg * 8 + 2 * k;
-          lds[Tile::at(col, pr)] = (ev[k] & 0xFFFFu) | (od[k] << 16);
-          lds[Tile::at(col + 1, pr)] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
+          // (even row, odd row) of column col, then of col + 1: byte picks
+          lds[Tile::at(col, pr)] = __builtin_amdgcn_perm(od[k], ev[k], 0x05040100u);
+          lds[Tile::at(col + 1, pr)] = __builtin_amdgcn_perm(od[k], ev[k], 0x07060302u);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int row = (threadIdx.x >> 3) + 32 * i, seg = threadIdx.x & 7;
+        const int row = (threadIdx.x >> 3) + 32 * i;
         const uint32_t v[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) lds[Tile::at(seg * 4 + k, row)] = v[k];
@@ -615,14 +630,20 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
     // ---- the next tile's loads fly while this one is coded
     const int64_t next = tile + gridDim.x;
     const bool have_next = next < ntile;
-    if (have_next) load_tile(next, buf);
-    // ---- code blocks: unit u -> (A-row cl, block j), block fastest; units
-    // one at a time for 32-element blocks (register pressure)
+    int64_t ntr = tr + step_r, ntc = tc + step_c;
+    if (ntc >= a.M) { ntc -= a.M; ntr += 1; }
+    if (have_next) load_tile(ntr, ntc, buf);
+    // ---- code blocks: unit i -> (A-row lane_ra + kRowStep * i, block j);
+    // units one at a time for 32-element blocks (register pressure)
+    const int64_t ra0 = c0 + lane_ra;  // A-row = column of x
+    const int64_t rb = r0 / B + j;     // block index along the A-row
+    uint8_t* cp0 = a.codes + ra0 * (a.W / 2) + rb * (B / 2);
+    uint8_t* sp0 = a.scales + ra0 * a.nblk_axis + rb;
+    const uint64_t n00 = (uint64_t)ra0 * (uint64_t)a.W + (uint64_t)(rb * B);
     constexpr int kUnroll = B == 32 ? 1 : kUnits;
 #pragma unroll kUnroll
     for (int i = 0; i < kUnits; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int cl = u / (TR / B), j = u % (TR / B);
+      const int cl = lane_ra + kRowStep * i;
       float t[B];
       float amax_t = 0.0f;
 #pragma unroll
@@ -647,9 +668,8 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
           amax_t = fmaxf(amax_t, fabsf(g[e]));
         }
       }
-      const int64_t ra = c0 + cl;                 // A-row = column of x
-      const int64_t rb = r0 / B + j;              // block index along the A-row
-      const uint64_t n0 = (uint64_t)ra * (uint64_t)a.W + (uint64_t)(rb * B);
+      const int64_t di = (int64_t)kRowStep * i;  // A-rows past the lane's first
+      const uint64_t n0 = n00 + (uint64_t)di * (uint64_t)a.W;
       ScaleCtx cc = c;
       if constexpr (TSM == kTsOuter) {
         // kOuter / B consecutive lanes hold the blocks of one 128-piece
@@ -657,18 +677,20 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
         const float ao = group_max<LPO>(amax_t);
         cc.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
         cc.den = cc.s_t * grid_max<FMT>();
-        if (j % LPO == 0) a.ts_out[ra * (a.W / kOuter) + rb / LPO] = cc.s_t;
+        if (j % LPO == 0) a.ts_out[(ra0 + di) * (a.W / kOuter) + rb / LPO] = cc.s_t;
       }
       uint32_t pk[B / 8];
       uint32_t sbyte;
       encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
                                                          a.sr_k1, n0, pk, sbyte);
-      uint8_t* cp = a.codes + ra * (a.W / 2) + rb * (B / 2);
+      uint8_t* cp = cp0 + di * (a.W / 2);
       if constexpr (B == 16) store8<true>(cp, pk[0], pk[1]);
       else store16<true>(cp, pk[0], pk[1], pk[2], pk[3]);
-      a.scales[ra * a.nblk_axis + rb] = (uint8_t)sbyte;
+      sp0[di * a.nblk_axis] = (uint8_t)sbyte;
     }
     tile = next;
+    tr = ntr;
+    tc = ntc;
     have = have_next;
   }
 }
@@ -1021,7 +1043,9 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
     using Tile = ColTile<T>;
     // interior: whole tiles; edges (bottom rows, right columns): run kernel
     const int64_t nrt = q.rows / Tile::TR, nct = q.cols / Tile::TC;
-    const bool tiles = nrt > 0 && nct > 0 && (q.ld * (int64_t)sizeof(T)) % 16 == 0;
+    // (a tile's byte extent below 2^31 keeps its per-lane load offsets in 32 bits)
+    const bool tiles = nrt > 0 && nct > 0 && (q.ld * (int64_t)sizeof(T)) % 16 == 0 &&
+                       q.ld * (int64_t)sizeof(T) * Tile::TR < ((int64_t)1 << 31);
     const int64_t rows_main = tiles ? nrt * Tile::TR : 0;
     const int64_t cols_main = tiles ? nct * Tile::TC : 0;
     if (tiles) {
