@@ -181,8 +181,9 @@ fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int6
     if (ws_bytes < 2 * sizeof(float) * (size_t)kAmaxPartials) return FP4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FP4_ERR_ALIGN;
   }
+  // fused tiles: BF16, whole 128 x 128 tiles, a tile's byte extent below 2^31
   const bool fused = !empty && in_dtype == FP4_BF16 && !is_mx(p->format) && rows % 128 == 0 &&
-                     cols % 128 == 0;
+                     cols % 128 == 0 && ld * 2 * 128 < ((int64_t)1 << 31);
   if (!fused) {
     // the two single-axis calls, one after the other on the stream
     st = fp4_quantize(x, in_dtype, rows, cols, ld, &pr, codes_row, scales_row, ts_row,

@@ -107,22 +107,52 @@ struct ScaleCtx {
   float s_t, den;
 };
 
+// Tensor-scale inputs of a workgroup: the amax partial maxima (4 per lane)
+// or the given scale.  Fetched before the lane's first data loads: loads
+// complete in issue order, so the prologue then waits only for these and
+// not for the data behind them.
+constexpr int kFetch = kAmaxPartials / kThreads;
+static_assert(kAmaxPartials % kThreads == 0, "partials per lane");
+struct ScaleFetch {
+  float v[kFetch];
+};
+
+template <int FMT, int TSM>
+__device__ __forceinline__ ScaleFetch scale_fetch(const float* partials, int npartials,
+                                                  const float* ts_in) {
+  ScaleFetch f;
+#pragma unroll
+  for (int k = 0; k < kFetch; ++k) f.v[k] = 0.0f;
+  if constexpr (!is_mx(FMT) && TSM == kTsCompute) {
+#pragma unroll
+    for (int k = 0; k < kFetch; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < npartials) f.v[k] = partials[i];
+    }
+  } else if constexpr (!is_mx(FMT) && TSM == kTsGiven) {
+    f.v[0] = ts_in[0];
+  }
+  return f;
+}
+
 // Tensor scale s_t = amax / (G * 448) and, in LDS, the reciprocal of every
 // decoded block scale: inv[S] = 1 / (s_t * decode(S)), 0 where that is 0.
 // Nothing for the MX formats and for outer scales (per 128-piece, coded
 // with the blocks).
 template <int FMT, int TSM>
-__device__ __forceinline__ ScaleCtx scale_prologue(const QuantArgs& a, float* inv_tab) {
+__device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* ts_out,
+                                                   float* inv_tab) {
   ScaleCtx c{0.0f, 0.0f};
   if constexpr (!is_mx(FMT) && TSM != kTsOuter) {
     if (TSM == kTsGiven) {
-      c.s_t = a.ts_in[0];
+      c.s_t = f.v[0];
     } else {
-      float m = 0.0f;
-      for (int i = threadIdx.x; i < a.npartials; i += kThreads) m = fmaxf(m, a.partials[i]);
+      float m = f.v[0];
+#pragma unroll
+      for (int k = 1; k < kFetch; ++k) m = fmaxf(m, f.v[k]);
       m = block_max_256(m);
       c.s_t = m / (grid_max<FMT>() * 448.0f);
-      if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
+      if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[0] = c.s_t;
     }
     c.den = c.s_t * grid_max<FMT>();
     if (threadIdx.x < 128) {
@@ -316,8 +346,9 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
   RowRaw<T, U> cur;
   bool have = w.major < a.n_major;
+  const ScaleFetch sf = scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in);
   if (have) cur.load(x + w.major * a.ld + w.minor * U);  // in flight during the prologue
-  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
+  const ScaleCtx c = scale_prologue<FMT, TSM>(sf, a.ts_out, inv_tab);
   while (have) {
     Walk nw = w;
     nw.advance(a.sq, a.sr, a.M);
@@ -408,7 +439,9 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
   constexpr int B = block_of<FMT>();
   constexpr int WPB = B / 8;  // code words per block
   __shared__ float inv_tab[128];
-  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
+  const ScaleCtx c =
+      scale_prologue<FMT, TSM>(scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in),
+                               a.ts_out, inv_tab);
   const bool vec_codes = (a.W % 32) == 0;  // 16-byte aligned A-rows of codes
 
   Walk w;
@@ -595,8 +628,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   int64_t tr = tile / a.M, tc = tile - tr * a.M;
   bool have = tile < ntile;
   uint4 buf[kLoads];
+  const ScaleFetch sf = scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in);
   if (have) load_tile(tr, tc, buf);  // in flight during the prologue
-  const ScaleCtx c = scale_prologue<FMT, TSM>(a, inv_tab);
+  const ScaleCtx c = scale_prologue<FMT, TSM>(sf, a.ts_out, inv_tab);
   // a lane's units: A-rows lane_ra + kRowStep * i of the tile, block j
   const int lane_ra = threadIdx.x / LPR, j = threadIdx.x % LPR;
   while (have) {
@@ -733,19 +767,21 @@ struct DualArgs {
 
 // Both axes' tensor scales and reciprocal tables (nothing for outer scales).
 template <int FMT, int TSM>
-__device__ __forceinline__ void dual_prologue(const DualArgs& a, float* inv_r, float* inv_c,
+__device__ __forceinline__ void dual_prologue(const DualArgs& a, const ScaleFetch& fr,
+                                              const ScaleFetch& fc, float* inv_r, float* inv_c,
                                               ScaleCtx& cr, ScaleCtx& cc) {
   cr = ScaleCtx{0.0f, 0.0f};
   cc = ScaleCtx{0.0f, 0.0f};
   if constexpr (TSM != kTsOuter) {
     if (TSM == kTsGiven) {
-      cr.s_t = a.ts_in_r[0];
-      cc.s_t = a.ts_in_c[0];
+      cr.s_t = fr.v[0];
+      cc.s_t = fc.v[0];
     } else {
-      float mr = 0.0f, mc = 0.0f;
-      for (int i = threadIdx.x; i < a.npartials; i += kThreads) {
-        mr = fmaxf(mr, a.partials[i]);
-        mc = fmaxf(mc, a.partials[a.npartials + i]);
+      float mr = fr.v[0], mc = fc.v[0];
+#pragma unroll
+      for (int k = 1; k < kFetch; ++k) {
+        mr = fmaxf(mr, fr.v[k]);
+        mc = fmaxf(mc, fc.v[k]);
       }
       mr = block_max_256(mr);
       mc = block_max_256(mc);
@@ -778,26 +814,35 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
   __shared__ __align__(16) uint32_t lds[kDT * kDP];
   const int seg = threadIdx.x & 15;  // 16-byte column segment (8 columns)
   const int q = threadIdx.x >> 4;    // row pair within a pass
-  // load i: rows 2p and 2p + 1 (p = q + 16 * (i % 4)) are loads i and i + 4
-  auto load_tile = [&](int64_t tile, uint4 (&buf)[kLoads]) {
-    const int64_t tr = tile / a.n_ct, tc = tile - tr * a.n_ct;
-    const uint16_t* base = x + tr * kDT * a.ld + tc * kDT + seg * 8;
+  // load i: rows 2p and 2p + 1 (p = q + 16 * (i % 4)) are loads i and i + 4;
+  // a wave-uniform base per load plus one per-lane 32-bit offset (the
+  // launcher keeps a tile's byte extent below 2^31)
+  const uint32_t lane_off = (uint32_t)(2 * q * a.ld + seg * 8) * 2u;
+  auto load_tile = [&](int64_t tr, int64_t tc, uint4 (&buf)[kLoads]) {
+    const char* base = reinterpret_cast<const char*>(x + tr * kDT * a.ld + tc * kDT);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int row = 2 * (q + 16 * (i & 3)) + (i >> 2);
-      buf[i] = *reinterpret_cast<const uint4*>(base + row * a.ld);
+      const int row_i = 32 * (i & 3) + (i >> 2);
+      buf[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row_i * a.ld * 2 + lane_off);
     }
   };
 
+  // (row tile, column tile) walk with a grid stride, no division in the loop
+  const int64_t step_r = gridDim.x / a.n_ct, step_c = gridDim.x - step_r * a.n_ct;
   int64_t tile = blockIdx.x;
+  int64_t tr = tile / a.n_ct, tc = tile - tr * a.n_ct;
   bool have = tile < a.ntile;
   uint4 buf[kLoads];
-  if (have) load_tile(tile, buf);  // in flight during the prologue
+  ScaleFetch fr{}, fc{};
+  if constexpr (!AMAX) {
+    fr = scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in_r);
+    fc = scale_fetch<FMT, TSM>(a.partials + a.npartials, a.npartials, a.ts_in_c);
+  }
+  if (have) load_tile(tr, tc, buf);  // in flight during the prologue
   ScaleCtx cr, cc;
-  if constexpr (!AMAX) dual_prologue<FMT, TSM>(a, inv_r, inv_c, cr, cc);
+  if constexpr (!AMAX) dual_prologue<FMT, TSM>(a, fr, fc, inv_r, inv_c, cr, cc);
   float mr = 0.0f, mc = 0.0f;  // AMAX: running maxima of the two axes
   while (have) {
-    const int64_t tr = tile / a.n_ct, tc = tile - tr * a.n_ct;
     const int64_t r0 = tr * kDT, c0 = tc * kDT;
     __syncthreads();  // previous tile's LDS reads are done
     // ---- registers -> LDS, transposed, for the column part
@@ -809,12 +854,18 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int col = seg * 8 + 2 * k;
-        lds[dual_at(col, pr)] = (ev[k] & 0xFFFFu) | (od[k] << 16);
-        lds[dual_at(col + 1, pr)] = (ev[k] >> 16) | (od[k] & 0xFFFF0000u);
+        // (even row, odd row) of column col, then of col + 1: byte picks
+        lds[dual_at(col, pr)] = __builtin_amdgcn_perm(od[k], ev[k], 0x05040100u);
+        lds[dual_at(col + 1, pr)] = __builtin_amdgcn_perm(od[k], ev[k], 0x07060302u);
       }
     }
     // ---- row part, from the registers
     const bool odd = seg & 1;
+    const int64_t row0 = r0 + 2 * q + (odd ? 1 : 0);  // the lane's row in pass 0
+    const int64_t b = c0 / 16 + (seg >> 1);           // block along the row
+    uint8_t* cpr = a.codes_r + row0 * (a.cols / 2) + b * 8;
+    uint8_t* spr = a.scales_r + row0 * (a.cols / 16) + b;
+    const uint64_t nr0 = (uint64_t)row0 * (uint64_t)a.cols + (uint64_t)(b * 16);
 #pragma unroll
     for (int i = 0; i < kLoads / 2; ++i) {
       const uint4 send = odd ? buf[i] : buf[i + kLoads / 2];
@@ -835,36 +886,41 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
       if constexpr (AMAX) {
         mr = fmaxf(mr, amax_t);
       } else {
-        const int64_t row = r0 + 2 * (q + 16 * i) + (odd ? 1 : 0);
-        const int64_t b = c0 / 16 + (seg >> 1);  // block along the row
+        const int64_t dr = 32 * i;  // rows past the lane's pass-0 row
         ScaleCtx c = cr;
         if constexpr (TSM == kTsOuter) {
           // the 8 lanes of this parity hold the row's 128-piece
           const float ao = parity_max16(amax_t);
           c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
           c.den = c.s_t * grid_max<FMT>();
-          if (seg < 2) a.ts_out_r[row * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
+          if (seg < 2) a.ts_out_r[(row0 + dr) * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
         }
         uint32_t pk[2];
         uint32_t sbyte;
         encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_r, a.sr_k0, a.sr_k1,
-                                                  (uint64_t)row * (uint64_t)a.cols +
-                                                      (uint64_t)(b * 16),
-                                                  pk, sbyte);
-        store8<true>(a.codes_r + row * (a.cols / 2) + b * 8, pk[0], pk[1]);
-        a.scales_r[row * (a.cols / 16) + b] = (uint8_t)sbyte;
+                                                  nr0 + (uint64_t)dr * (uint64_t)a.cols, pk,
+                                                  sbyte);
+        store8<true>(cpr + dr * (a.cols / 2), pk[0], pk[1]);
+        spr[dr * (a.cols / 16)] = (uint8_t)sbyte;
       }
     }
     __syncthreads();
     // ---- the next tile's loads fly while the column part is coded
     const int64_t next = tile + gridDim.x;
     const bool have_next = next < a.ntile;
-    if (have_next) load_tile(next, buf);
-    // ---- column part: unit u -> (x column cl, block j of 16 rows), j fastest
+    int64_t ntr = tr + step_r, ntc = tc + step_c;
+    if (ntc >= a.n_ct) { ntc -= a.n_ct; ntr += 1; }
+    if (have_next) load_tile(ntr, ntc, buf);
+    // ---- column part: unit i -> (x column (tid >> 3) + 32 i, block j = tid & 7)
+    const int j = threadIdx.x & 7;
+    const int64_t ra0 = c0 + (threadIdx.x >> 3);  // A-row = column of x
+    const int64_t rb = r0 / 16 + j;               // block down the column
+    uint8_t* cpc = a.codes_c + ra0 * (a.rows / 2) + rb * 8;
+    uint8_t* spc = a.scales_c + ra0 * (a.rows / 16) + rb;
+    const uint64_t nc0 = (uint64_t)ra0 * (uint64_t)a.rows + (uint64_t)(rb * 16);
 #pragma unroll
     for (int i = 0; i < kDT * (kDT / 16) / kThreads; ++i) {
-      const int u = threadIdx.x + i * kThreads;
-      const int cl = u >> 3, j = u & 7;
+      const int cl = (threadIdx.x >> 3) + 32 * i;
       const uint4 lo = *reinterpret_cast<const uint4*>(lds + dual_at(cl, 8 * j));
       const uint4 hi = *reinterpret_cast<const uint4*>(lds + dual_at(cl, 8 * j + 4));
       const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -877,26 +933,26 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
       if constexpr (AMAX) {
         mc = fmaxf(mc, amax_t);
       } else {
-        const int64_t ra = c0 + cl;     // A-row = column of x
-        const int64_t rb = r0 / 16 + j;  // block down the column
+        const int64_t da = 32 * i;  // A-rows past the lane's first
         ScaleCtx c = cc;
         if constexpr (TSM == kTsOuter) {
           const float ao = group_max<8>(amax_t);
           c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
           c.den = c.s_t * grid_max<FMT>();
-          if (j == 0) a.ts_out_c[ra * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
+          if (j == 0) a.ts_out_c[(ra0 + da) * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
         }
         uint32_t pk[2];
         uint32_t sbyte;
         encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_c, a.sr_k0, a.sr_k1,
-                                                  (uint64_t)ra * (uint64_t)a.rows +
-                                                      (uint64_t)(rb * 16),
-                                                  pk, sbyte);
-        store8<true>(a.codes_c + ra * (a.rows / 2) + rb * 8, pk[0], pk[1]);
-        a.scales_c[ra * (a.rows / 16) + rb] = (uint8_t)sbyte;
+                                                  nc0 + (uint64_t)da * (uint64_t)a.rows, pk,
+                                                  sbyte);
+        store8<true>(cpc + da * (a.rows / 2), pk[0], pk[1]);
+        spc[da * (a.rows / 16)] = (uint8_t)sbyte;
       }
     }
     tile = next;
+    tr = ntr;
+    tc = ntc;
     have = have_next;
   }
   if constexpr (AMAX) {
