@@ -118,6 +118,30 @@ __device__ __forceinline__ void fwht16(float (&t)[16]) {
   }
 }
 
+// Largest magnitude of fwht16(t), without its outputs: after the stages
+// h = 1, 2, 4 the last stage would give u + v and u - v for each pair
+// (u, v) = (t[j], t[j + 8]), and max(|fl(u + v)|, |fl(u - v)|) =
+// fl(|u| + |v|) exactly: one of the two is that sum up to sign and the
+// other's magnitude, |u| - |v| rounded, is not larger (rounding to nearest
+// is monotone and odd).  NaN and infinity propagate as in the full form
+// under fmaxf.  t is left holding the stage-4 inputs.
+__device__ __forceinline__ float fwht16_absmax(float (&t)[16]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j & h) continue;
+      const float u = t[j], v = t[j + h];
+      t[j] = u + v;
+      t[j + h] = u - v;
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(t[j]) + fabsf(t[j + 8]));
+  return m;
+}
+
 // Sign flip d_j a_j for a group (bit j of `signs` set: d_j = -1).
 __device__ __forceinline__ void apply_signs(float (&t)[16], uint32_t signs) {
 #pragma unroll

@@ -50,9 +50,12 @@ __global__ __launch_bounds__(kThreads) void amax_row_kernel(
     raw.load(x + w.major * ld + w.minor * 16);
     float t[16];
     raw.template group<RHT>(0, t, signs);
-    if (RHT) fwht16(t);
+    if (RHT) {
+      m = fmaxf(m, fwht16_absmax(t));
+    } else {
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+      for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+    }
     w.advance(sq, sr, M);
   }
   m = block_max_256(m);
@@ -75,9 +78,12 @@ __global__ __launch_bounds__(kThreads) void amax_col_kernel(
     for (int k = 0; k < C; ++k) {
       float t[16];
       raw.column(k, t);
-      if (RHT) fwht16(t);
+      if (RHT) {
+        m = fmaxf(m, fwht16_absmax(t));
+      } else {
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+        for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+      }
     }
     w.advance(sq, sr, M);
   }
@@ -879,29 +885,33 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
       const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       float t[16];
       widen_bf16_group<RHT>(w, a.signs, t);
-      if (RHT) fwht16(t);
-      float amax_t = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) amax_t = fmaxf(amax_t, fabsf(t[j]));
-      if constexpr (AMAX) {
-        mr = fmaxf(mr, amax_t);
+      if constexpr (AMAX && RHT) {
+        mr = fmaxf(mr, fwht16_absmax(t));
       } else {
-        const int64_t dr = 32 * i;  // rows past the lane's pass-0 row
-        ScaleCtx c = cr;
-        if constexpr (TSM == kTsOuter) {
-          // the 8 lanes of this parity hold the row's 128-piece
-          const float ao = parity_max16(amax_t);
-          c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
-          c.den = c.s_t * grid_max<FMT>();
-          if (seg < 2) a.ts_out_r[(row0 + dr) * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
+        if (RHT) fwht16(t);
+        float amax_t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax_t = fmaxf(amax_t, fabsf(t[j]));
+        if constexpr (AMAX) {
+          mr = fmaxf(mr, amax_t);
+        } else {
+          const int64_t dr = 32 * i;  // rows past the lane's pass-0 row
+          ScaleCtx c = cr;
+          if constexpr (TSM == kTsOuter) {
+            // the 8 lanes of this parity hold the row's 128-piece
+            const float ao = parity_max16(amax_t);
+            c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+            c.den = c.s_t * grid_max<FMT>();
+            if (seg < 2) a.ts_out_r[(row0 + dr) * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
+          }
+          uint32_t pk[2];
+          uint32_t sbyte;
+          encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_r, a.sr_k0, a.sr_k1,
+                                                    nr0 + (uint64_t)dr * (uint64_t)a.cols, pk,
+                                                    sbyte);
+          store8<true>(cpr + dr * (a.cols / 2), pk[0], pk[1]);
+          spr[dr * (a.cols / 16)] = (uint8_t)sbyte;
         }
-        uint32_t pk[2];
-        uint32_t sbyte;
-        encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_r, a.sr_k0, a.sr_k1,
-                                                  nr0 + (uint64_t)dr * (uint64_t)a.cols, pk,
-                                                  sbyte);
-        store8<true>(cpr + dr * (a.cols / 2), pk[0], pk[1]);
-        spr[dr * (a.cols / 16)] = (uint8_t)sbyte;
       }
     }
     __syncthreads();
@@ -926,28 +936,32 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
       const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       float t[16];
       widen_bf16_group<RHT>(w, a.signs, t);
-      if (RHT) fwht16(t);
-      float amax_t = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) amax_t = fmaxf(amax_t, fabsf(t[e]));
-      if constexpr (AMAX) {
-        mc = fmaxf(mc, amax_t);
+      if constexpr (AMAX && RHT) {
+        mc = fmaxf(mc, fwht16_absmax(t));
       } else {
-        const int64_t da = 32 * i;  // A-rows past the lane's first
-        ScaleCtx c = cc;
-        if constexpr (TSM == kTsOuter) {
-          const float ao = group_max<8>(amax_t);
-          c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
-          c.den = c.s_t * grid_max<FMT>();
-          if (j == 0) a.ts_out_c[(ra0 + da) * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
+        if (RHT) fwht16(t);
+        float amax_t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax_t = fmaxf(amax_t, fabsf(t[e]));
+        if constexpr (AMAX) {
+          mc = fmaxf(mc, amax_t);
+        } else {
+          const int64_t da = 32 * i;  // A-rows past the lane's first
+          ScaleCtx c = cc;
+          if constexpr (TSM == kTsOuter) {
+            const float ao = group_max<8>(amax_t);
+            c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+            c.den = c.s_t * grid_max<FMT>();
+            if (j == 0) a.ts_out_c[(ra0 + da) * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
+          }
+          uint32_t pk[2];
+          uint32_t sbyte;
+          encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_c, a.sr_k0, a.sr_k1,
+                                                    nc0 + (uint64_t)da * (uint64_t)a.rows, pk,
+                                                    sbyte);
+          store8<true>(cpc + da * (a.rows / 2), pk[0], pk[1]);
+          spc[da * (a.rows / 16)] = (uint8_t)sbyte;
         }
-        uint32_t pk[2];
-        uint32_t sbyte;
-        encode_block<FMT, SR, RHT, true, 16, TSM>(t, amax_t, c, inv_c, a.sr_k0, a.sr_k1,
-                                                  nc0 + (uint64_t)da * (uint64_t)a.rows, pk,
-                                                  sbyte);
-        store8<true>(cpc + da * (a.rows / 2), pk[0], pk[1]);
-        spc[da * (a.rows / 16)] = (uint8_t)sbyte;
       }
     }
     tile = next;
