@@ -44,16 +44,6 @@ struct DequantArgs {
   uint32_t signs;
 };
 
-// BF16 bits of v, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x0040u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = (uint16_t)bf16_rne(v); }
-
 // Row-axis output staging.  A lane's unit is WORDS contiguous 32-bit words
 // of output, and consecutive lanes hold consecutive units; writing them
 // straight out would make every store instruction touch 64 separate
@@ -88,23 +78,41 @@ struct RowStage {
   }
 };
 
-template <typename T>
-__device__ __forceinline__ void pack_out(const float* t, uint32_t* w, int n);
-template <>
-__device__ __forceinline__ void pack_out<float>(const float* t, uint32_t* w, int n) {
+__device__ __forceinline__ void pack_f32(const float* t, uint32_t* w, int n) {
   for (int j = 0; j < n; ++j) w[j] = __float_as_uint(t[j]);
 }
-template <>
-__device__ __forceinline__ void pack_out<uint16_t>(const float* t, uint32_t* w, int n) {
-  for (int j = 0; j < n / 2; ++j) w[j] = bf16_rne(t[2 * j]) | (bf16_rne(t[2 * j + 1]) << 16);
+
+// sign * L[k] of the two E2M1 codes in byte `sel` of w (low nibble first),
+// exactly: the hardware pair convert with scale 1.0.
+typedef float f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f2 e2m1_pair(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
 }
 
-// Values of block (ra, b): sign * L[k] * d, optionally through the inverse
-// RHT; t holds B values.
-template <int FMT, bool OUTER, bool INV>
+// Output words of block (ra, b): sign * L[k] * d (one binary32 product),
+// optionally through the inverse RHT a = D (1/4) H16 y, packed as T (two
+// BF16 values per word, or one FP32 value).  B * sizeof(T) / 4 words.
+//
+// E2M1 codes decode in hardware: the FP4 -> FP32 pair convert with scale
+// 1.0 gives sign * L[k] exactly (-0 for code 8), and (sign * L) * d equals
+// sign * (L * d) in IEEE arithmetic.  BF16 packing uses the packed RNE
+// convert (same bits as round-to-nearest-even, NaN kept quiet).  With the
+// inverse RHT the 1/4 moves into d when 2^-100 <= d <= 2^100: then every
+// y = L * d/4 is exactly y/4 rounded as y was, every butterfly sum is a
+// multiple of 2^-126 (no bits lost to the subnormal range) and no sum nears
+// overflow, so the butterfly of y/4 is the butterfly of y times 1/4 exactly;
+// other blocks multiply by 1/4 after the butterfly, as written.  The D sign
+// flips act on the packed words (negation commutes with rounding).
+template <int FMT, bool OUTER, bool INV, typename T>
 __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t, int64_t ra,
-                                              int64_t b, float* t) {
+                                              int64_t b, uint32_t* out) {
   constexpr int B = block_of<FMT>();
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   const uint32_t S = a.scales[ra * (a.W / B) + b];
   float d;
   if constexpr (is_mx(FMT)) {
@@ -123,18 +131,46 @@ __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t, i
     const uint4 v = *reinterpret_cast<const uint4*>(cp);
     words[0] = v.x; words[1] = v.y; words[2] = v.z; words[3] = v.w;
   }
+  const bool fold = INV && d >= 0x1p-100f && d <= 0x1p100f;
+  const float dm = fold ? d * 0.25f : d;
 #pragma unroll
   for (int h = 0; h < B / 16; ++h) {
     float g[16];
+    if constexpr (FMT == kUFP4) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
-      const float mag = grid_level<FMT>(c & 7u) * d;
-      g[j] = (c & 8u) ? -mag : mag;
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
+        const float mag = (float)(c & 7u) * dm;
+        g[j] = (c & 8u) ? -mag : mag;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // byte k of the group: elements 2k, 2k + 1
+        const f2 l = e2m1_pair(words[2 * h + (k >> 2)], k & 3);
+        g[2 * k] = l.x * dm;
+        g[2 * k + 1] = l.y * dm;
+      }
     }
-    if (INV) rht16_inverse(g, a.signs);
+    if constexpr (INV) {
+      fwht16(g);
+      if (!fold) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t[16 * h + j] = g[j];
+        for (int j = 0; j < 16; ++j) g[j] = g[j] * 0.25f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t m = INV ? pair_sign_mask(a.signs, k) : 0u;  // bits 15 and 31
+      if constexpr (sizeof(T) == 2) {
+        f2 v;
+        v.x = g[2 * k];
+        v.y = g[2 * k + 1];
+        out[8 * h + k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2)) ^ m;
+      } else {
+        out[16 * h + 2 * k] = __float_as_uint(g[2 * k]) ^ (m << 16);
+        out[16 * h + 2 * k + 1] = __float_as_uint(g[2 * k + 1]) ^ (m & 0x80000000u);
+      }
+    }
   }
 }
 
@@ -148,10 +184,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
     // BF16 rows: 2 bytes per value, a lane's 16-value group is two 16-byte
     // stores (staging measured slower here)
     while (w.major < a.n_major) {
-      float t[B];
-      dequant_block<FMT, OUTER, INV>(a, s_t, w.major, w.minor, t);
       uint32_t v[B / 2];
-      pack_out<T>(t, v, B);
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, w.major, w.minor, v);
       uint32_t* to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
 #pragma unroll
       for (int q = 0; q < B / 8; ++q) store16<false>(to + 4 * q, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
@@ -171,9 +205,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
       uint32_t v[WORDS];
       uint32_t* to = nullptr;
       if (w.major < a.n_major) {
-        float t[B];
-        dequant_block<FMT, OUTER, INV>(a, s_t, w.major, w.minor, t);
-        pack_out<T>(t, v, B);
+        dequant_block<FMT, OUTER, INV, T>(a, s_t, w.major, w.minor, v);
         to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
       } else {
 #pragma unroll
@@ -188,10 +220,15 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
   } else {
     while (w.major < a.n_major) {
       const int64_t ra = w.minor, b = w.major;
-      float t[B];
-      dequant_block<FMT, OUTER, INV>(a, s_t, ra, b, t);
+      constexpr int WORDS = B * (int)sizeof(T) / 4;
+      uint32_t v[WORDS];
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, ra, b, v);
 #pragma unroll
-      for (int j = 0; j < B; ++j) store_elem(out + (b * B + j) * a.ld_out + ra, t[j]);
+      for (int j = 0; j < B; ++j) {
+        T* p = out + (b * B + j) * a.ld_out + ra;
+        if constexpr (sizeof(T) == 2) *p = (T)(v[j / 2] >> (16 * (j & 1)));
+        else *p = __uint_as_float(v[j]);
+      }
       w.advance(a.sq, a.sr, a.M);
     }
   }
@@ -220,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void rht_kernel(const T* __restrict__ x, 
         load_group<0>(x, ld, w.major, w.minor * 16, t);
         if (INV) rht16_inverse(t, signs);
         else rht16_forward(t, signs);
-        pack_out<float>(t, v, 16);
+        pack_f32(t, v, 16);
         to = reinterpret_cast<uint32_t*>(y + w.major * cols + w.minor * 16);
       } else {
 #pragma unroll

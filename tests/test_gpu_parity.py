@@ -206,3 +206,48 @@ def test_error_statuses_through_binding():
     with pytest.raises(fp4.FP4Error) as e:
         fp4.quantize(x, "mxfp4")  # 48 % 32
     assert e.value.status == -3
+
+
+def _same_or_both_nan(got, want, bits, tag):
+    """Byte parity, except that NaN payloads may differ: positions must agree."""
+    if bits == 32:
+        g, w = got.view(np.uint32), want.view(np.uint32)
+        gn = ((g & 0x7F800000) == 0x7F800000) & ((g & 0x007FFFFF) != 0)
+        wn = ((w & 0x7F800000) == 0x7F800000) & ((w & 0x007FFFFF) != 0)
+    else:
+        g, w = got.view(np.uint16), want.view(np.uint16)
+        gn = ((g & 0x7F80) == 0x7F80) & ((g & 0x007F) != 0)
+        wn = ((w & 0x7F80) == 0x7F80) & ((w & 0x007F) != 0)
+    assert np.array_equal(gn, wn), "NaN positions " + tag
+    assert np.array_equal(g[~gn], w[~wn]), "values " + tag
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4"])
+def test_dequant_arbitrary_codes_and_scales(fmt):
+    """Dequantize of random codes with every scale byte and tensor scales
+    far from 1: decoded block scales below 2^-100, above 2^100 and infinite
+    take the path that applies the inverse RHT's 1/4 after the butterfly,
+    moderate ones fold it into d.  Against the oracle, both axes and
+    output types."""
+    rows, cols = 256, 384
+    rng = np.random.default_rng(21)
+    for axis in ("row", "col"):
+        cshape, sshape = fp4.output_shapes(rows, cols, fmt, axis)
+        codes = rng.integers(0, 256, cshape, dtype=np.uint8)
+        hi = 255 if fmt in fp4.MX else 127
+        scales = rng.integers(0, hi, sshape, dtype=np.uint8)
+        tss = (None,) if fmt in fp4.MX else (2.0 ** -20, 0.37, 1e4, 1e-35, 1e-39, 1e30, 1e38)
+        for ts in tss:
+            for inv in (False, True):
+                for odt, name, bits in ((torch.float32, "f32", 32), (torch.bfloat16, "bf16", 16)):
+                    note("dequant codes %s %s ts=%s inv=%s %s" % (fmt, axis, ts, inv, name))
+                    tsd = None if ts is None else torch.tensor([ts], dtype=torch.float32,
+                                                               device=DEV)
+                    out = fp4.dequantize(to_device(codes), to_device(scales), tsd, rows, cols,
+                                         fmt, axis, True, 2, inv, odt)
+                    torch.cuda.synchronize()
+                    want = oracle.dequantize(codes, scales,
+                                             None if ts is None else np.float32(ts), rows,
+                                             cols, fmt, axis, True, 2, inv, name)
+                    _same_or_both_nan(to_host(out), want, bits, "%s %s ts=%s inv=%s %s" % (
+                        fmt, axis, ts, inv, name))
