@@ -42,6 +42,7 @@ struct DequantArgs {
   int64_t ld_out, W;
   int64_t n_major, M, sq, sr;
   uint32_t signs;
+  int64_t blk0, col0;  // column axis: first block down the rows, first column
 };
 
 // Row-axis output staging.  A lane's unit is WORDS contiguous 32-bit words
@@ -108,29 +109,48 @@ __device__ __forceinline__ f2 e2m1_pair(uint32_t w, int sel) {
 // overflow, so the butterfly of y/4 is the butterfly of y times 1/4 exactly;
 // other blocks multiply by 1/4 after the butterfly, as written.  The D sign
 // flips act on the packed words (negation commutes with rounding).
+// The inputs of block (ra, b): its scale byte, its outer scale (double
+// block) and its code words.  Loaded one block ahead of the decode so the
+// loads fly while the previous block is decoded and stored.
+template <int FMT, bool OUTER>
+struct BlockIn {
+  uint32_t S;
+  float so;
+  uint32_t words[block_of<FMT>() / 8];
+};
+
+template <int FMT, bool OUTER>
+__device__ __forceinline__ BlockIn<FMT, OUTER> load_block(const DequantArgs& a, int64_t ra,
+                                                          int64_t b) {
+  constexpr int B = block_of<FMT>();
+  BlockIn<FMT, OUTER> in;
+  in.S = a.scales[ra * (a.W / B) + b];
+  // outer scales: the 128-piece of the A-row that holds block b
+  in.so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : 0.0f;
+  const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
+  if constexpr (B == 16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(cp);
+    in.words[0] = v.x; in.words[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(cp);
+    in.words[0] = v.x; in.words[1] = v.y; in.words[2] = v.z; in.words[3] = v.w;
+  }
+  return in;
+}
+
 template <int FMT, bool OUTER, bool INV, typename T>
-__device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t, int64_t ra,
-                                              int64_t b, uint32_t* out) {
+__device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t,
+                                              const BlockIn<FMT, OUTER>& in, uint32_t* out) {
   constexpr int B = block_of<FMT>();
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  const uint32_t S = a.scales[ra * (a.W / B) + b];
+  const uint32_t S = in.S;
   float d;
   if constexpr (is_mx(FMT)) {
     d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
   } else {
-    // outer scales: the 128-piece of the A-row that holds block b
-    const float so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : s_t;
-    d = S ? so * e4m3_decode(S) : 0.0f;
+    d = S ? (OUTER ? in.so : s_t) * e4m3_decode(S) : 0.0f;
   }
-  const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
-  uint32_t words[B / 8];
-  if constexpr (B == 16) {
-    const uint2 v = *reinterpret_cast<const uint2*>(cp);
-    words[0] = v.x; words[1] = v.y;
-  } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(cp);
-    words[0] = v.x; words[1] = v.y; words[2] = v.z; words[3] = v.w;
-  }
+  const uint32_t (&words)[B / 8] = in.words;
   const bool fold = INV && d >= 0x1p-100f && d <= 0x1p100f;
   const float dm = fold ? d * 0.25f : d;
 #pragma unroll
@@ -183,12 +203,15 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
   if constexpr (AXIS == 0 && sizeof(T) == 2) {
     // BF16 rows: 2 bytes per value, a lane's 16-value group is two 16-byte
     // stores (staging measured slower here)
+    // (loading the next block ahead measured slower here)
     while (w.major < a.n_major) {
       uint32_t v[B / 2];
-      dequant_block<FMT, OUTER, INV, T>(a, s_t, w.major, w.minor, v);
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, load_block<FMT, OUTER>(a, w.major, w.minor),
+                                        v);
       uint32_t* to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
 #pragma unroll
-      for (int q = 0; q < B / 8; ++q) store16<false>(to + 4 * q, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      for (int q = 0; q < B / 8; ++q)
+        store16<false>(to + 4 * q, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       w.advance(a.sq, a.sr, a.M);
     }
   } else if constexpr (AXIS == 0) {
@@ -200,12 +223,20 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
     __shared__ uint32_t* sdst[kThreads];
     const Stage st{sbuf, sdst};
     const int64_t units = a.n_major * a.M;
+    bool have = w.major < a.n_major;
+    BlockIn<FMT, OUTER> cur{};
+    if (have) cur = load_block<FMT, OUTER>(a, w.major, w.minor);
     for (int64_t base = (int64_t)blockIdx.x * kThreads; base < units;
          base += (int64_t)gridDim.x * kThreads) {
+      Walk nw = w;
+      nw.advance(a.sq, a.sr, a.M);
+      const bool have_next = nw.major < a.n_major;
+      BlockIn<FMT, OUTER> nxt{};
+      if (have_next) nxt = load_block<FMT, OUTER>(a, nw.major, nw.minor);
       uint32_t v[WORDS];
       uint32_t* to = nullptr;
-      if (w.major < a.n_major) {
-        dequant_block<FMT, OUTER, INV, T>(a, s_t, w.major, w.minor, v);
+      if (have) {
+        dequant_block<FMT, OUTER, INV, T>(a, s_t, cur, v);
         to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + w.minor * B);
       } else {
 #pragma unroll
@@ -215,22 +246,120 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
       __syncthreads();
       st.flush();
       __syncthreads();
-      w.advance(a.sq, a.sr, a.M);
+      cur = nxt;
+      w = nw;
+      have = have_next;
     }
   } else {
-    while (w.major < a.n_major) {
-      const int64_t ra = w.minor, b = w.major;
+    // edge strips of the tiled interior: units (block, column), column
+    // fastest, offset by (blk0, col0)
+    bool have = w.major < a.n_major;
+    BlockIn<FMT, OUTER> cur{};
+    if (have) cur = load_block<FMT, OUTER>(a, a.col0 + w.minor, a.blk0 + w.major);
+    while (have) {
+      Walk nw = w;
+      nw.advance(a.sq, a.sr, a.M);
+      const bool have_next = nw.major < a.n_major;
+      BlockIn<FMT, OUTER> nxt{};
+      if (have_next) nxt = load_block<FMT, OUTER>(a, a.col0 + nw.minor, a.blk0 + nw.major);
+      const int64_t ra = a.col0 + w.minor, b = a.blk0 + w.major;
       constexpr int WORDS = B * (int)sizeof(T) / 4;
       uint32_t v[WORDS];
-      dequant_block<FMT, OUTER, INV, T>(a, s_t, ra, b, v);
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, cur, v);
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         T* p = out + (b * B + j) * a.ld_out + ra;
         if constexpr (sizeof(T) == 2) *p = (T)(v[j / 2] >> (16 * (j & 1)));
         else *p = __uint_as_float(v[j]);
       }
-      w.advance(a.sq, a.sr, a.M);
+      cur = nxt;
+      w = nw;
+      have = have_next;
     }
+  }
+}
+
+// Column axis, interior tiles (the mirror of the quantize column tiles):
+// each lane decodes whole blocks of A-rows (columns of x) into LDS in the
+// tile's transposed layout, then the workgroup writes the tile out by rows,
+// 16 bytes per lane with 8 lanes on one 128-byte row segment.
+template <int FMT, bool OUTER, bool INV, typename T>
+__global__ __launch_bounds__(kThreads) void dequantize_col_tile_kernel(T* __restrict__ out,
+                                                                       DequantArgs a,
+                                                                       int64_t n_rt,
+                                                                       int64_t n_ct) {
+  using Tile = ColTile<T>;
+  constexpr int B = block_of<FMT>();
+  constexpr int TR = Tile::TR, TC = Tile::TC;
+  constexpr int kStores = TR * TC * (int)sizeof(T) / 16 / kThreads;  // 16-byte stores per lane
+  constexpr int kUnits = TC * (TR / B) / kThreads;                   // blocks per lane
+  constexpr int LPR = TR / B;                // lanes per A-row of a tile
+  constexpr int kRowStep = kThreads / LPR;   // A-rows between a lane's units
+  constexpr int WORDS = B * (int)sizeof(T) / 4;
+  __shared__ __align__(16) uint32_t lds[Tile::kWords];
+  const float s_t = (is_mx(FMT) || OUTER) ? 0.0f : a.ts[0];
+  const int64_t ntile = n_rt * n_ct;
+  const int lane_ra = threadIdx.x / LPR, j = threadIdx.x % LPR;
+  const int seg = threadIdx.x & 7;
+  // (row tile, column tile) walk with a grid stride, no division in the loop
+  const int64_t step_r = gridDim.x / n_ct, step_c = gridDim.x - step_r * n_ct;
+  int64_t tr = blockIdx.x / n_ct, tc = blockIdx.x - tr * n_ct;
+  for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+    const int64_t r0 = tr * TR, c0 = tc * TC;
+    BlockIn<FMT, OUTER> in[kUnits];
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i)
+      in[i] = load_block<FMT, OUTER>(a, c0 + lane_ra + kRowStep * i, r0 / B + j);
+    __syncthreads();  // the previous tile's rows are read out
+    // ---- decode unit i (A-row lane_ra + kRowStep * i, block j) into LDS
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int cl = lane_ra + kRowStep * i;
+      uint32_t v[WORDS];
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, in[i], v);
+      if constexpr (sizeof(T) == 2) {
+        // row pairs j*B/2 .. : whole aligned 4-word groups
+#pragma unroll
+        for (int q = 0; q < WORDS / 4; ++q)
+          *reinterpret_cast<uint4*>(lds + Tile::at(cl, j * B / 2 + 4 * q)) =
+              make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < B; ++e) lds[Tile::at(cl, j * B + e)] = v[e];
+      }
+    }
+    __syncthreads();
+    // ---- rows out: 16-byte pieces, 8 lanes per row segment
+    T* base = out + r0 * a.ld_out + c0;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < kStores / 2; ++i) {
+        const int pr = (threadIdx.x >> 3) + 32 * i;  // row pair
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int col = seg * 8 + 2 * k;
+          const uint32_t w0 = lds[Tile::at(col, pr)], w1 = lds[Tile::at(col + 1, pr)];
+          ev[k] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // row 2pr, columns col, col+1
+          od[k] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // row 2pr + 1
+        }
+        T* p = base + (int64_t)(2 * pr) * a.ld_out + seg * 8;
+        store16<false>(p, ev[0], ev[1], ev[2], ev[3]);
+        store16<false>(p + a.ld_out, od[0], od[1], od[2], od[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kStores; ++i) {
+        const int row = (threadIdx.x >> 3) + 32 * i;
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = lds[Tile::at(seg * 4 + k, row)];
+        store16<false>(base + (int64_t)row * a.ld_out + seg * 4, v[0], v[1], v[2], v[3]);
+      }
+    }
+    tr += step_r;
+    tc += step_c;
+    if (tc >= n_ct) { tc -= n_ct; tr += 1; }
   }
 }
 
@@ -299,17 +428,51 @@ inline WalkPlan plan_walk(int64_t n_major, int64_t M, int64_t cap) {
   return {(unsigned)g, stride / M, stride % M};
 }
 
+constexpr int64_t kTileGrid = 4096;  // workgroups of the column tiles (cap)
+
 template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 hipError_t launch_dequant_t(const DequantLaunch& q, hipStream_t s) {
   constexpr int B = block_of<FMT>();
-  const int64_t W = AXIS == 0 ? q.cols : q.rows;
-  const int64_t RA = AXIS == 0 ? q.rows : q.cols;
-  const int64_t nmaj = AXIS == 0 ? RA : W / B;
-  const int64_t M = AXIS == 0 ? W / B : RA;
-  const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
-  DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, nmaj, M, wp.sq, wp.sr, q.signs};
-  hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, AXIS, T>), dim3(wp.grid),
-                     dim3(kThreads), 0, s, static_cast<T*>(q.out), a);
+  T* out = static_cast<T*>(q.out);
+  if (AXIS == 0) {
+    const int64_t W = q.cols, nmaj = q.rows, M = W / B;
+    const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
+    DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, nmaj, M, wp.sq, wp.sr,
+                  q.signs, 0, 0};
+    hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, 0, T>), dim3(wp.grid),
+                       dim3(kThreads), 0, s, out, a);
+    return hipGetLastError();
+  }
+  // column axis: whole tiles through LDS (16-byte row stores), the right and
+  // bottom strips per element
+  using Tile = ColTile<T>;
+  const int64_t W = q.rows;
+  const bool tiles = (q.ld_out * (int64_t)sizeof(T)) % 16 == 0;
+  const int64_t nrt = tiles ? q.rows / Tile::TR : 0, nct = tiles ? q.cols / Tile::TC : 0;
+  const int64_t rows_main = nct > 0 ? nrt * Tile::TR : 0;
+  const int64_t cols_main = nrt > 0 ? nct * Tile::TC : 0;
+  DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, 0, 0, 0, 0, q.signs, 0, 0};
+  if (rows_main > 0 && cols_main > 0) {
+    const int64_t ntile = nrt * nct;
+    hipLaunchKernelGGL((dequantize_col_tile_kernel<FMT, OUTER, INV, T>),
+                       dim3((unsigned)(ntile < kTileGrid ? ntile : kTileGrid)), dim3(kThreads),
+                       0, s, out, a, nrt, nct);
+  }
+  auto strip = [&](int64_t blk_begin, int64_t blk_end, int64_t col_begin, int64_t col_end) {
+    if (blk_end <= blk_begin || col_end <= col_begin) return;
+    DequantArgs e = a;
+    e.blk0 = blk_begin;
+    e.col0 = col_begin;
+    e.n_major = blk_end - blk_begin;
+    e.M = col_end - col_begin;
+    const WalkPlan wp = plan_walk(e.n_major, e.M, kMaxGrid);
+    e.sq = wp.sq;
+    e.sr = wp.sr;
+    hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, 1, T>), dim3(wp.grid),
+                       dim3(kThreads), 0, s, out, e);
+  };
+  strip(0, rows_main / B, cols_main, q.cols);    // right of the tiles
+  strip(rows_main / B, W / B, 0, q.cols);        // below them
   return hipGetLastError();
 }
 template <int FMT, bool OUTER, bool INV, int AXIS>

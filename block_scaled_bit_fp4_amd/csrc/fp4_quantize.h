@@ -572,28 +572,6 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
 // each lane then codes whole blocks of one A-row, and the lanes of one A-row
 // write its TR/2 code bytes as one contiguous run.  A workgroup walks tiles
 // with a grid stride and loads its next tile while coding the current one.
-template <typename T>
-struct ColTile {
-  static constexpr int TR = 256;                        // rows per tile
-  static constexpr int TC = 128 / (int)sizeof(T);       // columns per tile
-  static constexpr int EPW = 4 / (int)sizeof(T);        // elements per LDS word
-  // Words per A-row.  BF16: 128 words (row pairs) plus 4 of padding, so
-  // every A-row starts 16-byte aligned and a block reads as 128-bit words;
-  // FP32: an odd pitch.
-  static constexpr int P = sizeof(T) == 2 ? TR / 2 + 4 : TR + 1;
-  static constexpr int kWords = TC * P;
-  // LDS word of (A-row col, position pr).  BF16 positions are XOR-swizzled
-  // in 4-word units, by bits 3-5 of col (the transposing stores of one
-  // instruction then reach 32 distinct banks per half wave) and by bit 5 of
-  // pr (the eight 128-bit reads of lanes on consecutive blocks then reach
-  // distinct 4-bank groups); aligned 4-word groups stay whole.
-  __device__ static __forceinline__ int at(int col, int pr) {
-    if constexpr (sizeof(T) == 2)
-      return col * P + (pr ^ (((col >> 3) & 7) << 2) ^ (((pr >> 5) & 1) << 2));
-    else
-      return col * P + pr;
-  }
-};
 
 template <int FMT, bool SR, bool RHT, int TSM, typename T>
 __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T* __restrict__ x,

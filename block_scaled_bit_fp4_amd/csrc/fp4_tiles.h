@@ -132,4 +132,32 @@ struct Walk {
   }
 };
 
+// Column-axis tiles of TR x-rows by TC x-columns (TC * sizeof(T) = 128
+// bytes), held in LDS transposed: A-row-major (an A-row is a column of x),
+// packed row pairs for BF16.  The quantize tiles write this layout from
+// row loads and read whole blocks from it; the dequantize tiles write
+// whole blocks into it and read it back as rows.
+template <typename T>
+struct ColTile {
+  static constexpr int TR = 256;                        // rows per tile
+  static constexpr int TC = 128 / (int)sizeof(T);       // columns per tile
+  static constexpr int EPW = 4 / (int)sizeof(T);        // elements per LDS word
+  // Words per A-row.  BF16: 128 words (row pairs) plus 4 of padding, so
+  // every A-row starts 16-byte aligned and a block reads as 128-bit words;
+  // FP32: an odd pitch.
+  static constexpr int P = sizeof(T) == 2 ? TR / 2 + 4 : TR + 1;
+  static constexpr int kWords = TC * P;
+  // LDS word of (A-row col, position pr).  BF16 positions are XOR-swizzled
+  // in 4-word units, by bits 3-5 of col (the transposing stores of one
+  // instruction then reach 32 distinct banks per half wave) and by bit 5 of
+  // pr (the eight 128-bit reads of lanes on consecutive blocks then reach
+  // distinct 4-bank groups); aligned 4-word groups stay whole.
+  __device__ static __forceinline__ int at(int col, int pr) {
+    if constexpr (sizeof(T) == 2)
+      return col * P + (pr ^ (((col >> 3) & 7) << 2) ^ (((pr >> 5) & 1) << 2));
+    else
+      return col * P + pr;
+  }
+};
+
 }  // namespace fp4dev
