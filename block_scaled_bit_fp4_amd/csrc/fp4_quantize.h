@@ -351,16 +351,22 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
   RowRaw<T, U> cur;
+  // After a tensor-amax pass the rows are taken last to first: the end of
+  // the input, read last by that pass, is then still in the memory-side
+  // cache when this pass starts.
+  constexpr bool kRev = TSM == kTsCompute && !is_mx(FMT);
+  auto row_of = [&](int64_t m) { return kRev ? a.n_major - 1 - m : m; };
   bool have = w.major < a.n_major;
   const ScaleFetch sf = scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in);
-  if (have) cur.load(x + w.major * a.ld + w.minor * U);  // in flight during the prologue
+  if (have) cur.load(x + row_of(w.major) * a.ld + w.minor * U);  // in flight during the prologue
   const ScaleCtx c = scale_prologue<FMT, TSM>(sf, a.ts_out, inv_tab);
   while (have) {
     Walk nw = w;
     nw.advance(a.sq, a.sr, a.M);
     const bool have_next = nw.major < a.n_major;
     RowRaw<T, U> nxt;
-    if (have_next) nxt.load(x + nw.major * a.ld + nw.minor * U);
+    if (have_next) nxt.load(x + row_of(nw.major) * a.ld + nw.minor * U);
+    const int64_t row = row_of(w.major);
 
     uint32_t packed[U / 8];
     uint32_t sb[NBU];
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
       }
     };
     auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
-      const uint64_t n0 = (uint64_t)w.major * (uint64_t)a.W + (uint64_t)(w.minor * U + bi * B);
+      const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(w.minor * U + bi * B);
       uint32_t pk[B / 8];
       encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
                                                          a.sr_k1, n0, pk, sb[bi]);
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
       ScaleCtx co;
       co.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
       co.den = co.s_t * grid_max<FMT>();
-      if (w.minor % LPO == 0) a.ts_out[w.major * (a.W / kOuter) + w.minor / LPO] = co.s_t;
+      if (w.minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + w.minor / LPO] = co.s_t;
 #pragma unroll
       for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
     } else {
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
         code(bi, t, amax_t, c);
       }
     }
-    uint8_t* cp = a.codes + w.major * (a.W / 2) + w.minor * (U / 2);
+    uint8_t* cp = a.codes + row * (a.W / 2) + w.minor * (U / 2);
     if constexpr (U >= 32) {
 #pragma unroll
       for (int i = 0; i < U / 32; ++i)
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
     } else {
       store8<true>(cp, packed[0], packed[1]);
     }
-    uint8_t* sp = a.scales + w.major * (a.W / B) + w.minor * NBU;
+    uint8_t* sp = a.scales + row * (a.W / B) + w.minor * NBU;
     if constexpr (NBU == 4)
       *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
     else if constexpr (NBU == 2)
@@ -595,8 +601,12 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   const int seg = threadIdx.x & 7;
   const uint32_t lane_off = (uint32_t)(((sizeof(T) == 2 ? 2 : 1) * (threadIdx.x >> 3)) * a.ld +
                                        seg * (16 / (int)sizeof(T))) * (uint32_t)sizeof(T);
+  // After a tensor-amax pass the row tiles are taken last to first (the end
+  // of the input, read last by that pass, is still in the memory-side cache)
+  constexpr bool kRev = TSM == kTsCompute && !is_mx(FMT);
+  auto rt = [&](int64_t t) { return kRev ? a.n_major - 1 - t : t; };
   auto load_tile = [&](int64_t tr, int64_t tc, uint4 (&buf)[kLoads]) {
-    const char* base = reinterpret_cast<const char*>(x + tr * TR * a.ld + tc * TC);
+    const char* base = reinterpret_cast<const char*>(x + rt(tr) * TR * a.ld + tc * TC);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int row_i = sizeof(T) == 2 ? 64 * (i % (kLoads / 2)) + (i >= kLoads / 2 ? 1 : 0)
@@ -618,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
   // a lane's units: A-rows lane_ra + kRowStep * i of the tile, block j
   const int lane_ra = threadIdx.x / LPR, j = threadIdx.x % LPR;
   while (have) {
-    const int64_t r0 = tr * TR, c0 = tc * TC;
+    const int64_t r0 = rt(tr) * TR, c0 = tc * TC;
     __syncthreads();  // previous tile's LDS reads are done
     // ---- registers -> LDS, transposed
     if constexpr (sizeof(T) == 2) {
@@ -802,8 +812,14 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
   // a wave-uniform base per load plus one per-lane 32-bit offset (the
   // launcher keeps a tile's byte extent below 2^31)
   const uint32_t lane_off = (uint32_t)(2 * q * a.ld + seg * 8) * 2u;
+  // After the tensor-amax pass the row tiles are taken last to first (the
+  // end of the input, read last by that pass, is still in the memory-side
+  // cache)
+  constexpr bool kRev = TSM == kTsCompute && !AMAX;
+  const int64_t n_rt = a.rows / kDT;
+  auto rt = [&](int64_t t) { return kRev ? n_rt - 1 - t : t; };
   auto load_tile = [&](int64_t tr, int64_t tc, uint4 (&buf)[kLoads]) {
-    const char* base = reinterpret_cast<const char*>(x + tr * kDT * a.ld + tc * kDT);
+    const char* base = reinterpret_cast<const char*>(x + rt(tr) * kDT * a.ld + tc * kDT);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int row_i = 32 * (i & 3) + (i >> 2);
@@ -827,7 +843,7 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
   if constexpr (!AMAX) dual_prologue<FMT, TSM>(a, fr, fc, inv_r, inv_c, cr, cc);
   float mr = 0.0f, mc = 0.0f;  // AMAX: running maxima of the two axes
   while (have) {
-    const int64_t r0 = tr * kDT, c0 = tc * kDT;
+    const int64_t r0 = rt(tr) * kDT, c0 = tc * kDT;
     __syncthreads();  // previous tile's LDS reads are done
     // ---- registers -> LDS, transposed, for the column part
 #pragma unroll
