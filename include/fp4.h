@@ -152,7 +152,8 @@ size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p)
  * (TetraJet-v2 page, Riepilogo Tecnico 2.A: the 1x16 groups realigned for
  * the transposed matrix; the [UFP4] page, Metodologia 2: quantized
  * operands of all three GEMMs).  With BF16 input, the NVFP4 or uniform
- * grid format and rows and cols multiples of 128, x is read once per pass
+ * grid format, rows and cols multiples of 128 and 256 * ld < 2^31 (a
+ * 128-row tile's byte extent), x is read once per pass
  * (once in all with a given tensor scale or outer scales, twice with
  * computed tensor scales instead of four times); otherwise the call runs
  * the two single-axis quantizations in turn.  ts_row / ts_col follow the
