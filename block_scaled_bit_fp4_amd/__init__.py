@@ -42,7 +42,8 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_NULL", -2: "FP4_ERR_FORMAT", -3: "FP4_ERR_SH
 
 # every symbol include/fp4.h declares
 EXPORTS = ("fp4_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_rht",
-           "fp4_rht_signs", "fp4_status_str", "fp4_workspace_bytes_dual", "fp4_quantize_dual")
+           "fp4_rht_signs", "fp4_status_str", "fp4_workspace_bytes_dual", "fp4_quantize_dual",
+           "fp4_gemm_mx")
 
 
 class FP4Error(RuntimeError):
@@ -90,6 +91,8 @@ def load():
         L.fp4_dequantize.restype = i32
         L.fp4_rht.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_uint64, i32, vp, vp]
         L.fp4_rht.restype = i32
+        L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+        L.fp4_gemm_mx.restype = i32
         L.fp4_rht_signs.argtypes = [ctypes.c_uint64]
         L.fp4_rht_signs.restype = ctypes.c_uint16
         L.fp4_status_str.argtypes = [i32]
@@ -264,6 +267,29 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: in
                                DTYPES[out.dtype], out.stride(0), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_dequantize")
+    return out
+
+
+def gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor,
+            b_scales: torch.Tensor, out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """C = A · Bᵀ of two MXFP4 operands quantized along K (``quantize(...,
+    "mxfp4", "row")`` outputs: codes [rows, K/2], scales [rows, K/32]).
+    Returns the M x N float32 or bfloat16 product."""
+    M, kh = a_codes.shape
+    N, kh2 = b_codes.shape
+    if kh != kh2:
+        raise ValueError("A and B must have the same K")
+    K = 2 * kh
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out.dtype not in DTYPES:
+        raise TypeError("out must be bfloat16 or float32")
+    st = load().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
+                            b_scales.data_ptr(), M, N, K, out.data_ptr(), DTYPES[out.dtype],
+                            out.stride(0), _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_gemm_mx")
     return out
 
 

@@ -276,6 +276,32 @@ fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, 
   return finish(fp4_launch_rht(q, s), s);
 }
 
+fp4_status fp4_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                       int64_t K, void* c, int32_t c_dtype, int64_t ldc, void* stream) {
+  if (c_dtype != FP4_BF16 && c_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return FP4_ERR_SHAPE;
+  if (M % 128 || N % 128 || K % 128 || K == 0) return FP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c)) return FP4_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(a_scales) | reinterpret_cast<uintptr_t>(b_scales)) % 4)
+    return FP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmLaunch q{};
+  q.a_codes = a_codes;
+  q.a_scales = a_scales;
+  q.b_codes = b_codes;
+  q.b_scales = b_scales;
+  q.M = M;
+  q.N = N;
+  q.K = K;
+  q.c = c;
+  q.c_dtype = c_dtype;
+  q.ldc = ldc;
+  return finish(fp4_launch_gemm_mx(q, s), s);
+}
+
 }  // extern "C"
 
 hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {

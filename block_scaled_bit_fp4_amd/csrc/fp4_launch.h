@@ -63,6 +63,18 @@ struct RhtLaunch {
   float* y;
 };
 
+// C = A · Bᵀ of MXFP4 operands quantized along K (M, N, K multiples of 128).
+struct GemmLaunch {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int64_t M, N, K;
+  void* c;
+  int c_dtype;  // 0 bf16, 1 f32
+  int64_t ldc;
+};
+
 hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s);
 // per-format instantiations (fp4_quantize_<format>.hip)
 hipError_t fp4_launch_quantize_nvfp4(const QuantLaunch& q, hipStream_t s);
@@ -73,4 +85,5 @@ hipError_t fp4_launch_quantize_dual_nvfp4(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_dual_ufp4(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s);
+hipError_t fp4_launch_gemm_mx(const GemmLaunch& q, hipStream_t s);
 hipError_t fp4_launch_write_scalar(float* p, float v, hipStream_t s);

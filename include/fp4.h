@@ -183,6 +183,26 @@ fp4_status fp4_dequantize(const uint8_t* codes, const uint8_t* scales,
 fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, int64_t ld,
                    int32_t axis, uint64_t rht_seed, int32_t inverse, float* y, void* stream);
 
+/* C = A * B^T for MXFP4 (or MXFP4-OAS) operands quantized along K: A is
+ * M x K, B is N x K, each as fp4_quantize writes it with axis FP4_AXIS_ROW
+ * (codes [rows][K/2], element 2j in the low nibble of byte j; E8M0 scales
+ * [rows][K/32]).  The GEMM consumer of the quantized operands, for the
+ * single-GEMM output quality the [UFP4] page measures per path
+ * ("Diagnosticos de Cuantizacion y GEMM") and the quantize overhead
+ * relative to the GEMM the [MXFP4] page reports ("4. Resultats
+ * Experimentaux").  An RHT applied to both operands along K cancels in the
+ * product (the 16-point transform is orthogonal).  Each product of two
+ * codes is exact; accumulation is in binary32 inside gfx950's scaled
+ * matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4), in its order, so
+ * results match an exact reference within a binary32 accumulation bound,
+ * not bit for bit.  C is M x N, FP32 or BF16 (round to nearest even), row
+ * leading dimension ldc >= N.  M, N and K must be multiples of 128 and
+ * K > 0 (else FP4_ERR_SHAPE); codes and C 16-byte aligned, scales 4-byte
+ * aligned (else FP4_ERR_ALIGN).  No workspace; nothing allocated. */
+fp4_status fp4_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
+                       int64_t K, void* c, int32_t c_dtype, int64_t ldc, void* stream);
+
 /* The RHT sign mask of a seed (host function): low 16 bits of word 0 of
  * Philox4x32-10(key = seed, counter = (0, 0, 1, 0)); bit j set: d_j = -1. */
 uint16_t fp4_rht_signs(uint64_t rht_seed);

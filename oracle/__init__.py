@@ -288,6 +288,18 @@ def quantize_block(y, fmt, rounding, scale_byte, tensor_scale, row_a, col_a0, W,
     return out
 
 
+def gemm_mx(a_codes, a_scales, b_codes, b_scales, M, N, K, fmt="mxfp4") -> np.ndarray:
+    """C = A · Bᵀ of two MXFP4 operands quantized along K, in float64: each
+    operand rebuilt element by element by ``dequantize`` (sign * L[k] *
+    2^(S - 127), exact), then one float64 matrix product.  The plain
+    definition of the GEMM the [UFP4] page's single-GEMM diagnostics and the
+    [MXFP4] page's GEMM kernels consume ("Diagnosticos de Cuantizacion y
+    GEMM"; "4. Resultats Experimentaux")."""
+    a = dequantize(a_codes, a_scales, None, M, K, fmt, "row").astype(np.float64)
+    b = dequantize(b_codes, b_scales, None, N, K, fmt, "row").astype(np.float64)
+    return a @ b.T
+
+
 # ------------------------------------------------------------ unpack helpers
 def unpack_codes(codes: np.ndarray) -> np.ndarray:
     """[R, W/2] packed bytes -> [R, W] 4-bit codes (even column = low nibble)."""
