@@ -177,6 +177,158 @@ def cpu_baseline(w, tensors, budget_s=12.0):
                 reps, len(w.calls), dt)}
 
 
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
+
+
+def gemm_bench(args, w, dev):
+    """The GEMM workload: operands quantized once (outside the timed region),
+    then each step runs the workload's GEMMs; value = their flops over their
+    time.  Also reported: each operand's quantize time (the quantize
+    overhead relative to the GEMMs), the output SQNR of every GEMM against a
+    float32 product of the BF16 inputs, with and without the RHT, and the
+    oracle's GEMM rate on a sample."""
+    import numpy as np
+    import torch
+
+    import block_scaled_bit_fp4_amd as fp4
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    host = {k: w.make(k) for k in w.tensors}
+    x = {k: to_dev(v) for k, v in host.items()}
+    stream = torch.cuda.current_stream()
+
+    def quant(op, rht):
+        t, axis, rounding, sr_seed = op
+        return fp4.quantize(x[t], w.fmt, axis, rounding, rht, 0, sr_seed)
+
+    ops = {}
+    for gm in w.gemms:
+        for op in (gm.a, gm.b):
+            if op not in ops:
+                ops[op] = quant(op, w.rht)[:2]
+    shapes, outs = [], []
+    for gm in w.gemms:
+        (ac, _), (bc, _) = ops[gm.a], ops[gm.b]
+        M, N, K = ac.shape[0], bc.shape[0], 2 * ac.shape[1]
+        shapes.append((M, N, K))
+        outs.append(torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+
+    def run(i):
+        gm = w.gemms[i]
+        (ac, asc), (bc, bsc) = ops[gm.a], ops[gm.b]
+        fp4.gemm_mx(ac, asc, bc, bsc, out=outs[i], stream=stream)
+
+    def step():
+        for i in range(len(w.gemms)):
+            run(i)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    flops = [2.0 * M * N * K for M, N, K in shapes]
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    reps = max(5, args.steps // 2)
+    per_call = [timed(lambda i=i: run(i), reps) for i in range(len(w.gemms))]
+    quant_us = {}
+    for op in ops:
+        lab = "%s %s %s" % (op[0], op[1], op[2])
+        t, axis, rounding, sr_seed = op
+        codes, scales = ops[op]
+        quant_us[lab] = round(timed(lambda: fp4.quantize(
+            x[t], w.fmt, axis, rounding, w.rht, 0, sr_seed, codes=codes, scales=scales,
+            stream=stream), reps) * 1e3, 2)
+
+    # output SQNR per path against float32 products of the BF16 inputs
+    sqnr = {}
+    plain = {op: quant(op, False)[:2] for op in ops}
+    for gm, (M, N, K) in zip(w.gemms, shapes):
+        def operand(op):
+            t, axis = op[0], op[1]
+            v = x[t].float()
+            return (v if axis == "row" else v.t()).contiguous()
+        ref = operand(gm.a) @ operand(gm.b).t().contiguous()
+        ref_e = float((ref.double() ** 2).sum())
+        res = {}
+        for tag, qs in (("rht", ops), ("no_rht", plain)):
+            (ac, asc), (bc, bsc) = qs[gm.a], qs[gm.b]
+            c = fp4.gemm_mx(ac, asc, bc, bsc, out_dtype=torch.float32)
+            err = float(((c.double() - ref.double()) ** 2).sum())
+            res[tag] = round(10.0 * np.log10(ref_e / err), 2) if err > 0 else None
+            del c
+        sqnr[gm.name] = res
+        del ref
+        torch.cuda.empty_cache()
+
+    dom = max(range(len(w.gemms)), key=lambda i: per_call[i])
+    achieved = flops[dom] / (per_call[dom] * 1e-3) / 1e12
+    line = {
+        "metric": "MXFP4 GEMM TFLOP/s (forward, input-gradient and weight-gradient GEMMs of one "
+                  "linear layer)",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description,
+                   "gemms": [{"name": gm.name, "M": M, "N": N, "K": K}
+                             for gm, (M, N, K) in zip(w.gemms, shapes)],
+                   "per_call_us": [round(m * 1e3, 2) for m in per_call],
+                   "per_call_tflops": [round(f / (m * 1e-3) / 1e12, 1)
+                                       for f, m in zip(flops, per_call)],
+                   "quantize_us": quant_us,
+                   "quantize_over_gemm": round(sum(quant_us.values()) /
+                                               (sum(per_call) * 1e3), 4),
+                   "output_sqnr_db": sqnr},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "call %d (%s GEMM): fp4_gemm_mx" % (dom, w.gemms[dom].name),
+                     "mean_us": round(per_call[dom] * 1e3, 2)},
+        "cpu_baseline": None if args.no_cpu_baseline else gemm_cpu_baseline(w, host, ops),
+    }
+    return line
+
+
+def gemm_cpu_baseline(w, host, ops, budget_s=12.0):
+    """The oracle's GEMM on the host: 64 x 64 output blocks of the forward
+    GEMM (its full K), repeated for ~budget_s."""
+    import oracle
+    gm = w.gemms[0]
+    (ac, asc), (bc, bsc) = ops[gm.a], ops[gm.b]
+    a, sa = ac[:64].cpu().numpy(), asc[:64].cpu().numpy()
+    b, sb = bc[:64].cpu().numpy(), bsc[:64].cpu().numpy()
+    K = 2 * a.shape[1]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm_mx(a, sa, b, sb, 64, 64, K)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(reps * 2.0 * 64 * 64 * K / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d blocks of 64 x 64 outputs of the %s GEMM (K = %d) in %.1f s" % (
+                reps, gm.name, K, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +370,9 @@ def main():
     w = workloads.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if isinstance(w, workloads.GemmWorkload):
+        print(json.dumps(gemm_bench(args, w, dev)), flush=True)
+        return
     tensors = {}
     for call in w.calls:
         if call.tensor not in tensors:

@@ -229,6 +229,44 @@ def _w_dequant() -> Workload:
     return w
 
 
+@dataclass
+class Gemm:
+    """One GEMM C = A · Bᵀ of MXFP4 operands quantized along K: each operand
+    is (tensor, axis, rounding, sr_seed) of a quantize call whose A is the
+    GEMM operand (axis "col" quantizes the transpose)."""
+    name: str
+    a: tuple
+    b: tuple
+
+
+@dataclass
+class GemmWorkload:
+    name: str
+    description: str
+    fmt: str
+    rht: bool
+    tensors: dict = field(default_factory=dict)
+    gemms: list = field(default_factory=list)
+
+    def make(self, name: str) -> np.ndarray:
+        rows, cols, _dt, maker = self.tensors[name]
+        return maker()
+
+
+def _w_gemm_mx() -> GemmWorkload:
+    lin = _w_linear_layer()
+    w = GemmWorkload("mxfp4_rht_training_gemms_h4096_f14336_t16384",
+                     "the three GEMMs of one linear layer (hidden 4096, FFN 14336, 16384 tokens) "
+                     "on MXFP4 + RHT operands quantized along each GEMM's K (SR on dY): forward "
+                     "Y = X Wᵀ, input gradient dX = dY W, weight gradient dW = dYᵀ X; BF16 out",
+                     "mxfp4", True)
+    w.tensors = dict(lin.tensors)
+    w.gemms = [Gemm("fprop", ("X", "row", "rtne", 0), ("W", "row", "rtne", 0)),
+               Gemm("dgrad", ("dY", "row", "sr", 1), ("W", "col", "rtne", 0)),
+               Gemm("wgrad", ("dY", "col", "sr", 1), ("X", "col", "rtne", 0))]
+    return w
+
+
 WORKLOADS = {
     "single_fp32": _w_single_fp32,
     "activation": _w_activation,
@@ -241,6 +279,7 @@ WORKLOADS = {
     "linear_layer_dual": _w_linear_layer_dual,
     "training_operands": _w_training_operands,
     "dequant": _w_dequant,
+    "gemm_mx": _w_gemm_mx,
 }
 
 
