@@ -282,6 +282,8 @@ fp4_status fp4_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales,
   if (c_dtype != FP4_BF16 && c_dtype != FP4_F32) return FP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || ldc < N) return FP4_ERR_SHAPE;
   if (M % 128 || N % 128 || K % 128 || K == 0) return FP4_ERR_SHAPE;
+  // each operand's codes are addressed with 32-bit byte offsets
+  if (M * (K / 2) > 0xFFFFFFFFll || N * (K / 2) > 0xFFFFFFFFll) return FP4_ERR_SHAPE;
   if (M == 0 || N == 0) return FP4_OK;
   if (!a_codes || !a_scales || !b_codes || !b_scales || !c) return FP4_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(b_codes) || !aligned16(c)) return FP4_ERR_ALIGN;

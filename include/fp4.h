@@ -196,8 +196,9 @@ fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, 
  * matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4), in its order, so
  * results match an exact reference within a binary32 accumulation bound,
  * not bit for bit.  C is M x N, FP32 or BF16 (round to nearest even), row
- * leading dimension ldc >= N.  M, N and K must be multiples of 128 and
- * K > 0 (else FP4_ERR_SHAPE); codes and C 16-byte aligned, scales 4-byte
+ * leading dimension ldc >= N.  M, N and K must be multiples of 128, K > 0,
+ * and each operand's codes under 4 GiB (M * K / 2 and N * K / 2 bytes),
+ * else FP4_ERR_SHAPE; codes and C 16-byte aligned, scales 4-byte
  * aligned (else FP4_ERR_ALIGN).  No workspace; nothing allocated. */
 fp4_status fp4_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales,
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t M, int64_t N,
