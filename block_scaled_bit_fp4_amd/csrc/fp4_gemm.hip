@@ -26,6 +26,7 @@ constexpr int kRowBytes = kBK / 2;   // code bytes of one row per step
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
@@ -40,70 +41,97 @@ struct GemmArgs {
   int64_t n_tn;       // column tiles
 };
 
-// Direct global -> LDS loads (the buffer instructions' LDS form): each lane
-// of a wave deposits its 16 (or 4) bytes at the wave's LDS base + lane *
-// size, so a wave instruction fills 1 KB (256 B) contiguously and no
-// staging registers are needed, which leaves room for a three-deep pipeline.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ void buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds,
-                                int size, int voffset, int soffset, int offset,
-                                int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// LDS: two stages of codes (A tile then B tile, 256 rows x 64 bytes each)
+// and two buffers of scales, each holding a group of 16 K steps: the step's
+// E8M0 word (four K blocks) of each row, step-major -- word (step s, row r)
+// at s * 1 KB + 4 r, A then B -- so the words a wave reads for one step
+// (32 consecutive rows) are consecutive.
+constexpr int kTileBytes = kBM * kRowBytes;            // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;            // 32 KB
+constexpr int kGroupSteps = 16;                        // K steps per scale group
+constexpr int kScaleOpBytes = kGroupSteps * kBM * 4;   // 16 KB per operand
+constexpr int kScaleBufBytes = 2 * kScaleOpBytes;      // 32 KB
+constexpr int kScaleBase = 2 * kStageBytes;
+constexpr int kLdsBytes = kScaleBase + 2 * kScaleBufBytes;  // 128 KB
 
-// Buffer descriptor (base, byte range, gfx9 data format word), wave-uniform.
-__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-constexpr int kStages = 3;                 // K steps in LDS at once
-constexpr int kTileBytes = kBM * kRowBytes;  // one operand's codes per step (16 KB)
-constexpr int kScaleOff = 2 * kTileBytes;    // then A's and B's scale words
-constexpr int kStageSize = kScaleOff + (kBM + kBN) * 4;
-
-// Position of (row, 16-byte segment s) of a step's operand tile: rows of 64
+// Position of (row, 16-byte segment s) of a stage's operand tile: rows of 64
 // bytes, segments XOR-swizzled by bits 2-3 of the row, so the 16 lanes of a
-// 16-byte fragment-read phase (16 consecutive rows, one segment) reach 16
-// distinct 4-bank groups.
+// 16-byte fragment-read phase (16 consecutive rows, one segment) and of a
+// 16-byte store phase (4 rows, 4 segments) reach 16 distinct 4-bank groups.
 __device__ __forceinline__ int tile_at(int row, int s) {
   return row * kRowBytes + ((s ^ ((row >> 2) & 3)) << 4);
 }
 
-// One K step of the workgroup's operands into LDS stage `st`: wave w loads
-// rows 64w .. 64w + 63 of A and of B (4 instructions each, 16 rows of 64
-// bytes per instruction) and the step's scale words of those rows.  Rows
-// past M or N read the last row (never stored).
-__device__ __forceinline__ void issue_stage(const GemmArgs& g, i32x4 ra, i32x4 rbs, i32x4 rsa,
-                                            i32x4 rsb, int64_t m0, int64_t n0, int64_t ks,
-                                            uint8_t* st) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rb = g.K / 2, sb = g.K / 32;
-  const int seg_phys = lane & 3;
+// Global fetches.  Wave w fetches rows 64w .. 64w + 63 of A and of B, four
+// loads each per K step: 16 rows per load, four lanes per row reading the
+// row's 64 code bytes in address order (64-byte row pieces are what the L2
+// serves at full rate; narrower per-row pieces run several times slower).
+// Scales come the same way, 64 bytes per row = a group of 16 steps: group
+// g + 1 is fetched as eight loads per wave during steps 16g + 8 .. 16g + 15
+// (loads 0-3 for A's rows, 4-7 for B's), into the buffer group g - 1 used.
+struct Fetch {
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  int code_a[4], code_b[4];  // lane byte offsets of its four rows' codes (step 0)
+  int row_a, row_b;          // the lane's first row in A and in B (q = 0)
+  int last_a, last_b;        // M - 1, N - 1
+  uint32_t sb;               // scale bytes per row, K / 32
+};
+
+// Byte offset of the lane's 16-byte scale piece of (clamped) row `row` in
+// group `grp`: the row's words of steps 16 grp + 4p .. 16 grp + 4p + 3.
+__device__ __forceinline__ uint32_t scale_off(const Fetch& f, int row, int grp) {
+  return (uint32_t)row * f.sb + 16u * (threadIdx.x & 3) + (uint32_t)grp * (kGroupSteps * 4);
+}
+
+__device__ __forceinline__ void fetch_step(const Fetch& f, int j, int nk, u32x4 (&ca)[4],
+                                           u32x4 (&cb)[4], u32x4& sc) {
+  const int js = min(j, nk - 1);  // past the last step: a harmless re-read
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int r0 = wave * 64 + q * 16;       // first row of this instruction
-    const int r = r0 + (lane >> 2);
-    const int s = seg_phys ^ ((r >> 2) & 3);  // the global segment this lane fetches
-    const int va = (int)(min(m0 + r, g.M - 1) * rb + ks * kRowBytes + s * 16);
-    const int vb = (int)(min(n0 + r, g.N - 1) * rb + ks * kRowBytes + s * 16);
-    buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + r0 * kRowBytes), 16, va,
-                    0, 0, 0);
-    buffer_load_lds(rbs,
-                    (__attribute__((address_space(3))) void*)(st + kTileBytes + r0 * kRowBytes),
-                    16, vb, 0, 0, 0);
+    ca[q] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.code_a[q] + js * kRowBytes, 0, 0));
+    cb[q] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.code_b[q] + js * kRowBytes, 0, 0));
   }
-  const int r = wave * 64 + lane;
-  const int vsa = (int)(min(m0 + r, g.M - 1) * sb + ks * 4);
-  const int vsb = (int)(min(n0 + r, g.N - 1) * sb + ks * 4);
-  buffer_load_lds(rsa, (__attribute__((address_space(3))) void*)(st + kScaleOff + wave * 256), 4,
-                  vsa, 0, 0, 0);
-  buffer_load_lds(rsb,
-                  (__attribute__((address_space(3))) void*)(st + kScaleOff + kBM * 4 + wave * 256),
-                  4, vsb, 0, 0, 0);
+  if ((j & (kGroupSteps - 1)) >= kGroupSteps / 2) {
+    // piece i of group j / 16 + 1; pieces past the row's last group read
+    // the next row (or nothing, past the buffer) into a buffer no step reads
+    const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2, q = i & 3;
+    const bool is_a = i < 4;
+    const int row = is_a ? min(f.row_a + 16 * q, f.last_a) : min(f.row_b + 16 * q, f.last_b);
+    sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       is_a ? f.rsa : f.rsb, (int)scale_off(f, row, (j >> 4) + 1), 0, 0));
+  }
+}
+
+// A scale row piece (16 bytes: the row's words of steps 4p .. 4p + 3 of
+// its group) into the group's buffer, operand `op`, row `r`.
+__device__ __forceinline__ void store_scale_piece(uint8_t* lds, int group, int op, int r,
+                                                  const u32x4& sc) {
+  const int p = threadIdx.x & 3;
+  uint8_t* base = lds + kScaleBase + (group & 1) * kScaleBufBytes + op * kScaleOpBytes +
+                  (4 * p) * (kBM * 4) + r * 4;
+  *reinterpret_cast<uint32_t*>(base) = sc.x;
+  *reinterpret_cast<uint32_t*>(base + kBM * 4) = sc.y;
+  *reinterpret_cast<uint32_t*>(base + 2 * kBM * 4) = sc.z;
+  *reinterpret_cast<uint32_t*>(base + 3 * kBM * 4) = sc.w;
+}
+
+// Store a fetched step into its LDS stage (and its scale piece, if any).
+__device__ __forceinline__ void store_step(uint8_t* lds, int j, const int (&st_off)[4],
+                                           const u32x4 (&ca)[4], const u32x4 (&cb)[4],
+                                           const u32x4& sc) {
+  uint8_t* st = lds + (j & 1) * kStageBytes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    *reinterpret_cast<u32x4*>(st + st_off[q]) = ca[q];
+    *reinterpret_cast<u32x4*>(st + kTileBytes + st_off[q]) = cb[q];
+  }
+  if ((j & (kGroupSteps - 1)) >= kGroupSteps / 2) {
+    const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2;
+    const int r = (threadIdx.x >> 6) * 64 + (i & 3) * 16 + ((threadIdx.x & 63) >> 2);
+    store_scale_piece(lds, (j >> 4) + 1, i >> 2, r, sc);
+  }
 }
 
 __device__ __forceinline__ void store_c(float* p, float v) { *p = v; }
@@ -114,51 +142,117 @@ __device__ __forceinline__ void store_c(uint16_t* p, float v) {
   *p = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_convertvector(w, b2));
 }
 
-// One K step of a wave from an LDS stage: two sub-steps of 4 x 4 MFMAs of
-// 32 x 32 x 64.
-__device__ __forceinline__ void mma_step(const uint8_t* st, f32x16 (&acc)[4][4], int wm, int wn,
-                                         int fr, int fk) {
-  const uint32_t* sca = reinterpret_cast<const uint32_t*>(st + kScaleOff);
+// Fragment reads of one half step (64 of the 128 K elements) for a wave:
+// A rows wm * 128 + t * 32 + fr and B rows wn * 128 + t * 32 + fr, t = 0..3,
+// 16 bytes each at the lane's segment; `oa` and `ob` are the lane's byte
+// offsets of its t = 0 rows (swizzled segment included).
+__device__ __forceinline__ void load_frags(const uint8_t* st, int oa, int ob, u32x4 (&a)[4],
+                                           u32x4 (&b)[4]) {
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    i32x8 af[4], bf[4];
-    int sa[4], sb[4];
-    const int kb = sub * 2 + fk;  // the lane's 32-element block within the step
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int ra = wm * 128 + t * 32 + fr, rbw = wn * 128 + t * 32 + fr;
-      const u32x4 va = *reinterpret_cast<const u32x4*>(st + tile_at(ra, kb));
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(st + kTileBytes + tile_at(rbw, kb));
-      af[t] = i32x8{(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0};
-      bf[t] = i32x8{(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0};
-      // the instruction reads its scale from byte 0
-      sa[t] = (int)((sca[ra] >> (8 * kb)) & 0xFFu);
-      sb[t] = (int)((sca[kBM + rbw] >> (8 * kb)) & 0xFFu);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4,
-                                                                    4, 0, sa[i], 0, sb[j]);
+  for (int t = 0; t < 4; ++t) {
+    a[t] = *reinterpret_cast<const u32x4*>(st + oa + t * 32 * kRowBytes);
+    b[t] = *reinterpret_cast<const u32x4*>(st + kTileBytes + ob + t * 32 * kRowBytes);
   }
 }
 
+// Step j's scale words of the lane's rows (byte i = K block i of the step).
+__device__ __forceinline__ void load_scales(const uint8_t* lds, int j, int ra, int rb,
+                                            uint32_t (&wa)[4], uint32_t (&wb)[4]) {
+  const uint8_t* plane = lds + kScaleBase + ((j >> 4) & 1) * kScaleBufBytes +
+                         (j & (kGroupSteps - 1)) * (kBM * 4);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    wa[t] = *reinterpret_cast<const uint32_t*>(plane + (ra + t * 32) * 4);
+    wb[t] = *reinterpret_cast<const uint32_t*>(plane + kScaleOpBytes + (rb + t * 32) * 4);
+  }
+}
+
+// 4 x 4 MFMAs of 32 x 32 x 64 on one half step; `sh` selects the lane's
+// scale byte (its K block) in the step's scale words.
+__device__ __forceinline__ void mma_half(const u32x4 (&a)[4], const u32x4 (&b)[4],
+                                         const uint32_t (&wa)[4], const uint32_t (&wb)[4], int sh,
+                                         f32x16 (&acc)[4][4]) {
+  i32x8 af[4], bf[4];
+  int sa[4], sb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    af[t] = i32x8{(int)a[t].x, (int)a[t].y, (int)a[t].z, (int)a[t].w, 0, 0, 0, 0};
+    bf[t] = i32x8{(int)b[t].x, (int)b[t].y, (int)b[t].z, (int)b[t].w, 0, 0, 0, 0};
+    // the instruction reads its scale from byte 0
+    sa[t] = (int)((wa[t] >> sh) & 0xFFu);
+    sb[t] = (int)((wb[t] >> sh) & 0xFFu);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0,
+                                                                  sa[i], 0, sb[j]);
+}
+
+// An empty statement that reads one register of every accumulator: the
+// half step's MFMAs (pure operations, which instruction selection may
+// otherwise sink past the scheduling barrier into the next half step) are
+// issued before it.
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j][0]));
+}
+
+// Interleave a half step's 16 MFMAs with the LDS reads issued beside them
+// (the next half step's fragments and scale words), one read after each of
+// the first MFMAs, so the reads' latency hides behind the matrix pipe
+// instead of stalling the single wave.  `VMEM` global loads go first.
+template <int VMEM>
+__device__ __forceinline__ void interleave_half() {
+  if (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, VMEM, 0);  // global loads
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_sched_barrier(0);  // nothing crosses the half-step boundary
+}
+
 // Workgroup: 4 waves in 2 x 2, each computing a 128 x 128 block of C as
-// 4 x 4 MFMA tiles of 32 x 32; K steps of 128 in a three-stage LDS ring
-// filled by direct loads two steps ahead.
+// 4 x 4 MFMA tiles of 32 x 32; K steps of 128.  Software pipeline per step
+// ks: the first half's MFMAs run on fragments read earlier while the second
+// half's fragments are read; at mid step the registers fetched for step
+// ks + 1 go to LDS (the stage step ks - 1 used), one barrier publishes them,
+// step ks + 2 is fetched, and the second half's MFMAs run while step
+// ks + 1's first fragments and scale words are read.
 template <typename TC>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint8_t lds[kStages * kStageSize];
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t tm = blockIdx.x / g.n_tn, tn = blockIdx.x - tm * g.n_tn;
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
-  const int64_t nk = g.K / kBK;
-  const i32x4 ra = make_rsrc(g.a, (uint32_t)(g.M * (g.K / 2)));
-  const i32x4 rbs = make_rsrc(g.b, (uint32_t)(g.N * (g.K / 2)));
-  const i32x4 rsa = make_rsrc(g.as, (uint32_t)(g.M * (g.K / 32)));
-  const i32x4 rsb = make_rsrc(g.bs, (uint32_t)(g.N * (g.K / 32)));
+  const int nk = (int)(g.K / kBK);
+  const int64_t rb = g.K / 2, sb = g.K / 32;
+
+  Fetch f;
+  f.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(uint32_t)(g.M * rb), 0x00020000);
+  f.rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, (int)(uint32_t)(g.N * rb), 0x00020000);
+  f.rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.as, (short)0, (int)(uint32_t)(g.M * sb), 0x00020000);
+  f.rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.bs, (short)0, (int)(uint32_t)(g.N * sb), 0x00020000);
+  int st_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = wave * 64 + q * 16 + (lane >> 2), p = lane & 3;
+    // rows past M or N read the last row (never stored)
+    f.code_a[q] = (int)(min(m0 + r, g.M - 1) * rb) + p * 16;
+    f.code_b[q] = (int)(min(n0 + r, g.N - 1) * rb) + p * 16;
+    st_off[q] = tile_at(r, p);
+  }
+  f.row_a = (int)m0 + wave * 64 + (lane >> 2);
+  f.row_b = (int)n0 + wave * 64 + (lane >> 2);
+  f.last_a = (int)g.M - 1;
+  f.last_b = (int)g.N - 1;
+  f.sb = (uint32_t)sb;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -167,19 +261,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int fr = lane & 31, fk = lane >> 5;  // fragment row, K block
-  issue_stage(g, ra, rbs, rsa, rsb, m0, n0, 0, lds);
-  issue_stage(g, ra, rbs, rsa, rsb, m0, n0, min((int64_t)1, nk - 1), lds + kStageSize);
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    // this wave's loads of step ks are done before the barrier (the
-    // compiler waits for all of this wave's outstanding loads here: it
-    // cannot tell the stages apart); the barrier makes every wave's share
-    // visible and frees the stage read in step ks - 1
-    __builtin_amdgcn_s_waitcnt((10 & 0xF) | (0x7 << 4) | (0xF << 8));
-    __syncthreads();
-    issue_stage(g, ra, rbs, rsa, rsb, m0, n0, min(ks + 2, nk - 1),
-                lds + ((ks + 2) % kStages) * kStageSize);
-    mma_step(lds + (ks % kStages) * kStageSize, acc, wm, wn, fr, fk);
+  const int rowa = wm * 128 + fr, rowb = wn * 128 + fr;
+  // tile_at() of the lane's t = 0 rows for the two half steps (the swizzle
+  // depends on bits 2-3 of the row, which t * 32 does not change)
+  const int oa0 = tile_at(rowa, fk), oa1 = tile_at(rowa, 2 + fk);
+  const int ob0 = tile_at(rowb, fk), ob1 = tile_at(rowb, 2 + fk);
+  const int sh0 = 8 * fk, sh1 = 8 * (2 + fk);
+
+  // Prologue: scale group 0 (all eight pieces), then steps 0 (stored) and
+  // 1 (in flight).
+  u32x4 ca[4], cb[4], sc;
+  {
+    u32x4 s0[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s0[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            f.rsa, (int)scale_off(f, min(f.row_a + 16 * q, f.last_a), 0), 0, 0));
+      s0[4 + q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                f.rsb, (int)scale_off(f, min(f.row_b + 16 * q, f.last_b), 0), 0, 0));
+    }
+    fetch_step(f, 0, nk, ca, cb, sc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      store_scale_piece(lds, 0, i >> 2, wave * 64 + (i & 3) * 16 + (lane >> 2), s0[i]);
+    store_step(lds, 0, st_off, ca, cb, sc);
   }
+  fetch_step(f, 1, nk, ca, cb, sc);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS stores done (loads may stay in flight)
+  __syncthreads();
+
+  u32x4 a0[4], b0[4], a1[4], b1[4];
+  uint32_t wa[4], wb[4];
+  load_scales(lds, 0, rowa, rowb, wa, wb);
+  load_frags(lds, oa0, ob0, a0, b0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const uint8_t* st = lds + (ks & 1) * kStageBytes;
+    load_frags(st, oa1, ob1, a1, b1);
+    mma_half(a0, b0, wa, wb, sh0, acc);
+    pin_acc(acc);
+    interleave_half<0>();
+
+    // Step ks + 1 has landed in registers: store it, then one barrier makes
+    // it visible.  Every wave finished reading step ks - 1 (whose stage this
+    // is) before the previous barrier.  A plain s_barrier after explicit
+    // waits: the workgroup fence of __syncthreads adds nothing here.
+    store_step(lds, ks + 1, st_off, ca, cb, sc);
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_step(f, ks + 2, nk, ca, cb, sc);
+    // the next step's first fragments and scale words (a clamped, unused
+    // read after the last step)
+    const uint8_t* sn = lds + ((ks + 1) & 1) * kStageBytes;
+    uint32_t wan[4], wbn[4];
+    load_scales(lds, ks + 1, rowa, rowb, wan, wbn);
+    load_frags(sn, oa0, ob0, a0, b0);
+    mma_half(a1, b1, wa, wb, sh1, acc);
+    pin_acc(acc);
+    interleave_half<8>();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wa[t] = wan[t];
+      wb[t] = wbn[t];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // M and N are multiples of 128, so a wave's 128 x 128 block lies wholly
   // inside C or wholly past its edge

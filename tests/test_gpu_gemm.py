@@ -38,7 +38,10 @@ def _check(c_gpu, a, sa, b, sb, M, N, K, dtype, tag):
         bound[tuple(bad[0])])
 
 
-@pytest.mark.parametrize("shape", [(128, 128, 128), (256, 384, 512), (384, 256, 1152)])
+# K = 128 x (1, 4, 9, 21, 33) steps: one step, whole and partial 16-step
+# scale groups, and groups past the first
+@pytest.mark.parametrize("shape", [(128, 128, 128), (256, 384, 512), (384, 256, 1152),
+                                   (256, 256, 2688), (128, 384, 4224)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_random_codes(shape, dtype):
     M, N, K = shape
