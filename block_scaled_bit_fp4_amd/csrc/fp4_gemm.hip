@@ -201,12 +201,25 @@ __device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
     for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j][0]));
 }
 
-// Interleave a half step's 16 MFMAs with the LDS reads issued beside them
-// (the next half step's fragments and scale words), one read after each of
-// the first MFMAs, so the reads' latency hides behind the matrix pipe
-// instead of stalling the single wave.  `VMEM` global loads go first.
+// Interleave a half step's 16 MFMAs with the LDS traffic issued beside it,
+// one LDS instruction after each MFMA, so the traffic's latency hides
+// behind the matrix pipe instead of stalling the single wave.  First half:
+// the next step's stores alternate with this step's second-half fragment
+// reads.  Second half: `VMEM` global loads first, then the next step's
+// first fragments and scale words.
+__device__ __forceinline__ void interleave_first() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS store
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_barrier(0);  // nothing crosses the half-step boundary
+}
+
 template <int VMEM>
-__device__ __forceinline__ void interleave_half() {
+__device__ __forceinline__ void interleave_second() {
   if (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, VMEM, 0);  // global loads
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
@@ -214,7 +227,52 @@ __device__ __forceinline__ void interleave_half() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  __builtin_amdgcn_sched_barrier(0);  // nothing crosses the half-step boundary
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K step ks.  `set` holds step ks + 1, fetched three steps earlier
+// (two register sets alternate, so a fetch has a step and a half to land).
+// First half: store it to LDS (the stage step ks - 1 used, which every wave
+// finished reading before the previous barrier) between the MFMAs on the
+// first fragments, while this step's second-half fragments are read.  One
+// barrier publishes it; `set` is refilled with step ks + 3; the second
+// half's MFMAs run while step ks + 1's first fragments and scale words are
+// read.
+__device__ __forceinline__ void k_step(const Fetch& f, uint8_t* lds, int ks, int nk,
+                                       const int (&st_off)[4], int rowa, int rowb, int oa0,
+                                       int ob0, int oa1, int ob1, int sh0, int sh1,
+                                       u32x4 (&a0)[4], u32x4 (&b0)[4], u32x4 (&a1)[4],
+                                       u32x4 (&b1)[4], uint32_t (&wa)[4], uint32_t (&wb)[4],
+                                       u32x4 (&ca)[4], u32x4 (&cb)[4], u32x4& sc,
+                                       f32x16 (&acc)[4][4]) {
+  const uint8_t* st = lds + (ks & 1) * kStageBytes;
+  store_step(lds, ks + 1, st_off, ca, cb, sc);
+  load_frags(st, oa1, ob1, a1, b1);
+  mma_half(a0, b0, wa, wb, sh0, acc);
+  pin_acc(acc);
+  interleave_first();
+
+  // LDS traffic done (the loads in flight stay in flight), then a plain
+  // s_barrier: the workgroup fence of __syncthreads would make the
+  // compiler wait for every outstanding load.
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_step(f, ks + 3, nk, ca, cb, sc);
+  // the next step's first fragments and scale words (a clamped, unused
+  // read after the last step)
+  const uint8_t* sn = lds + ((ks + 1) & 1) * kStageBytes;
+  uint32_t wan[4], wbn[4];
+  load_scales(lds, ks + 1, rowa, rowb, wan, wbn);
+  load_frags(sn, oa0, ob0, a0, b0);
+  mma_half(a1, b1, wa, wb, sh1, acc);
+  pin_acc(acc);
+  interleave_second<8>();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    wa[t] = wan[t];
+    wb[t] = wbn[t];
+  }
 }
 
 // Workgroup: 4 waves in 2 x 2, each computing a 128 x 128 block of C as
@@ -268,9 +326,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
   const int ob0 = tile_at(rowb, fk), ob1 = tile_at(rowb, 2 + fk);
   const int sh0 = 8 * fk, sh1 = 8 * (2 + fk);
 
-  // Prologue: scale group 0 (all eight pieces), then steps 0 (stored) and
-  // 1 (in flight).
-  u32x4 ca[4], cb[4], sc;
+  // Prologue: scale group 0 (all eight pieces) and step 0 stored; steps 1
+  // and 2 in flight in the two register sets.
+  u32x4 ca0[4], cb0[4], sc0, ca1[4], cb1[4], sc1;
   {
     u32x4 s0[8];
 #pragma unroll
@@ -280,51 +338,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
       s0[4 + q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 f.rsb, (int)scale_off(f, min(f.row_b + 16 * q, f.last_b), 0), 0, 0));
     }
-    fetch_step(f, 0, nk, ca, cb, sc);
+    fetch_step(f, 0, nk, ca0, cb0, sc0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       store_scale_piece(lds, 0, i >> 2, wave * 64 + (i & 3) * 16 + (lane >> 2), s0[i]);
-    store_step(lds, 0, st_off, ca, cb, sc);
+    store_step(lds, 0, st_off, ca0, cb0, sc0);
   }
-  fetch_step(f, 1, nk, ca, cb, sc);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS stores done (loads may stay in flight)
+  fetch_step(f, 1, nk, ca1, cb1, sc1);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // step 0's stores done before set 0 is refilled
+  fetch_step(f, 2, nk, ca0, cb0, sc0);
   __syncthreads();
 
-  u32x4 a0[4], b0[4], a1[4], b1[4];
-  uint32_t wa[4], wb[4];
+  u32x4 a0[4], b0[4], a1[4], b1[4];  // first- and second-half fragments
+  uint32_t wa[4], wb[4];             // the step's scale words
   load_scales(lds, 0, rowa, rowb, wa, wb);
   load_frags(lds, oa0, ob0, a0, b0);
-  for (int ks = 0; ks < nk; ++ks) {
-    const uint8_t* st = lds + (ks & 1) * kStageBytes;
-    load_frags(st, oa1, ob1, a1, b1);
-    mma_half(a0, b0, wa, wb, sh0, acc);
-    pin_acc(acc);
-    interleave_half<0>();
-
-    // Step ks + 1 has landed in registers: store it, then one barrier makes
-    // it visible.  Every wave finished reading step ks - 1 (whose stage this
-    // is) before the previous barrier.  A plain s_barrier after explicit
-    // waits: the workgroup fence of __syncthreads adds nothing here.
-    store_step(lds, ks + 1, st_off, ca, cb, sc);
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    fetch_step(f, ks + 2, nk, ca, cb, sc);
-    // the next step's first fragments and scale words (a clamped, unused
-    // read after the last step)
-    const uint8_t* sn = lds + ((ks + 1) & 1) * kStageBytes;
-    uint32_t wan[4], wbn[4];
-    load_scales(lds, ks + 1, rowa, rowb, wan, wbn);
-    load_frags(sn, oa0, ob0, a0, b0);
-    mma_half(a1, b1, wa, wb, sh1, acc);
-    pin_acc(acc);
-    interleave_half<8>();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      wa[t] = wan[t];
-      wb[t] = wbn[t];
-    }
+  // steps in pairs (step ks stores set 1 = step ks + 1, step ks + 1 set 0),
+  // an odd last step after the loop
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    k_step(f, lds, ks, nk, st_off, rowa, rowb, oa0, ob0, oa1, ob1, sh0, sh1, a0, b0, a1, b1, wa,
+           wb, ca1, cb1, sc1, acc);
+    k_step(f, lds, ks + 1, nk, st_off, rowa, rowb, oa0, ob0, oa1, ob1, sh0, sh1, a0, b0, a1, b1,
+           wa, wb, ca0, cb0, sc0, acc);
   }
+  if (ks < nk)
+    k_step(f, lds, ks, nk, st_off, rowa, rowb, oa0, ob0, oa1, ob1, sh0, sh1, a0, b0, a1, b1, wa,
+           wb, ca1, cb1, sc1, acc);
   __builtin_amdgcn_s_waitcnt(0);
 
   // M and N are multiples of 128, so a wave's 128 x 128 block lies wholly
