@@ -83,25 +83,30 @@ __device__ __forceinline__ uint32_t scale_off(const Fetch& f, int row, int grp) 
   return (uint32_t)row * f.sb + 16u * (threadIdx.x & 3) + (uint32_t)grp * (kGroupSteps * 4);
 }
 
-__device__ __forceinline__ void fetch_step(const Fetch& f, int j, int nk, u32x4 (&ca)[4],
-                                           u32x4 (&cb)[4], u32x4& sc) {
-  const int js = min(j, nk - 1);  // past the last step: a harmless re-read
+// Step j's code loads of one operand (four per wave); past the last step a
+// harmless re-read of it.
+__device__ __forceinline__ void fetch_codes(__amdgpu_buffer_rsrc_t r, const int (&off)[4], int j,
+                                            int nk, u32x4 (&c)[4]) {
+  const int js = min(j, nk - 1);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ca[q] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.code_a[q] + js * kRowBytes, 0, 0));
-    cb[q] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.code_b[q] + js * kRowBytes, 0, 0));
-  }
-  if ((j & (kGroupSteps - 1)) >= kGroupSteps / 2) {
-    // piece i of group j / 16 + 1; pieces past the row's last group read
-    // the next row (or nothing, past the buffer) into a buffer no step reads
-    const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2, q = i & 3;
-    const bool is_a = i < 4;
-    const int row = is_a ? min(f.row_a + 16 * q, f.last_a) : min(f.row_b + 16 * q, f.last_b);
-    sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       is_a ? f.rsa : f.rsb, (int)scale_off(f, row, (j >> 4) + 1), 0, 0));
-  }
+  for (int q = 0; q < 4; ++q)
+    c[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off[q] + js * kRowBytes, 0, 0));
+}
+
+// The scale piece step j carries (steps 16g + 8 .. 16g + 15 carry group
+// g + 1: piece i = j mod 16 - 8, A's rows for i < 4, B's for the rest).
+// Pieces past the row's last group read the next row (or nothing, past the
+// buffer) into a buffer no step reads.
+__device__ __forceinline__ bool has_piece(int j) {
+  return (j & (kGroupSteps - 1)) >= kGroupSteps / 2;
+}
+
+__device__ __forceinline__ void fetch_scale(const Fetch& f, int j, u32x4& sc) {
+  const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2, q = i & 3;
+  const bool is_a = i < 4;
+  const int row = is_a ? min(f.row_a + 16 * q, f.last_a) : min(f.row_b + 16 * q, f.last_b);
+  sc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                     is_a ? f.rsa : f.rsb, (int)scale_off(f, row, (j >> 4) + 1), 0, 0));
 }
 
 // A scale row piece (16 bytes: the row's words of steps 4p .. 4p + 3 of
@@ -117,21 +122,22 @@ __device__ __forceinline__ void store_scale_piece(uint8_t* lds, int group, int o
   *reinterpret_cast<uint32_t*>(base + 3 * kBM * 4) = sc.w;
 }
 
-// Store a fetched step into its LDS stage (and its scale piece, if any).
-__device__ __forceinline__ void store_step(uint8_t* lds, int j, const int (&st_off)[4],
-                                           const u32x4 (&ca)[4], const u32x4 (&cb)[4],
-                                           const u32x4& sc) {
+// Store a fetched step's codes into its LDS stage.
+__device__ __forceinline__ void store_codes(uint8_t* lds, int j, const int (&st_off)[4],
+                                            const u32x4 (&ca)[4], const u32x4 (&cb)[4]) {
   uint8_t* st = lds + (j & 1) * kStageBytes;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     *reinterpret_cast<u32x4*>(st + st_off[q]) = ca[q];
     *reinterpret_cast<u32x4*>(st + kTileBytes + st_off[q]) = cb[q];
   }
-  if ((j & (kGroupSteps - 1)) >= kGroupSteps / 2) {
-    const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2;
-    const int r = (threadIdx.x >> 6) * 64 + (i & 3) * 16 + ((threadIdx.x & 63) >> 2);
-    store_scale_piece(lds, (j >> 4) + 1, i >> 2, r, sc);
-  }
+}
+
+// Store step j's scale piece (has_piece(j)) into its group's buffer.
+__device__ __forceinline__ void store_scale(uint8_t* lds, int j, const u32x4& sc) {
+  const int i = (j & (kGroupSteps - 1)) - kGroupSteps / 2;
+  const int r = (threadIdx.x >> 6) * 64 + (i & 3) * 16 + ((threadIdx.x & 63) >> 2);
+  store_scale_piece(lds, (j >> 4) + 1, i >> 2, r, sc);
 }
 
 __device__ __forceinline__ void store_c(float* p, float v) { *p = v; }
@@ -201,43 +207,34 @@ __device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
     for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j][0]));
 }
 
-// Interleave a half step's 16 MFMAs with the LDS traffic issued beside it,
-// one LDS instruction after each MFMA, so the traffic's latency hides
-// behind the matrix pipe instead of stalling the single wave.  First half:
-// the next step's stores alternate with this step's second-half fragment
-// reads.  Second half: `VMEM` global loads first, then the next step's
-// first fragments and scale words.
-__device__ __forceinline__ void interleave_first() {
+// Interleave a half step's 16 MFMAs with the memory instructions issued
+// beside them: `READS` LDS reads and `LOADS` global loads, one after each
+// MFMA, loads every other MFMA.  The MFMA stream keeps the matrix pipe busy
+// while the reads' latency hides behind it, and the loads trickle into the
+// address unit (about 16 clocks per 1 KB wave load) instead of blocking all
+// four waves' instruction streams at once.
+template <int READS, int LOADS>
+__device__ __forceinline__ void interleave_half() {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS store
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+    if (i < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    if (i < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+    if (READS > 8 && i < READS - 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);  // nothing crosses the half-step boundary
 }
 
-template <int VMEM>
-__device__ __forceinline__ void interleave_second() {
-  if (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, VMEM, 0);  // global loads
-#pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// One K step ks.  `set` holds step ks + 1, fetched three steps earlier
-// (two register sets alternate, so a fetch has a step and a half to land).
-// First half: store it to LDS (the stage step ks - 1 used, which every wave
-// finished reading before the previous barrier) between the MFMAs on the
-// first fragments, while this step's second-half fragments are read.  One
-// barrier publishes it; `set` is refilled with step ks + 3; the second
-// half's MFMAs run while step ks + 1's first fragments and scale words are
-// read.
+// One K step ks.  The register set holds step ks + 1, fetched about two
+// steps earlier (two sets alternate).  Start: store it to LDS (the stage
+// step ks - 1 used, which every wave finished reading before the previous
+// barrier) and refill the set's scale piece.  First half: MFMAs on the
+// first fragments, while this step's second-half fragments are read and
+// A's codes of step ks + 3 are fetched into the set.  One barrier publishes
+// step ks + 1.  Second half: MFMAs on the second fragments, while step
+// ks + 1's first fragments and scale words are read and B's codes of step
+// ks + 3 are fetched.
 __device__ __forceinline__ void k_step(const Fetch& f, uint8_t* lds, int ks, int nk,
                                        const int (&st_off)[4], int rowa, int rowb, int oa0,
                                        int ob0, int oa1, int ob1, int sh0, int sh1,
@@ -246,11 +243,16 @@ __device__ __forceinline__ void k_step(const Fetch& f, uint8_t* lds, int ks, int
                                        u32x4 (&ca)[4], u32x4 (&cb)[4], u32x4& sc,
                                        f32x16 (&acc)[4][4]) {
   const uint8_t* st = lds + (ks & 1) * kStageBytes;
-  store_step(lds, ks + 1, st_off, ca, cb, sc);
+  store_codes(lds, ks + 1, st_off, ca, cb);
+  if (has_piece(ks + 1)) store_scale(lds, ks + 1, sc);
+  if (has_piece(ks + 3)) fetch_scale(f, ks + 3, sc);
+  __builtin_amdgcn_sched_barrier(0);
+
   load_frags(st, oa1, ob1, a1, b1);
+  fetch_codes(f.ra, f.code_a, ks + 3, nk, ca);
   mma_half(a0, b0, wa, wb, sh0, acc);
   pin_acc(acc);
-  interleave_first();
+  interleave_half<8, 4>();
 
   // LDS traffic done (the loads in flight stay in flight), then a plain
   // s_barrier: the workgroup fence of __syncthreads would make the
@@ -258,16 +260,16 @@ __device__ __forceinline__ void k_step(const Fetch& f, uint8_t* lds, int ks, int
   __builtin_amdgcn_s_waitcnt(0xC07F);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  fetch_step(f, ks + 3, nk, ca, cb, sc);
   // the next step's first fragments and scale words (a clamped, unused
   // read after the last step)
   const uint8_t* sn = lds + ((ks + 1) & 1) * kStageBytes;
   uint32_t wan[4], wbn[4];
   load_scales(lds, ks + 1, rowa, rowb, wan, wbn);
   load_frags(sn, oa0, ob0, a0, b0);
+  fetch_codes(f.rb, f.code_b, ks + 3, nk, cb);
   mma_half(a1, b1, wa, wb, sh1, acc);
   pin_acc(acc);
-  interleave_second<8>();
+  interleave_half<12, 4>();
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     wa[t] = wan[t];
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
 
   // Prologue: scale group 0 (all eight pieces) and step 0 stored; steps 1
   // and 2 in flight in the two register sets.
-  u32x4 ca0[4], cb0[4], sc0, ca1[4], cb1[4], sc1;
+  u32x4 ca0[4], cb0[4], sc0 = {}, ca1[4], cb1[4], sc1 = {};
   {
     u32x4 s0[8];
 #pragma unroll
@@ -338,15 +340,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
       s0[4 + q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                 f.rsb, (int)scale_off(f, min(f.row_b + 16 * q, f.last_b), 0), 0, 0));
     }
-    fetch_step(f, 0, nk, ca0, cb0, sc0);
+    fetch_codes(f.ra, f.code_a, 0, nk, ca0);
+    fetch_codes(f.rb, f.code_b, 0, nk, cb0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       store_scale_piece(lds, 0, i >> 2, wave * 64 + (i & 3) * 16 + (lane >> 2), s0[i]);
-    store_step(lds, 0, st_off, ca0, cb0, sc0);
+    store_codes(lds, 0, st_off, ca0, cb0);
   }
-  fetch_step(f, 1, nk, ca1, cb1, sc1);
+  // steps 0 .. 2 carry no scale piece
+  fetch_codes(f.ra, f.code_a, 1, nk, ca1);
+  fetch_codes(f.rb, f.code_b, 1, nk, cb1);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // step 0's stores done before set 0 is refilled
-  fetch_step(f, 2, nk, ca0, cb0, sc0);
+  fetch_codes(f.ra, f.code_a, 2, nk, ca0);
+  fetch_codes(f.rb, f.code_b, 2, nk, cb0);
   __syncthreads();
 
   u32x4 a0[4], b0[4], a1[4], b1[4];  // first- and second-half fragments
