@@ -72,3 +72,29 @@ def quantize_both(x: np.ndarray, fmt, axis="row", rounding="rtne", rht=False, rh
     elif fmt not in fp4.MX:
         assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots), "tensor scale " + tag
     return c, s, ts, (oc, osc, ots)
+
+
+def gemm_bound(a_codes, a_scales, b_codes, b_scales, M, N, K):
+    """Binary32 summation bound of an MXFP4 GEMM against the exact product:
+    K * 2^-23 * (|A| . |B|^T) (each product of two codes and two power-of-two
+    scales is exact; only the order and rounding of the K-term sum differ)."""
+    a = np.abs(oracle.dequantize(a_codes, a_scales, None, M, K, "mxfp4", "row")).astype(np.float64)
+    b = np.abs(oracle.dequantize(b_codes, b_scales, None, N, K, "mxfp4", "row")).astype(np.float64)
+    return K * 2.0 ** -23 * (a @ b.T)
+
+
+def check_gemm(c_gpu, a, sa, b, sb, M, N, K, dtype, tag):
+    """GPU GEMM output against the oracle's float64 product within
+    gemm_bound, plus half a BF16 unit (at most 2^-8 of |C|) for BF16."""
+    ref = oracle.gemm_mx(a, sa, b, sb, M, N, K)
+    bound = gemm_bound(a, sa, b, sb, M, N, K)
+    if dtype == torch.bfloat16:
+        got = (to_host(c_gpu).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bound = bound * (1 + 2.0 ** -7) + 2.0 ** -8 * np.abs(ref)
+    else:
+        got = to_host(c_gpu).astype(np.float64)
+    err = np.abs(got - ref)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "%s: %d entries out of bound, first %s: gpu %r ref %r bound %r" % (
+        tag, len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])],
+        bound[tuple(bad[0])])

@@ -12,30 +12,13 @@ import torch
 import block_scaled_bit_fp4_amd as fp4
 import oracle
 import workloads
-from tests.gpu_util import DEV, note, to_device, to_host
+from tests.gpu_util import DEV, check_gemm, note, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
 
-def _bound(a_codes, a_scales, b_codes, b_scales, M, N, K):
-    a = np.abs(oracle.dequantize(a_codes, a_scales, None, M, K, "mxfp4", "row")).astype(np.float64)
-    b = np.abs(oracle.dequantize(b_codes, b_scales, None, N, K, "mxfp4", "row")).astype(np.float64)
-    return K * 2.0 ** -23 * (a @ b.T)
-
-
 def _check(c_gpu, a, sa, b, sb, M, N, K, dtype, tag):
-    ref = oracle.gemm_mx(a, sa, b, sb, M, N, K)
-    bound = _bound(a, sa, b, sb, M, N, K)
-    if dtype == torch.bfloat16:
-        got = (to_host(c_gpu).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        bound = bound * (1 + 2.0 ** -7) + 2.0 ** -8 * np.abs(ref)
-    else:
-        got = to_host(c_gpu).astype(np.float64)
-    err = np.abs(got - ref)
-    bad = np.argwhere(err > bound)
-    assert bad.size == 0, "%s: %d entries out of bound, first %s: gpu %r ref %r bound %r" % (
-        tag, len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])],
-        bound[tuple(bad[0])])
+    check_gemm(c_gpu, a, sa, b, sb, M, N, K, dtype, tag)
 
 
 # K = 128 x (1, 4, 9, 21, 33) steps: one step, whole and partial 16-step

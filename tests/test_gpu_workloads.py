@@ -9,7 +9,7 @@ import torch
 import block_scaled_bit_fp4_amd as fp4
 import oracle
 import workloads
-from tests.gpu_util import assert_bytes_equal, note, quantize_both, to_device, to_host
+from tests.gpu_util import assert_bytes_equal, check_gemm, note, quantize_both, to_device, to_host
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -31,9 +31,45 @@ def _dual_full(x, call):
             assert to_host(t).view(np.uint32)[0] == np.float32(ots).view(np.uint32)
 
 
+def _gemm_full(key, w):
+    """A GEMM workload: every operand quantization byte-exact at full size,
+    then each GEMM in the benchmark's configuration (BF16 out) with 256
+    sampled outputs against the oracle's per-element dot products."""
+    cache, ops = {}, {}
+    for gm in w.gemms:
+        for op in (gm.a, gm.b):
+            if op in ops:
+                continue
+            t, axis, rounding, sr_seed = op
+            if t not in cache:
+                note("generating %s/%s" % (key, t))
+                cache[t] = w.make(t)
+            note("workload %s: %s %s %s %s rht=%s" % (key, t, w.fmt, axis, rounding, w.rht))
+            # quantize_both compares codes and scales byte for byte
+            c, s, _ts, (oc, osc, _ots) = quantize_both(cache[t], w.fmt, axis, rounding, w.rht, 0,
+                                                       sr_seed)
+            ops[op] = (c, s, oc, osc)
+    rng = np.random.default_rng(7)
+    for gm in w.gemms:
+        (ac, asc, oac, oasc), (bc, bsc, obc, obsc) = ops[gm.a], ops[gm.b]
+        M, N, K = ac.shape[0], bc.shape[0], 2 * ac.shape[1]
+        note("workload %s: %s GEMM %dx%dx%d" % (key, gm.name, M, N, K))
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
+        fp4.gemm_mx(ac, asc, bc, bsc, out=out)
+        torch.cuda.synchronize()
+        ms, ns = rng.integers(0, M, 16), rng.integers(0, N, 16)
+        sub = out[torch.tensor(ms, device=out.device)][:, torch.tensor(ns, device=out.device)]
+        check_gemm(sub, oac[ms], oasc[ms], obc[ns], obsc[ns], 16, 16, K, torch.bfloat16,
+                   "%s %s sampled" % (key, gm.name))
+        del out
+
+
 @pytest.mark.parametrize("key", list(workloads.WORKLOADS))
 def test_workload_full_size(key):
     w = workloads.workload(key)
+    if isinstance(w, workloads.GemmWorkload):
+        _gemm_full(key, w)
+        return
     cache = {}
     for call in w.calls:
         if call.tensor not in cache:
