@@ -10,10 +10,11 @@ there is no CPU fallback, and importing the library fails loudly when
 Formats: ``"nvfp4"`` (E2M1, 16-element blocks, E4M3 scale, FP32 tensor
 scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
 (uniform 0..7 grid, 16-element blocks, E4M3 scale, FP32 tensor scale),
-``"mxfp4_oas"`` (MXFP4 with overflow-aware E8M0 scales).  NVFP4 and the
-uniform grid also take double-block scales (``outer=True``): one FP32 outer
-scale per 128 elements of each row of the quantized operand instead of the
-tensor scale.
+``"mxfp4_oas"`` (MXFP4 with overflow-aware E8M0 scales), ``"e2m1_cap2"``
+(E2M1 cut at magnitude 2, NVFP4's scaling with the block amax mapped to 2).
+The two-level formats (NVFP4, the uniform grid, the cut E2M1) also take
+double-block scales (``outer=True``): one FP32 outer scale per 128 elements
+of each row of the quantized operand instead of the tensor scale.
 """
 from __future__ import annotations
 
@@ -26,8 +27,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4.so")
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16}
 MX = ("mxfp4", "mxfp4_oas")
 OUTER = 128  # elements per outer scale (double-block mode)
 TS_COMPUTE, TS_GIVEN, TS_OUTER128 = 0, 1, 2
@@ -162,7 +163,7 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
              workspace: Optional[torch.Tensor] = None, stream=None, outer: bool = False):
     """Quantize a BF16/FP32 device matrix.  Returns (codes, scales, tensor_scale).
 
-    ``tensor_scale``: None computes the NVFP4/UFP4 tensor scale from the data;
+    ``tensor_scale``: None computes the two-level tensor scale from the data;
     a float or one-element float32 device tensor supplies it.  The returned
     tensor scale is a one-element float32 device tensor (None for the MX
     formats).  ``outer=True`` selects double-block scales: the third result

@@ -59,7 +59,7 @@ bool outer_scales(const fp4_params* p) {
 fp4_status check_params(const fp4_params* p) {
   if (!p) return FP4_ERR_NULL;
   if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4 &&
-      p->format != FP4_MXFP4_OAS)
+      p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2)
     return FP4_ERR_FORMAT;
   if (p->block != (is_mx(p->format) ? 32 : 16)) return FP4_ERR_FORMAT;
   if (p->axis != FP4_AXIS_ROW && p->axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
@@ -212,8 +212,9 @@ fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int6
   q.scales_col = scales_col;
   q.ts_col = ts_col;
   q.workspace = static_cast<float*>(workspace);
-  const hipError_t e = p->format == FP4_NVFP4 ? fp4_launch_quantize_dual_nvfp4(q, s)
-                                              : fp4_launch_quantize_dual_ufp4(q, s);
+  const hipError_t e = p->format == FP4_NVFP4   ? fp4_launch_quantize_dual_nvfp4(q, s)
+                       : p->format == FP4_UFP4 ? fp4_launch_quantize_dual_ufp4(q, s)
+                                               : fp4_launch_quantize_dual_e2m1_cap2(q, s);
   return finish(e, s);
 }
 
@@ -311,6 +312,7 @@ hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
     case FP4_NVFP4: return fp4_launch_quantize_nvfp4(q, s);
     case FP4_MXFP4: return fp4_launch_quantize_mxfp4(q, s);
     case FP4_UFP4: return fp4_launch_quantize_ufp4(q, s);
+    case FP4_E2M1_CAP2: return fp4_launch_quantize_e2m1_cap2(q, s);
     default: return fp4_launch_quantize_mxfp4_oas(q, s);
   }
 }

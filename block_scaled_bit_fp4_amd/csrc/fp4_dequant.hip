@@ -523,6 +523,7 @@ hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
     case kNVFP4: return dq_outer<kNVFP4>(q, s);
     case kMXFP4: return dq_outer<kMXFP4>(q, s);
     case kUFP4: return dq_outer<kUFP4>(q, s);
+    case kCAP2: return dq_outer<kNVFP4>(q, s);  // E2M1 codes, E4M3 scales: decoded as NVFP4
     default: return dq_outer<kMXOAS>(q, s);
   }
 }

@@ -19,7 +19,10 @@
 
 namespace fp4dev {
 
-enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3 };
+// kCAP2: E2M1 codes cut at magnitude 2 (levels 0, .5, 1, 1.5, 2, equally
+// spaced), NVFP4's two-level scaling with the block amax mapped to 2 -- the
+// range-restricted E2M1 of [UFP4] Metodologia 2 (Ablacion).
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4 };
 // Tensor-scale modes of the two-level formats: computed from the data,
 // given by the caller, or one outer scale per kOuter elements of an A-row.
 enum : int { kTsCompute = 0, kTsGiven = 1, kTsOuter = 2 };
@@ -225,6 +228,7 @@ __device__ __forceinline__ float grid_level(uint32_t k) {
 // [2,4), 2 above 4) and the even code is the even multiple of the spacing,
 // so rint(m / spacing) decides; values past 6 saturate.
 // Uniform: rint(m), saturating at 7.
+// The cut E2M1 saturates at code 4 (magnitude 2).
 template <int FMT>
 __device__ __forceinline__ uint32_t round_rtne_sw(float m) {
   if constexpr (FMT == kUFP4) {
@@ -233,7 +237,7 @@ __device__ __forceinline__ uint32_t round_rtne_sw(float m) {
     const bool lo = m < 2.0f, mid = m < 4.0f;
     const float q = lo ? m * 2.0f : (mid ? m : m * 0.5f);
     const float off = lo ? 0.0f : (mid ? 2.0f : 4.0f);
-    return (uint32_t)fminf(__builtin_rintf(q) + off, 7.0f);
+    return (uint32_t)fminf(__builtin_rintf(q) + off, FMT == kCAP2 ? 4.0f : 7.0f);
   }
 }
 
@@ -254,12 +258,14 @@ __device__ __forceinline__ uint32_t round_sr_sw(float m, uint32_t u16) {
   }
   const float fl = __builtin_floorf(q);
   const float up = (q - fl) * 4194304.0f >= (float)(u16 * 64u + 1u) ? 1.0f : 0.0f;
-  return (uint32_t)fminf(fl + off + up, 7.0f);
+  return (uint32_t)fminf(fl + off + up, FMT == kCAP2 ? 4.0f : 7.0f);
 }
 
 // G, the largest level, in the two-level tensor scale amax / (G * 448).
 template <int FMT>
-__device__ __forceinline__ float grid_max() { return FMT == kUFP4 ? 7.0f : 6.0f; }
+__device__ __forceinline__ float grid_max() {
+  return FMT == kUFP4 ? 7.0f : (FMT == kCAP2 ? 2.0f : 6.0f);
+}
 
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {

@@ -205,8 +205,18 @@ __device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a, uint32_t b, uin
 
 // Encode 8 scaled values (all finite) into one word of 4-bit codes.
 template <int FMT, bool SR>
-__device__ __forceinline__ uint32_t encode8_fast(const float* v, const uint32_t (&r)[4]) {
+__device__ __forceinline__ uint32_t encode8_fast(const float* v_in, const uint32_t (&r)[4]) {
   uint32_t word = 0;
+  // The cut E2M1 saturates at 2: clamp first (sign, and the sign of zero,
+  // kept), then the E2M1 converts below see no value past their level 2
+  // except 2 itself.  Other formats code the values as they are.
+  float vc[8];
+  const float* v = v_in;
+  if constexpr (FMT == kCAP2) {
+#pragma unroll
+    for (int l = 0; l < 8; ++l) vc[l] = fminf(fmaxf(v_in[l], -2.0f), 2.0f);
+    v = vc;
+  }
   if constexpr (FMT == kUFP4 && !SR) {
     // Uniform grid, round to nearest even: adding 2^23 to min(m, 7) rounds
     // it to an integer (binary32 addition, ties to even) held in the low

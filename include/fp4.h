@@ -59,7 +59,7 @@
  *  - codes: rows_A x (W / 2) bytes; byte (i, j/2) holds A[i][j], even j in
  *    the low nibble.  rows_A = rows (ROW) or cols (COL); W = cols or rows.
  *  - scales: rows_A x (W / B) bytes.
- *  - tensor_scale (NVFP4 / UFP4 only): one float; with FP4_TS_OUTER128,
+ *  - tensor_scale (two-level formats only): one float; with FP4_TS_OUTER128,
  *    rows_A x (W / 128) floats, row-major (requires W % 128 == 0).
  *
  * Ownership and concurrency: the library allocates no memory and keeps no
@@ -98,6 +98,13 @@ typedef int32_t fp4_status;
 #define FP4_MXFP4 1     /* E2M1, 32-element blocks, E8M0 scale */
 #define FP4_UFP4 2      /* uniform 0..7 grid, 16-element blocks, E4M3 + FP32 */
 #define FP4_MXFP4_OAS 3 /* MXFP4 with overflow-aware E8M0 scales */
+/* E2M1 with its range cut at 2 ("Replanteamiento del Sesgo de Contraccion
+ * en el Preentrenamiento de LLM en FP4", Metodologia 2, Ablacion: limiting
+ * E2M1's maximum to emulate a uniform grid): codes 0..4 only (levels 0, .5,
+ * 1, 1.5, 2, equally spaced), values past 2 saturate at 2; NVFP4's
+ * 16-element blocks, E4M3 scale and FP32 tensor (or outer) scale, with the
+ * block amax mapped to 2 (s_t = amax / (2 * 448)).  Dequantizes as NVFP4. */
+#define FP4_E2M1_CAP2 4
 
 #define FP4_AXIS_ROW 0 /* quantize along rows of x */
 #define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
@@ -113,8 +120,8 @@ typedef int32_t fp4_status;
 #define FP4_TS_OUTER128 2 /* double block: one outer scale per 128 elements */
 
 typedef struct {
-  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 / FP4_MXFP4_OAS */
-  int32_t block;    /* 16 for NVFP4 and UFP4, 32 for MXFP4 and MXFP4_OAS */
+  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 / FP4_MXFP4_OAS / FP4_E2M1_CAP2 */
+  int32_t block;    /* 16 for NVFP4, UFP4 and E2M1_CAP2, 32 for MXFP4 and MXFP4_OAS */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
@@ -130,7 +137,8 @@ size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
 
 /* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
  * scales (layouts above).  tensor_scale is written (COMPUTE, OUTER128) or
- * read (GIVEN) for NVFP4/UFP4 and may be NULL for the MX formats.
+ * read (GIVEN) for the two-level formats (NVFP4, UFP4, E2M1_CAP2) and may
+ * be NULL for the MX formats.
  * workspace must hold fp4_workspace_bytes() bytes.  Requirements: block
  * matches the format; W divisible by the block (and by 16 when rht, by 128
  * with OUTER128); ld >= cols; x, codes, scales 16-byte aligned; ld *
@@ -151,8 +159,8 @@ size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p)
  * The forward and the weight-gradient GEMM both need an operand this way
  * (TetraJet-v2 page, Riepilogo Tecnico 2.A: the 1x16 groups realigned for
  * the transposed matrix; the [UFP4] page, Metodologia 2: quantized
- * operands of all three GEMMs).  With BF16 input, the NVFP4 or uniform
- * grid format, rows and cols multiples of 128 and 256 * ld < 2^31 (a
+ * operands of all three GEMMs).  With BF16 input, a two-level format
+ * (NVFP4, uniform grid, cut E2M1), rows and cols multiples of 128 and 256 * ld < 2^31 (a
  * 128-row tile's byte extent), x is read once per pass
  * (once in all with a given tensor scale or outer scales, twice with
  * computed tensor scales instead of four times); otherwise the call runs

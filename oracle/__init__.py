@@ -38,11 +38,11 @@ _SO = os.path.join(_HERE, "libfp4_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4}
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
-GRIDS = {"e2m1": 0, "uniform": 1}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32}
+GRIDS = {"e2m1": 0, "uniform": 1, "e2m1_cap2": 2}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16}
 TS_MODES = {"compute": 0, "given": 1, "outer128": 2}
 OUTER = 128  # outer block of the double-block mode
 MX = ("mxfp4", "mxfp4_oas")

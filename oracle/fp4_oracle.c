@@ -30,6 +30,13 @@ static const double* grid_levels(int grid) {
   return grid == FP4R_GRID_UNIFORM ? kUniform : kE2M1;
 }
 
+/* The largest code a grid rounds to: 7, or 4 (magnitude 2) for the E2M1
+ * grid cut at 2 ([UFP4] Ablacion: E2M1 with its maximum limited, which the
+ * page tried as an emulation of a uniform grid; cut at 2 the levels 0, .5,
+ * 1, 1.5, 2 are equally spaced).  Codes above the top still decode through
+ * the E2M1 table. */
+static int grid_top(int grid) { return grid == FP4R_GRID_E2M1_CAP2 ? 4 : 7; }
+
 float fp4r_level(int grid, int k) { return (float)grid_levels(grid)[k & 7]; }
 
 /* ------------------------------------------------------------------------
@@ -192,8 +199,8 @@ int fp4r_e8m0_exponent_oas(float amax) {
 
 /* ------------------------------------------------------------------------
  * Rounding a magnitude m >= 0 to a grid.  k is the bin with
- * L[k] <= m < L[k+1]; m >= L[7] saturates at 7 ([MXFP4] 2.A: saturation at
- * the FP4 limit).  RTNE compares m with the exact midpoint, ties to the even
+ * L[k] <= m < L[k+1]; m >= L[top] saturates at the grid's top code (7, or 4
+ * for the cut E2M1; [MXFP4] 2.A: saturation at the FP4 limit).  RTNE compares m with the exact midpoint, ties to the even
  * code ([UFP4] Metodologia 1: RTNE bins).  SR rounds up with probability
  * p = (m - L[k]) / (L[k+1] - L[k]) using a 16-bit draw ([TJ2] 2.A:
  * stochastic rounding so that E[round(x)] = x; [UFP4] Metodologia 2: SR on
@@ -203,17 +210,18 @@ int fp4r_e8m0_exponent_oas(float amax) {
  * p * 2^22 < 1), which is within one of p * 2^16: E[round(m)] equals m to
  * within 2^-16 of a bin width.
  * ---------------------------------------------------------------------- */
-static int bin_below(double m, const double* L) {
+static int bin_below(double m, const double* L, int top) {
   int k = 0;
-  while (k < 7 && L[k + 1] <= m) ++k;
+  while (k < top && L[k + 1] <= m) ++k;
   return k;
 }
 
 int fp4r_round_rtne(float mf, int grid) {
   const double* L = grid_levels(grid);
+  const int top = grid_top(grid);
   double m = (double)mf;
-  if (m >= L[7]) return 7;
-  int k = bin_below(m, L);
+  if (m >= L[top]) return top;
+  int k = bin_below(m, L, top);
   double mid = 0.5 * (L[k] + L[k + 1]);
   if (m < mid) return k;
   if (m > mid) return k + 1;
@@ -222,9 +230,10 @@ int fp4r_round_rtne(float mf, int grid) {
 
 int fp4r_round_sr(float mf, int grid, uint32_t u16) {
   const double* L = grid_levels(grid);
+  const int top = grid_top(grid);
   double m = (double)mf;
-  if (m >= L[7]) return 7;
-  int k = bin_below(m, L);
+  if (m >= L[top]) return top;
+  int k = bin_below(m, L, top);
   double p = (m - L[k]) / (L[k + 1] - L[k]);
   /* p * 2^22 and 64 * u16 + 1 are exact in binary64 */
   return (p * 4194304.0 >= 64.0 * (double)(u16 & 0xFFFFu) + 1.0) ? k + 1 : k;
@@ -260,12 +269,15 @@ static int64_t a_index(int axis, int64_t i, int64_t j, int64_t ld) {
 }
 
 static int grid_of(int format) {
-  return format == FP4R_UFP4 ? FP4R_GRID_UNIFORM : FP4R_GRID_E2M1;
+  if (format == FP4R_UFP4) return FP4R_GRID_UNIFORM;
+  return format == FP4R_E2M1_CAP2 ? FP4R_GRID_E2M1_CAP2 : FP4R_GRID_E2M1;
 }
 
-/* G, the largest grid level, used by the two-level tensor scale. */
+/* G, the largest grid level, used by the two-level tensor scale and the
+ * block scale's target. */
 static float grid_max(int format) {
-  return format == FP4R_UFP4 ? 7.0f : 6.0f;
+  if (format == FP4R_UFP4) return 7.0f;
+  return format == FP4R_E2M1_CAP2 ? 2.0f : 6.0f;
 }
 
 static int is_mx(int format) {
@@ -275,7 +287,7 @@ static int is_mx(int format) {
 static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
                         int64_t ld) {
   if (!p) return -1;
-  if (p->format < 0 || p->format > 3) return -1;
+  if (p->format < 0 || p->format > 4) return -1;
   if (is_mx(p->format) ? p->block != 32 : p->block != 16) return -1;
   if (!is_mx(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
   if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;

@@ -44,22 +44,25 @@ extern "C" {
 #endif
 
 /* enumerations (values mirror the product's C-ABI by convention only) */
-enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3 };
+/* FP4R_E2M1_CAP2: E2M1 codes restricted to magnitudes <= 2 ([UFP4]
+ * Metodologia 2, Ablacion: an E2M1 whose range is cut to emulate a uniform
+ * grid), NVFP4's two-level scaling with the block amax mapped to 2. */
+enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3, FP4R_E2M1_CAP2 = 4 };
 enum { FP4R_ROW = 0, FP4R_COL = 1 };
 enum { FP4R_RTNE = 0, FP4R_SR = 1 };
 enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
 enum { FP4R_TS_COMPUTE = 0, FP4R_TS_GIVEN = 1, FP4R_TS_OUTER128 = 2 };
 /* Outer blocks of the double-block mode ([TJ2] 2.A): 128 elements. */
 enum { FP4R_OUTER = 128 };
-enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1 };
+enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1, FP4R_GRID_E2M1_CAP2 = 2 };
 
 typedef struct {
-  int32_t format;   /* FP4R_NVFP4 / FP4R_MXFP4 / FP4R_UFP4 / FP4R_MXFP4_OAS */
-  int32_t block;    /* 16 (NVFP4, UFP4) or 32 (MXFP4, MXFP4_OAS) */
+  int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 */
+  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2) or 32 (MXFP4, MXFP4_OAS) */
   int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
   int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4R_TS_COMPUTE, _GIVEN or _OUTER128 (NVFP4/UFP4) */
+  int32_t ts_mode;  /* FP4R_TS_COMPUTE, _GIVEN or _OUTER128 (two-level formats) */
   uint64_t rht_seed;
   uint64_t sr_seed;
 } fp4r_params;

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 FUSED = [(128, 128), (256, 384), (384, 256), (512, 128)]
 SPLIT = [((96, 160), "bf16"), ((128, 256), "f32"), ((1056, 352), "bf16")]
-COMBOS = list(itertools.product(["nvfp4", "ufp4"], ["rtne", "sr"], [False, True],
+COMBOS = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2"], ["rtne", "sr"], [False, True],
                                 ["compute", "given", "outer"]))
 
 

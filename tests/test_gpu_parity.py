@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352), (48, 80)]
 KINDS = workloads.SMALL_KINDS
 
-COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas"], ["row", "col"],
+COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas", "e2m1_cap2"], ["row", "col"],
                                 ["rtne", "sr"], [False, True], ["bf16", "f32"]))
 
 # Double-block (outer scale per 128) shapes: W % 128 == 0 on the axis used.
@@ -32,7 +32,7 @@ COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas"], ["row",
 # tiles plus a right strip of 8 columns and a bottom strip of 128 rows;
 # (384, 1152) row: nine outer pieces per row; (256, 384): whole tiles.
 OUTER_SHAPES = [(128, 256), (640, 200), (384, 1152), (256, 384)]
-OUTER_COMBOS = list(itertools.product(["nvfp4", "ufp4"], ["row", "col"], ["rtne", "sr"],
+OUTER_COMBOS = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2"], ["row", "col"], ["rtne", "sr"],
                                       [False, True], ["bf16", "f32"]))
 
 
@@ -102,7 +102,7 @@ def test_every_kind_nvfp4_rht(kind):
         quantize_both(x, "ufp4", "col", rounding, True, 1, 1)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "e2m1_cap2"])
 def test_given_tensor_scale(fmt):
     x = _input("t3", (128, 256), 3, "bf16")
     # 1e-39 (subnormal): 1/d overflows, blocks take the per-element careful
@@ -125,7 +125,7 @@ def test_poison_and_determinism():
 def test_col_equals_row_of_transpose_on_gpu():
     x = _input("t3", (256, 160), 4, "bf16")
     xt = np.ascontiguousarray(x.T)
-    for fmt in ("nvfp4", "mxfp4", "ufp4"):
+    for fmt in ("nvfp4", "mxfp4", "ufp4", "e2m1_cap2"):
         note("transpose %s" % fmt)
         c1, s1, t1 = fp4.quantize(to_device(x), fmt, "col", "sr", True, 6, 8)
         c2, s2, t2 = fp4.quantize(to_device(xt), fmt, "row", "sr", True, 6, 8)
@@ -161,7 +161,7 @@ def test_strided_input():
     assert_bytes_equal(to_host(s), osc, "scales")
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
 @pytest.mark.parametrize("rounding", ["rtne", "sr"])
 def test_column_axis_odd_column_count(fmt, rounding):
     """cols odd (one column per lane) through a strided view, ld = 40."""
@@ -195,7 +195,7 @@ def test_empty_and_single_block():
 def test_all_zero_tensor():
     x = np.zeros((64, 64), dtype=np.float32)
     x[3, 5] = -0.0
-    for fmt in ("nvfp4", "mxfp4", "ufp4"):
+    for fmt in ("nvfp4", "mxfp4", "ufp4", "e2m1_cap2"):
         note("zeros %s" % fmt)
         quantize_both(x, fmt, "row", "sr", True, 0, 0)
         quantize_both(x, fmt, "col", "rtne", False, 0, 0)
@@ -222,7 +222,7 @@ def _same_or_both_nan(got, want, bits, tag):
     assert np.array_equal(g[~gn], w[~wn]), "values " + tag
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "e2m1_cap2"])
 def test_dequant_arbitrary_codes_and_scales(fmt):
     """Dequantize of random codes with every scale byte and tensor scales
     far from 1: decoded block scales below 2^-100, above 2^100 and infinite

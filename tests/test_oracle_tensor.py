@@ -80,15 +80,16 @@ def test_tensor_scale_definition_and_top_block():
 def test_on_grid_blocks_round_trip_exactly():
     rng = np.random.default_rng(8)
     e4 = np.arange(0x08, 0x7F)  # normal E4M3 bytes
-    for fmt, levels in (("nvfp4", E2M1), ("ufp4", UNI)):
+    for fmt, levels in (("nvfp4", E2M1), ("ufp4", UNI), ("e2m1_cap2", E2M1[:5])):
         G = levels[-1]
+        top = len(levels) - 1
         s_t = np.float32(2.0 ** -10)
         rows = []
         for _ in range(64):
             S = int(rng.choice(e4))
             d = np.float32(s_t * np.float32(oracle.e4m3_decode(S)))
-            k = rng.integers(0, 8, 16)
-            k[rng.integers(0, 16)] = 7  # the block amax is G * d
+            k = rng.integers(0, top + 1, 16)
+            k[rng.integers(0, 16)] = top  # the block amax is G * d
             sgn = rng.choice([-1.0, 1.0], 16)
             rows.append((sgn * levels[k] * np.float64(d)).astype(np.float32))
         x = np.stack(rows)
@@ -108,7 +109,7 @@ def test_on_grid_blocks_round_trip_exactly():
 
 
 # ------------------------------------------------------------ transpose invariant
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
 @pytest.mark.parametrize("rounding", ["rtne", "sr"])
 @pytest.mark.parametrize("rht", [False, True])
 def test_col_equals_row_of_transpose(fmt, rounding, rht):
@@ -135,10 +136,17 @@ def _nearest_tie_even(value: float, cands: np.ndarray) -> int:
     return int(even[0] if even else idx[0])
 
 
+def _levels(fmt):
+    """A format's rounding levels: the uniform grid, E2M1, or E2M1 cut at 2."""
+    if fmt == "ufp4":
+        return UNI
+    return E2M1[:5] if fmt == "e2m1_cap2" else E2M1
+
+
 def _brute_quantize(x: np.ndarray, fmt: str):
     """Independent scalar quantizer (no RHT, RTNE, row axis) for tiny inputs."""
     R, C = x.shape
-    levels = UNI if fmt == "ufp4" else E2M1
+    levels = _levels(fmt)
     B = 32 if fmt == "mxfp4" else 16
     table = _e4m3_table()
     G = np.float32(levels[-1])
@@ -165,12 +173,13 @@ def _brute_quantize(x: np.ndarray, fmt: str):
                 k = 0
                 if d != 0 and yj != 0:
                     v = np.float32(yj * np.float32(np.float32(1) / d))
-                    k = 7 if abs(v) >= levels[-1] else _nearest_tie_even(abs(float(v)), levels)
+                    top = len(levels) - 1
+                    k = top if abs(v) >= levels[-1] else _nearest_tie_even(abs(float(v)), levels)
                 codes[i, b * B + j] = (8 if np.signbit(yj) else 0) | k
     return codes, scales, s_t
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
 @pytest.mark.parametrize("kind", ["normal", "wide_range", "tiny", "zeros_mixed", "grid_ties"])
 def test_brute_force_tiny(fmt, kind):
     x = workloads.small_case(kind, 3, 64, 21)
@@ -183,14 +192,14 @@ def test_brute_force_tiny(fmt, kind):
 
 
 # --------------------------------------------------------------------- properties
-@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "e2m1_cap2"])
 def test_each_code_is_a_nearest_level(fmt):
     x = workloads.to_bf16_bits(workloads.small_case("t3", 128, 256, 4))
     codes, scales, ts = oracle.quantize(x, fmt, rht=True, rht_seed=2)
     y = oracle.rht(x, "row", 2)
     xhat = oracle.dequantize(codes, scales, ts, 128, 256, fmt, rht=True, rht_seed=2)
     B = 32 if fmt == "mxfp4" else 16
-    levels = UNI if fmt == "ufp4" else E2M1
+    levels = _levels(fmt)
     if fmt == "mxfp4":
         d = np.ldexp(1.0, scales.astype(np.int64) - 127)
     else:

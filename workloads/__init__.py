@@ -137,10 +137,11 @@ def _w_mx_weight() -> Workload:
 def _w_up_proj() -> Workload:
     w = Workload("ufp4_vs_nvfp4_upproj_8192x28672",
                  "8192x28672 BF16 N(0, 0.02^2) with 0.01% entries at +-20 sigma: "
-                 "uniform grid vs NVFP4, both with RHT, RTNE, row axis")
+                 "uniform grid vs NVFP4 vs E2M1 cut at 2, all with RHT, RTNE, row axis")
     w.tensors["w"] = (8192, 28672, "bf16", lambda: weight_with_spikes(8192, 28672, 0))
     w.calls = [Call("w", "ufp4", "row", "rtne", True, 0, 0),
-               Call("w", "nvfp4", "row", "rtne", True, 0, 0)]
+               Call("w", "nvfp4", "row", "rtne", True, 0, 0),
+               Call("w", "e2m1_cap2", "row", "rtne", True, 0, 0)]
     return w
 
 
