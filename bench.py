@@ -37,8 +37,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
 KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/" + f for f in (
     "fp4_quantize.h", "fp4_quantize_nvfp4.hip", "fp4_quantize_mxfp4.hip", "fp4_quantize_ufp4.hip",
-    "fp4_quantize_mxfp4_oas.hip", "fp4_quantize_e2m1_cap2.hip", "fp4_dequant.hip", "fp4_tiles.h",
-    "fp4_device.h")]
+    "fp4_quantize_mxfp4_oas.hip", "fp4_quantize_e2m1_cap2.hip", "fp4_quantize_mxfp4_mbs.hip",
+    "fp4_dequant.hip", "fp4_tiles.h", "fp4_device.h")]
 MX = ("mxfp4", "mxfp4_oas")
 
 

@@ -11,7 +11,10 @@ Formats: ``"nvfp4"`` (E2M1, 16-element blocks, E4M3 scale, FP32 tensor
 scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
 (uniform 0..7 grid, 16-element blocks, E4M3 scale, FP32 tensor scale),
 ``"mxfp4_oas"`` (MXFP4 with overflow-aware E8M0 scales), ``"e2m1_cap2"``
-(E2M1 cut at magnitude 2, NVFP4's scaling with the block amax mapped to 2).
+(E2M1 cut at magnitude 2, NVFP4's scaling with the block amax mapped to 2),
+``"mxfp4_mbs"`` (static macro-block scaling: a macro scale with an 8-bit
+mantissa per 128 elements over 16-element E8M0 blocks; always returns the
+macro-scale array as its third result, as ``outer=True`` does).
 The two-level formats (NVFP4, the uniform grid, the cut E2M1) also take
 double-block scales (``outer=True``): one FP32 outer scale per 128 elements
 of each row of the quantized operand instead of the tensor scale.
@@ -27,8 +30,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4.so")
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
+         "mxfp4_mbs": 16}
+ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that exist only with 128-element macro scales
 MX = ("mxfp4", "mxfp4_oas")
 OUTER = 128  # elements per outer scale (double-block mode)
 TS_COMPUTE, TS_GIVEN, TS_OUTER128 = 0, 1, 2
@@ -172,7 +177,7 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    outer = bool(outer) and fmt not in MX
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
     given = tensor_scale is not None and not outer
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
     cshape, sshape = output_shapes(rows, cols, fmt, axis)
@@ -216,7 +221,7 @@ def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", r
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    outer = bool(outer) and fmt not in MX
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
     given = tensor_scale is not None and not outer
     p = make_params(fmt, "row", rounding, rht, rht_seed, sr_seed, given, outer)
     dev = x.device

@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["fp4_api.cpp", "fp4_quantize_nvfp4.hip", "fp4_quantize_mxfp4.hip",
            "fp4_quantize_ufp4.hip", "fp4_quantize_mxfp4_oas.hip", "fp4_quantize_e2m1_cap2.hip",
-           "fp4_dequant.hip", "fp4_gemm.hip"]
+           "fp4_quantize_mxfp4_mbs.hip", "fp4_dequant.hip", "fp4_gemm.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall",

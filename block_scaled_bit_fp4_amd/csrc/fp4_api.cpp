@@ -59,8 +59,9 @@ bool outer_scales(const fp4_params* p) {
 fp4_status check_params(const fp4_params* p) {
   if (!p) return FP4_ERR_NULL;
   if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4 &&
-      p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2)
+      p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2 && p->format != FP4_MXFP4_MBS)
     return FP4_ERR_FORMAT;
+  if (p->format == FP4_MXFP4_MBS && p->ts_mode != FP4_TS_OUTER128) return FP4_ERR_FORMAT;
   if (p->block != (is_mx(p->format) ? 32 : 16)) return FP4_ERR_FORMAT;
   if (p->axis != FP4_AXIS_ROW && p->axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
   if (p->rounding != FP4_RTNE && p->rounding != FP4_SR) return FP4_ERR_FORMAT;
@@ -212,9 +213,10 @@ fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int6
   q.scales_col = scales_col;
   q.ts_col = ts_col;
   q.workspace = static_cast<float*>(workspace);
-  const hipError_t e = p->format == FP4_NVFP4   ? fp4_launch_quantize_dual_nvfp4(q, s)
-                       : p->format == FP4_UFP4 ? fp4_launch_quantize_dual_ufp4(q, s)
-                                               : fp4_launch_quantize_dual_e2m1_cap2(q, s);
+  const hipError_t e = p->format == FP4_NVFP4        ? fp4_launch_quantize_dual_nvfp4(q, s)
+                       : p->format == FP4_UFP4      ? fp4_launch_quantize_dual_ufp4(q, s)
+                       : p->format == FP4_E2M1_CAP2 ? fp4_launch_quantize_dual_e2m1_cap2(q, s)
+                                                    : fp4_launch_quantize_dual_mxfp4_mbs(q, s);
   return finish(e, s);
 }
 
@@ -313,6 +315,7 @@ hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
     case FP4_MXFP4: return fp4_launch_quantize_mxfp4(q, s);
     case FP4_UFP4: return fp4_launch_quantize_ufp4(q, s);
     case FP4_E2M1_CAP2: return fp4_launch_quantize_e2m1_cap2(q, s);
+    case FP4_MXFP4_MBS: return fp4_launch_quantize_mxfp4_mbs(q, s);
     default: return fp4_launch_quantize_mxfp4_oas(q, s);
   }
 }

@@ -147,6 +147,8 @@ __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t,
   float d;
   if constexpr (is_mx(FMT)) {
     d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
+  } else if constexpr (FMT == kMBS) {
+    d = __builtin_ldexpf(in.so, (int)S - 127);  // macro scale times 2^e_b
   } else {
     d = S ? (OUTER ? in.so : s_t) * e4m3_decode(S) : 0.0f;
   }
@@ -491,6 +493,7 @@ hipError_t dq_inv(const DequantLaunch& q, hipStream_t s) {
 template <int FMT>
 hipError_t dq_outer(const DequantLaunch& q, hipStream_t s) {
   if constexpr (is_mx(FMT)) return dq_inv<FMT, false>(q, s);
+  else if constexpr (FMT == kMBS) return dq_inv<FMT, true>(q, s);  // macro scales only
   else return q.outer ? dq_inv<FMT, true>(q, s) : dq_inv<FMT, false>(q, s);
 }
 
@@ -524,6 +527,7 @@ hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
     case kMXFP4: return dq_outer<kMXFP4>(q, s);
     case kUFP4: return dq_outer<kUFP4>(q, s);
     case kCAP2: return dq_outer<kNVFP4>(q, s);  // E2M1 codes, E4M3 scales: decoded as NVFP4
+    case kMBS: return dq_outer<kMBS>(q, s);
     default: return dq_outer<kMXOAS>(q, s);
   }
 }

@@ -22,7 +22,10 @@ namespace fp4dev {
 // kCAP2: E2M1 codes cut at magnitude 2 (levels 0, .5, 1, 1.5, 2, equally
 // spaced), NVFP4's two-level scaling with the block amax mapped to 2 -- the
 // range-restricted E2M1 of [UFP4] Metodologia 2 (Ablacion).
-enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4 };
+// kMBS: MXFP4 with static macro-block scaling ([MXFP4] 2.B): a scale with
+// an 8-bit mantissa per 128-element macro block (carried like the outer
+// scales), 16-element blocks with E8M0 scales relative to it, E2M1 codes.
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4, kMBS = 5 };
 // Tensor-scale modes of the two-level formats: computed from the data,
 // given by the caller, or one outer scale per kOuter elements of an A-row.
 enum : int { kTsCompute = 0, kTsGiven = 1, kTsOuter = 2 };
@@ -197,6 +200,28 @@ __device__ __forceinline__ int e8m0_exponent(float amax) {
   const int e = ex - 129;
   return (ex == 0 || e < -127) ? -127 : e;
 }
+
+// x >= 0 finite, rounded to 8 fraction bits (9 significant bits from its
+// leading one), ties to even.  Normal: the low 15 significand bits go, with
+// the carry running into the exponent.  Subnormal: the bits below the
+// leading one's ninth go (none when it has at most nine).
+__device__ __forceinline__ float round8(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u >= 0x00800000u) {
+    u = (u + 0x3FFFu + ((u >> 15) & 1u)) & 0xFFFF8000u;
+  } else if (u != 0u) {
+    const int drop = (31 - __builtin_clz(u)) - 8;
+    if (drop > 0) {
+      const uint32_t lsb = (u >> drop) & 1u;
+      u = (u + (1u << (drop - 1)) - 1u + lsb) & ~((1u << drop) - 1u);
+    }
+  }
+  return __uint_as_float(u);
+}
+
+// MBS-Static macro scale ([MXFP4] 2.B, computed directly from the macro
+// block's maximum): round8(amax / 6), so the maximum lands on E2M1's 6.
+__device__ __forceinline__ float mbs_macro_scale(float amax) { return round8(amax / 6.0f); }
 
 // Overflow-aware MX exponent ([MXFP4] 2.A): amax / 2^e in (3.5, 7].  From
 // the standard e, amax / 2^e = 4 * 1.f lies in [4, 8); it exceeds 7 exactly

@@ -82,9 +82,11 @@ hipError_t fp4_launch_quantize_mxfp4(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_ufp4(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_mxfp4_oas(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_e2m1_cap2(const QuantLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_mxfp4_mbs(const QuantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_dual_nvfp4(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_dual_ufp4(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_quantize_dual_e2m1_cap2(const DualLaunch& q, hipStream_t s);
+hipError_t fp4_launch_quantize_dual_mxfp4_mbs(const DualLaunch& q, hipStream_t s);
 hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s);
 hipError_t fp4_launch_rht(const RhtLaunch& q, hipStream_t s);
 hipError_t fp4_launch_gemm_mx(const GemmLaunch& q, hipStream_t s);

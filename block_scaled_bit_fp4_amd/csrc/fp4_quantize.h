@@ -117,6 +117,14 @@ struct ScaleCtx {
 // or the given scale.  Fetched before the lane's first data loads: loads
 // complete in issue order, so the prologue then waits only for these and
 // not for the data behind them.
+// Scale of a 128-element outer piece from its amax: the double block's
+// amax / (G * 448) ([TJ2] 2.A), or the MBS-Static macro scale.
+template <int FMT>
+__device__ __forceinline__ float outer_scale(float amax) {
+  if constexpr (FMT == kMBS) return mbs_macro_scale(amax);
+  else return amax / (grid_max<FMT>() * 448.0f);
+}
+
 constexpr int kFetch = kAmaxPartials / kThreads;
 static_assert(kAmaxPartials % kThreads == 0, "partials per lane");
 struct ScaleFetch {
@@ -308,6 +316,13 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
     const int e = FMT == kMXOAS ? e8m0_exponent_oas(amax_b) : e8m0_exponent(amax_b);
     sbyte = (uint32_t)(e + 127);
     inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+  } else if constexpr (FMT == kMBS) {
+    // [MXFP4] 2.B static macro-block scaling: the MX exponent rule on
+    // amax_b / M (M, the macro scale, in c.s_t), d_b = M * 2^e_b
+    const int e = (c.s_t != 0.0f && amax_b != 0.0f) ? e8m0_exponent(amax_b / c.s_t) : -127;
+    sbyte = (uint32_t)(e + 127);
+    const float d = __builtin_ldexpf(c.s_t, e);
+    inv = d != 0.0f ? 1.0f / d : 0.0f;
   } else {
     sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
     if constexpr (TSM == kTsOuter) {
@@ -416,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
       }
       ao = group_max<LPO>(ao);
       ScaleCtx co;
-      co.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+      co.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
       co.den = co.s_t * grid_max<FMT>();
       if (w.minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + w.minor / LPO] = co.s_t;
 #pragma unroll
@@ -503,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
       }
 #pragma unroll
       for (int k = 0; k < C; ++k) {
-        co[k].s_t = (RHT ? ao[k] * 0.25f : ao[k]) / (grid_max<FMT>() * 448.0f);
+        co[k].s_t = outer_scale<FMT>(RHT ? ao[k] * 0.25f : ao[k]);
         co[k].den = co[k].s_t * grid_max<FMT>();
         a.ts_out[(col + k) * (a.W / kOuter) + blk0 * B / kOuter] = co[k].s_t;
       }
@@ -713,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
         // kOuter / B consecutive lanes hold the blocks of one 128-piece
         constexpr int LPO = kOuter / B;
         const float ao = group_max<LPO>(amax_t);
-        cc.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+        cc.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
         cc.den = cc.s_t * grid_max<FMT>();
         if (j % LPO == 0) a.ts_out[(ra0 + di) * (a.W / kOuter) + rb / LPO] = cc.s_t;
       }
@@ -904,7 +919,7 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
           if constexpr (TSM == kTsOuter) {
             // the 8 lanes of this parity hold the row's 128-piece
             const float ao = parity_max16(amax_t);
-            c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+            c.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
             c.den = c.s_t * grid_max<FMT>();
             if (seg < 2) a.ts_out_r[(row0 + dr) * (a.cols / kOuter) + c0 / kOuter] = c.s_t;
           }
@@ -954,7 +969,7 @@ __global__ __launch_bounds__(kThreads, 4) void dual_tile_kernel(const uint16_t* 
           ScaleCtx c = cc;
           if constexpr (TSM == kTsOuter) {
             const float ao = group_max<8>(amax_t);
-            c.s_t = (RHT ? ao * 0.25f : ao) / (grid_max<FMT>() * 448.0f);
+            c.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
             c.den = c.s_t * grid_max<FMT>();
             if (j == 0) a.ts_out_c[(ra0 + da) * (a.rows / kOuter) + r0 / kOuter] = c.s_t;
           }
@@ -1172,6 +1187,8 @@ template <int FMT, bool SR, bool RHT>
 hipError_t pick_tsm(const QuantLaunch& q, hipStream_t s) {
   if constexpr (is_mx(FMT)) {
     return pick_dtype<FMT, SR, RHT, kTsCompute>(q, s);  // no tensor scale
+  } else if constexpr (FMT == kMBS) {
+    return pick_dtype<FMT, SR, RHT, kTsOuter>(q, s);  // macro scales only
   } else {
     switch (q.ts_mode) {
       case kTsGiven: return pick_dtype<FMT, SR, RHT, kTsGiven>(q, s);
@@ -1222,6 +1239,7 @@ hipError_t launch_dual_t(const DualLaunch& q, hipStream_t s) {
 }
 template <int FMT, bool SR, bool RHT>
 hipError_t dual_pick_tsm(const DualLaunch& q, hipStream_t s) {
+  if constexpr (FMT == kMBS) return launch_dual_t<FMT, SR, RHT, kTsOuter>(q, s);
   switch (q.ts_mode) {
     case kTsGiven: return launch_dual_t<FMT, SR, RHT, kTsGiven>(q, s);
     case kTsOuter: return launch_dual_t<FMT, SR, RHT, kTsOuter>(q, s);

@@ -105,6 +105,15 @@ typedef int32_t fp4_status;
  * 16-element blocks, E4M3 scale and FP32 tensor (or outer) scale, with the
  * block amax mapped to 2 (s_t = amax / (2 * 448)).  Dequantizes as NVFP4. */
 #define FP4_E2M1_CAP2 4
+/* MXFP4 with static macro-block scaling ("Unveiling the Potential of
+ * Quantization with MXFP4", 2.B MBS-Static): for each 128-element piece of
+ * a row of A, a macro scale M = amax / 6 rounded to 8 fraction bits (FP32,
+ * stored where the double block stores its outer scales); for each
+ * 16-element block an E8M0 byte e_b + 127 with e_b = floor(log2(amax_b /
+ * M)) - 2 clamped to [-127, 127] (-127 when M or amax_b is 0), d_b = M *
+ * 2^e_b (binary32); E2M1 elements, saturating at 6.  Requires ts_mode =
+ * FP4_TS_OUTER128 and block 16. */
+#define FP4_MXFP4_MBS 5
 
 #define FP4_AXIS_ROW 0 /* quantize along rows of x */
 #define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
@@ -120,8 +129,8 @@ typedef int32_t fp4_status;
 #define FP4_TS_OUTER128 2 /* double block: one outer scale per 128 elements */
 
 typedef struct {
-  int32_t format;   /* FP4_NVFP4 / FP4_MXFP4 / FP4_UFP4 / FP4_MXFP4_OAS / FP4_E2M1_CAP2 */
-  int32_t block;    /* 16 for NVFP4, UFP4 and E2M1_CAP2, 32 for MXFP4 and MXFP4_OAS */
+  int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
+  int32_t block;    /* 16 for NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS; 32 for MXFP4, MXFP4_OAS */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */

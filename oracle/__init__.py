@@ -38,11 +38,13 @@ _SO = os.path.join(_HERE, "libfp4_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5}
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 GRIDS = {"e2m1": 0, "uniform": 1, "e2m1_cap2": 2}
-BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16}
+BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
+         "mxfp4_mbs": 16}
+ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that only exist with 128-element outer scales
 TS_MODES = {"compute": 0, "given": 1, "outer128": 2}
 OUTER = 128  # outer block of the double-block mode
 MX = ("mxfp4", "mxfp4_oas")
@@ -102,6 +104,10 @@ def lib():
         L.fp4r_e4m3_decode.restype = ctypes.c_float
         L.fp4r_e8m0_exponent.argtypes = [ctypes.c_float]
         L.fp4r_e8m0_exponent.restype = ctypes.c_int
+        L.fp4r_round8.argtypes = [ctypes.c_float]
+        L.fp4r_round8.restype = ctypes.c_float
+        L.fp4r_mbs_macro_scale.argtypes = [ctypes.c_float]
+        L.fp4r_mbs_macro_scale.restype = ctypes.c_float
         L.fp4r_e8m0_exponent_oas.argtypes = [ctypes.c_float]
         L.fp4r_e8m0_exponent_oas.restype = ctypes.c_int
         L.fp4r_round_rtne.argtypes = [ctypes.c_float, ctypes.c_int]
@@ -225,6 +231,7 @@ def quantize(x: np.ndarray, fmt="nvfp4", axis="row", rounding="rtne", rht=False,
     of outer scales."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
+    outer = outer or fmt in ALWAYS_OUTER
     mode = "outer128" if outer else ("given" if tensor_scale is not None else "compute")
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, mode)
     ra, w = (rows, cols) if axis == "row" else (cols, rows)
@@ -242,6 +249,16 @@ def quantize(x: np.ndarray, fmt="nvfp4", axis="row", rounding="rtne", rht=False,
     if fmt in MX:
         return codes, scales, None
     return codes, scales, (ts[:, : w // OUTER] if outer else float(ts[0]))
+
+
+def round8(x: float) -> float:
+    """A binary32 value rounded to 8 fraction bits (ties to even)."""
+    return float(lib().fp4r_round8(float(x)))
+
+
+def mbs_macro_scale(amax: float) -> float:
+    """MBS-Static macro scale of a 128-element piece: round8(amax / 6)."""
+    return float(lib().fp4r_mbs_macro_scale(float(amax)))
 
 
 def dequantize(codes, scales, tensor_scale, rows, cols, fmt="nvfp4", axis="row", rht=False,

@@ -172,6 +172,25 @@ uint8_t fp4r_e4m3_encode(float r) {
  * block amax lands near the top of the E2M1 range and saturates at 6).
  * e = floor(log2 amax) - 2, where 2 is E2M1's largest exponent.
  * ---------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------
+ * Macro-block scaling, static ([MXFP4] 2.B): a scale of higher precision
+ * (an 8-bit mantissa) per 128-element macro block, taken directly from the
+ * macro block's maximum, over the 16-element blocks.  Reading: M =
+ * round8(amax / 6) in binary32 (the largest element then sits at the top
+ * E2M1 level 6), kept as FP32; round8 rounds the significand to 8 fraction
+ * bits.  Done here in binary64, where every step is exact: scaling by a
+ * power of two into [256, 512) and rint (ties to even).
+ * ---------------------------------------------------------------------- */
+float fp4r_round8(float x) {
+  if (x == 0.0f || !isfinite(x)) return x;
+  int ex;
+  (void)frexp((double)x, &ex); /* |x| = f * 2^ex, f in [0.5, 1) */
+  double scaled = ldexp((double)x, 9 - ex); /* [256, 512) */
+  return (float)ldexp(rint(scaled), ex - 9);
+}
+
+float fp4r_mbs_macro_scale(float amax) { return fp4r_round8(amax / 6.0f); }
+
 int fp4r_e8m0_exponent(float amax) {
   if (!(amax > 0.0f)) return -127;
   int ex;
@@ -287,7 +306,8 @@ static int is_mx(int format) {
 static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
                         int64_t ld) {
   if (!p) return -1;
-  if (p->format < 0 || p->format > 4) return -1;
+  if (p->format < 0 || p->format > 5) return -1;
+  if (p->format == FP4R_MXFP4_MBS && p->ts_mode != FP4R_TS_OUTER128) return -1;
   if (is_mx(p->format) ? p->block != 32 : p->block != 16) return -1;
   if (!is_mx(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
   if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;
@@ -324,6 +344,8 @@ static void load_row(const void* x, int dt, int axis, int64_t ld, int64_t i,
  * ---------------------------------------------------------------------- */
 static float block_decode_scale(const fp4r_params* p, uint8_t sbyte, float s_t) {
   if (is_mx(p->format)) return ldexpf(1.0f, (int)sbyte - 127);
+  /* MBS: d_b = M * 2^e_b in binary32 (s_t holds the macro scale M) */
+  if (p->format == FP4R_MXFP4_MBS) return ldexpf(s_t, (int)sbyte - 127);
   if (sbyte == 0) return 0.0f;
   return s_t * fp4r_e4m3_decode(sbyte);
 }
@@ -332,6 +354,13 @@ static uint8_t block_scale_byte(const fp4r_params* p, float amax_b, float s_t) {
   if (p->format == FP4R_MXFP4) return (uint8_t)(fp4r_e8m0_exponent(amax_b) + 127);
   if (p->format == FP4R_MXFP4_OAS)
     return (uint8_t)(fp4r_e8m0_exponent_oas(amax_b) + 127);
+  /* MBS: the MX exponent rule applied to amax_b / M, so the block's largest
+   * element lands in [4, 8) times d_b = M * 2^e_b (e_b = 0 for the block
+   * holding the macro maximum: amax / M is then about 6). */
+  if (p->format == FP4R_MXFP4_MBS) {
+    if (s_t == 0.0f || amax_b == 0.0f) return 0x00;
+    return (uint8_t)(fp4r_e8m0_exponent(amax_b / s_t) + 127);
+  }
   if (s_t == 0.0f || amax_b == 0.0f) return 0x00;
   float den = s_t * grid_max(p->format);
   float r = amax_b / den;
@@ -420,7 +449,9 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
           float amax_o = 0.0f;
           for (int e = 0; e < FP4R_OUTER; ++e)
             if (fabsf(y[o * FP4R_OUTER + e]) > amax_o) amax_o = fabsf(y[o * FP4R_OUTER + e]);
-          tensor_scale[i * nout + o] = amax_o / (grid_max(p->format) * 448.0f);
+          tensor_scale[i * nout + o] = p->format == FP4R_MXFP4_MBS
+                                           ? fp4r_mbs_macro_scale(amax_o)
+                                           : amax_o / (grid_max(p->format) * 448.0f);
         }
       }
       for (int64_t b = 0; b < nblk; ++b) {

@@ -47,7 +47,12 @@ extern "C" {
 /* FP4R_E2M1_CAP2: E2M1 codes restricted to magnitudes <= 2 ([UFP4]
  * Metodologia 2, Ablacion: an E2M1 whose range is cut to emulate a uniform
  * grid), NVFP4's two-level scaling with the block amax mapped to 2. */
-enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3, FP4R_E2M1_CAP2 = 4 };
+/* FP4R_MXFP4_MBS: MXFP4 with macro-block scaling, static variant ([MXFP4]
+ * 2.B): one scale with an 8-bit mantissa per 128-element macro block,
+ * computed from the macro block's maximum, over 16-element blocks with
+ * E8M0 scales relative to it.  Always with 128-element outer scales. */
+enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3, FP4R_E2M1_CAP2 = 4,
+       FP4R_MXFP4_MBS = 5 };
 enum { FP4R_ROW = 0, FP4R_COL = 1 };
 enum { FP4R_RTNE = 0, FP4R_SR = 1 };
 enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
@@ -57,8 +62,8 @@ enum { FP4R_OUTER = 128 };
 enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1, FP4R_GRID_E2M1_CAP2 = 2 };
 
 typedef struct {
-  int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 */
-  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2) or 32 (MXFP4, MXFP4_OAS) */
+  int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
+  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS) or 32 (MXFP4, MXFP4_OAS) */
   int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
   int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */
@@ -93,6 +98,11 @@ float fp4r_e4m3_decode(uint8_t b);
 /* MX scale exponent for a block amax: floor(log2 amax) - 2 clamped to
  * [-127, 127]; amax == 0 gives -127. */
 int fp4r_e8m0_exponent(float amax);
+/* A binary32 value rounded to 8 fraction bits (9 significant bits counted
+ * from its leading one, normal or subnormal), ties to even. */
+float fp4r_round8(float x);
+/* MBS-Static macro scale of a 128-element piece: round8(amax / 6). */
+float fp4r_mbs_macro_scale(float amax);
 
 /* Overflow-aware MX exponent ([MXFP4] 2.A): the e that places amax / 2^e
  * in (3.5, 7], i.e. the smallest e with amax <= 7 * 2^e, clamped to

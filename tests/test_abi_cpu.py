@@ -82,9 +82,11 @@ def test_quantize_validation(lib):
     assert _q(lib, bad) == -2
     bad = P("mxfp4_oas"); bad.block = 16
     assert _q(lib, bad) == -2
-    bad = P("nvfp4"); bad.format = 5
-    assert _q(lib, bad) == -2
     bad = P("e2m1_cap2"); bad.block = 32
+    assert _q(lib, bad) == -2
+    assert _q(lib, P("mxfp4_mbs")) == -2                         # MBS needs its macro scales
+    assert _q(lib, P("mxfp4_mbs", ts_given=True)) == -2
+    bad = P("nvfp4"); bad.format = 6
     assert _q(lib, bad) == -2
     assert _q(lib, P("nvfp4", outer=True), cols=144, ld=144) == -3   # W % 128
     assert _q(lib, P("ufp4", outer=True, axis="col"), rows=96) == -3

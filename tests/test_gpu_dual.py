@@ -19,6 +19,8 @@ FUSED = [(128, 128), (256, 384), (384, 256), (512, 128)]
 SPLIT = [((96, 160), "bf16"), ((128, 256), "f32"), ((1056, 352), "bf16")]
 COMBOS = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2"], ["rtne", "sr"], [False, True],
                                 ["compute", "given", "outer"]))
+# MBS-Static exists only with its 128-element macro scales
+COMBOS += list(itertools.product(["mxfp4_mbs"], ["rtne", "sr"], [False, True], ["outer"]))
 
 
 def _check(x, fmt, rounding, rht, mode, seed):
@@ -51,15 +53,17 @@ def test_dual_fused_parity(fmt, rounding, rht, mode):
         _check(x, fmt, rounding, rht, mode, 11 + i)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "mxfp4_oas"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "mxfp4_oas", "mxfp4_mbs"])
 def test_dual_split_parity(fmt):
+    mbs = fmt == "mxfp4_mbs"  # macro scales only: both dims multiples of 128
     for (shape, dt), rounding, rht in itertools.product(SPLIT, ["rtne", "sr"], [False, True]):
-        if shape[0] % fp4.BLOCK[fmt] or shape[1] % fp4.BLOCK[fmt]:
+        unit = 128 if mbs else fp4.BLOCK[fmt]
+        if shape[0] % unit or shape[1] % unit:
             continue
         a = workloads.small_case("t3", shape[0], shape[1], 9)
         x = workloads.to_bf16_bits(a) if dt == "bf16" else a
         note("dual split %s %s rht=%s %s %s" % (fmt, rounding, rht, shape, dt))
-        _check(x, fmt, rounding, rht, "compute", 3)
+        _check(x, fmt, rounding, rht, "outer" if mbs else "compute", 3)
 
 
 def test_dual_matches_single_calls_full_operand():

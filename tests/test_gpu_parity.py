@@ -32,7 +32,7 @@ COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas", "e2m1_ca
 # tiles plus a right strip of 8 columns and a bottom strip of 128 rows;
 # (384, 1152) row: nine outer pieces per row; (256, 384): whole tiles.
 OUTER_SHAPES = [(128, 256), (640, 200), (384, 1152), (256, 384)]
-OUTER_COMBOS = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2"], ["row", "col"], ["rtne", "sr"],
+OUTER_COMBOS = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2", "mxfp4_mbs"], ["row", "col"], ["rtne", "sr"],
                                       [False, True], ["bf16", "f32"]))
 
 

@@ -86,7 +86,7 @@ class Call:
     rht: bool = False
     rht_seed: int = 0
     sr_seed: int = 0
-    outer: bool = False   # NVFP4 / uniform: outer scale per 128 elements
+    outer: bool = False   # two-level formats: outer (MBS: macro) scale per 128 elements
     op: str = "quantize"  # "quantize", "dequantize" (of this call's own codes) or "rht"
     out_dtype: str = "bf16"  # dequantize output
 
@@ -190,6 +190,17 @@ def _w_mx_weight_oas() -> Workload:
     return w
 
 
+def _w_mx_weight_mbs() -> Workload:
+    w = _w_mx_weight()
+    w.name = "mxfp4_mbs_weight_8192x8192"
+    w.description = ("8192x8192 BF16 N(0, 0.02^2): MXFP4 with static macro-block scaling (macro "
+                     "scale per 128, E8M0 per 16), RTNE, row and column axis, RHT off and on")
+    for c in w.calls:
+        c.fmt = "mxfp4_mbs"
+        c.outer = True
+    return w
+
+
 def _w_linear_layer_dual() -> Workload:
     w = _w_linear_layer()
     w.name = "nvfp4_rht_dual_linear_h4096_f14336_t16384"
@@ -277,6 +288,7 @@ WORKLOADS = {
     "activation_outer": _w_activation_outer,
     "linear_layer_outer": _w_linear_layer_outer,
     "mx_weight_oas": _w_mx_weight_oas,
+    "mx_weight_mbs": _w_mx_weight_mbs,
     "linear_layer_dual": _w_linear_layer_dual,
     "training_operands": _w_training_operands,
     "dequant": _w_dequant,
