@@ -31,6 +31,10 @@
  *  - Double-block scaling (an outer scale per 128 elements, inner 16-element
  *    E4M3 scales, no whole-tensor amax): TetraJet-v2 page, Riepilogo
  *    Tecnico 2.A.
+ *  - Macro-block scaling, static variant (a scale with an 8-bit mantissa
+ *    per 128 elements over 16-element E8M0 blocks): the MXFP4 page, 2.B.
+ *  - E2M1 with its range cut to emulate a uniform grid: the shrinkage-bias
+ *    page, Metodologia 2 (Ablacion).
  *
  * Numerics (one output per input; any launch geometry gives the same bytes):
  *  - A is the logical operand: x (FP4_AXIS_ROW) or x^T (FP4_AXIS_COL); W is
@@ -43,11 +47,13 @@
  *    elements v = y * (1/d) rounded to the grid.  S = 0 or d = 0 gives
  *    signed-zero codes.  With FP4_TS_OUTER128, each 128-element piece of an
  *    A-row has its own s_o = amax_piece / (G * 448), used in place of s_t.
+ *    E2M1_CAP2 is NVFP4 with G = 2.
  *    MXFP4: d = 2^e, e = floor(log2 amax_b) - 2 clamped to [-127, 127],
  *    scale byte e + 127.  MXFP4_OAS: e is the integer with
- *    3.5 < amax_b / 2^e <= 7, same clamp and byte.
- *  - Grids: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; UFP4 {0, 1, ..., 7}; values
- *    past the top level saturate.  RTNE ties go to the even code.  SR rounds
+ *    3.5 < amax_b / 2^e <= 7, same clamp and byte.  MXFP4_MBS: see its
+ *    #define below (macro scale in the outer-scale slot, E8M0 per 16).
+ *  - Grids: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; E2M1_CAP2 {0, .5, 1, 1.5, 2};
+ *    UFP4 {0, 1, ..., 7}; values past the top level saturate.  RTNE ties go to the even code.  SR rounds
  *    up iff u16 < p * 65536, p = (m - L[k]) / (L[k+1] - L[k]); u16 is half of
  *    a Philox4x32-10 word (Salmon et al., SC'11) with key = sr_seed and
  *    counter (g, 0, 0), g = n / 8, n = row_A * W + col_A; element n % 8 takes
@@ -126,7 +132,7 @@ typedef int32_t fp4_status;
 
 #define FP4_TS_COMPUTE 0  /* tensor scale computed from the data, written out */
 #define FP4_TS_GIVEN 1    /* tensor scale read from *tensor_scale */
-#define FP4_TS_OUTER128 2 /* double block: one outer scale per 128 elements */
+#define FP4_TS_OUTER128 2 /* double block (MBS: macro scale): one FP32 per 128 elements */
 
 typedef struct {
   int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
@@ -134,7 +140,8 @@ typedef struct {
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for the MX formats) */
+  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for MXFP4 and MXFP4_OAS;
+                       MXFP4_MBS requires _OUTER128) */
   uint64_t rht_seed;
   uint64_t sr_seed;
 } fp4_params;
