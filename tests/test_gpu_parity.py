@@ -251,3 +251,29 @@ def test_dequant_arbitrary_codes_and_scales(fmt):
                                              cols, fmt, axis, True, 2, inv, name)
                     _same_or_both_nan(to_host(out), want, bits, "%s %s ts=%s inv=%s %s" % (
                         fmt, axis, ts, inv, name))
+
+
+def test_dequant_mbs_arbitrary_codes_scales_and_macro():
+    """MBS-Static dequantize of random codes, every E8M0 byte and macro scales
+    from zero and subnormals to 1e30: d_b = M * 2^(byte - 127) underflows,
+    overflows and lands on subnormals; the inverse RHT's 1/4 folds into d or
+    not.  Against the oracle, both axes and output types."""
+    rows, cols = 256, 384
+    rng = np.random.default_rng(22)
+    macros = np.array([0.0, 1e-44, 3e-39, 2.0 ** -100, 0.37, 6.5, 2.0 ** 60, 1e30], np.float32)
+    for axis in ("row", "col"):
+        cshape, sshape = fp4.output_shapes(rows, cols, "mxfp4_mbs", axis)
+        oshape = fp4.outer_shape(rows, cols, axis)
+        codes = rng.integers(0, 256, cshape, dtype=np.uint8)
+        scales = rng.integers(0, 255, sshape, dtype=np.uint8)
+        macro = rng.choice(macros, oshape).astype(np.float32)
+        for inv in (False, True):
+            for odt, name, bits in ((torch.float32, "f32", 32), (torch.bfloat16, "bf16", 16)):
+                note("dequant mbs %s inv=%s %s" % (axis, inv, name))
+                out = fp4.dequantize(to_device(codes), to_device(scales), to_device(macro), rows,
+                                     cols, "mxfp4_mbs", axis, True, 2, inv, odt)
+                torch.cuda.synchronize()
+                want = oracle.dequantize(codes, scales, macro, rows, cols, "mxfp4_mbs", axis,
+                                         True, 2, inv, name)
+                _same_or_both_nan(to_host(out), want, bits,
+                                  "mbs %s inv=%s %s" % (axis, inv, name))
