@@ -124,7 +124,8 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, copy_mi
         return rows, big, reported, delims
 
     import workloads
-    ncalls = len(workloads.workload(workload).calls)
+    wl = workloads.workload(workload)
+    ncalls = len(wl.gemms) if isinstance(wl, workloads.GemmWorkload) else len(wl.calls)
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
            "copy_mib": copy_mib, "commands": commands}
     per = {}
@@ -280,6 +281,22 @@ def gemm_bench(args, w, dev):
         del ref
         torch.cuda.empty_cache()
 
+    if args.copy_mib:
+        # Counter runs: each GEMM once, each followed by a 1 MiB delimiter
+        # copy, then one copy of known size that calibrates the counters.
+        small = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        small2 = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        small2.copy_(small)
+        for i in range(len(w.gemms)):
+            run(i)
+            small2.copy_(small)
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     dom = max(range(len(w.gemms)), key=lambda i: per_call[i])
     achieved = flops[dom] / (per_call[dom] * 1e-3) / 1e12
     line = {
@@ -300,7 +317,8 @@ def gemm_bench(args, w, dev):
                    "output_sqnr_db": sqnr},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for(args.workload, dom),
                      "kernel": "call %d (%s GEMM): fp4_gemm_mx" % (dom, w.gemms[dom].name),
                      "mean_us": round(per_call[dom] * 1e3, 2)},
         "cpu_baseline": None if args.no_cpu_baseline else gemm_cpu_baseline(w, host, ops),
