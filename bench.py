@@ -180,6 +180,9 @@ def cpu_baseline(w, tensors, budget_s=12.0):
 
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
+# formats whose GEMM-level quality the GEMM workload reports through
+# dequantize + a float32 GEMM (same operands, recipes and seeds)
+GEMM_SQNR_FORMATS = ("nvfp4", "ufp4", "e2m1_cap2", "mxfp4", "mxfp4_oas", "mxfp4_mbs")
 
 
 def gemm_bench(args, w, dev):
@@ -187,7 +190,8 @@ def gemm_bench(args, w, dev):
     then each step runs the workload's GEMMs; value = their flops over their
     time.  Also reported: each operand's quantize time (the quantize
     overhead relative to the GEMMs), the output SQNR of every GEMM against a
-    float32 product of the BF16 inputs, with and without the RHT, and the
+    float32 product of the BF16 inputs, with and without the RHT (FP4 GEMM;
+    and for every format through dequantize and a float32 GEMM), and the
     oracle's GEMM rate on a sample."""
     import numpy as np
     import torch
@@ -263,6 +267,22 @@ def gemm_bench(args, w, dev):
     # output SQNR per path against float32 products of the BF16 inputs
     sqnr = {}
     plain = {op: quant(op, False)[:2] for op in ops}
+
+    def dequantized(op, fmt, rht):
+        # the operand quantized in `fmt` and dequantized exactly to float32
+        # by the library (still rotated: both operands of a GEMM carry the
+        # same RHT along K, which cancels in the product), as [rows, K]
+        t, axis, rounding, sr_seed = op
+        c, sc, ts = fp4.quantize(x[t], fmt, axis, rounding, rht, 0, sr_seed)
+        R, C = x[t].shape
+        v = fp4.dequantize(c, sc, ts, R, C, fmt, axis, rht, 0, False, torch.float32)
+        return (v if axis == "row" else v.t()).contiguous()
+
+    def db(c, ref, ref_e):
+        err = float(((c.double() - ref.double()) ** 2).sum())
+        return round(10.0 * np.log10(ref_e / err), 2) if err > 0 else None
+
+    fmt_sqnr = {f: {} for f in GEMM_SQNR_FORMATS}
     for gm, (M, N, K) in zip(w.gemms, shapes):
         def operand(op):
             t, axis = op[0], op[1]
@@ -274,10 +294,20 @@ def gemm_bench(args, w, dev):
         for tag, qs in (("rht", ops), ("no_rht", plain)):
             (ac, asc), (bc, bsc) = qs[gm.a], qs[gm.b]
             c = fp4.gemm_mx(ac, asc, bc, bsc, out_dtype=torch.float32)
-            err = float(((c.double() - ref.double()) ** 2).sum())
-            res[tag] = round(10.0 * np.log10(ref_e / err), 2) if err > 0 else None
+            res[tag] = db(c, ref, ref_e)
             del c
         sqnr[gm.name] = res
+        # every format through dequantize + one float32 GEMM (the formats the
+        # scaled MFMA cannot take; MXFP4 again as a check on the FP4 GEMM)
+        for f in GEMM_SQNR_FORMATS:
+            r = {}
+            for tag, rht in (("rht", True), ("no_rht", False)):
+                a = dequantized(gm.a, f, rht)
+                b = dequantized(gm.b, f, rht)
+                c = a @ b.t().contiguous()
+                r[tag] = db(c, ref, ref_e)
+                del a, b, c
+            fmt_sqnr[f][gm.name] = r
         del ref
         torch.cuda.empty_cache()
 
@@ -314,7 +344,8 @@ def gemm_bench(args, w, dev):
                    "quantize_us": quant_us,
                    "quantize_over_gemm": round(sum(quant_us.values()) /
                                                (sum(per_call) * 1e3), 4),
-                   "output_sqnr_db": sqnr},
+                   "output_sqnr_db": sqnr,
+                   "output_sqnr_db_by_format": fmt_sqnr},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": FP4_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
