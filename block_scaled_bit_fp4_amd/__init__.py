@@ -143,6 +143,10 @@ def workspace_bytes_dual(rows: int, cols: int, params: Params) -> int:
     return int(load().fp4_workspace_bytes_dual(rows, cols, ctypes.byref(params)))
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def new_workspace(rows: int, cols: int, params: Params, device) -> Optional[torch.Tensor]:
     """A workspace for repeated quantize calls (None if none is needed); its
     contents need no initialization."""
@@ -201,8 +205,7 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
         workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     st = load().fp4_quantize(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
                              ctypes.byref(p), codes.data_ptr(), scales.data_ptr(), _ptr(ts),
-                             _ptr(workspace), nws if workspace is not None else 0,
-                             _stream(stream))
+                             _ptr(workspace), _nbytes(workspace), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize")
     return codes, scales, ts
@@ -250,7 +253,7 @@ def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", r
     st = load().fp4_quantize_dual(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
                                   ctypes.byref(p), cr.data_ptr(), sr_.data_ptr(), _ptr(tr),
                                   cc.data_ptr(), sc.data_ptr(), _ptr(tc), _ptr(workspace),
-                                  nws if workspace is not None else 0, _stream(stream))
+                                  _nbytes(workspace), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize_dual")
     return outs[0], outs[1]

@@ -3,8 +3,11 @@
 // to the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdint>
 #include <cstdlib>
+#include <random>
 
 #include "fp4.h"
 #include "fp4_launch.h"
@@ -85,6 +88,32 @@ bool needs_workspace(const fp4_params* p) {
   return two_level(p) && p->ts_mode == FP4_TS_COMPUTE;
 }
 
+// Tag of one quantize call: unique within the process (a counter) and,
+// from a random start, unlike the tags of other processes that may have
+// used the same device memory.  Never 0.
+uint64_t next_call_tag() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    uint64_t v = ((uint64_t)rd() << 32) ^ rd();
+    v ^= (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull;
+    return v;
+  }()};
+  uint64_t t;
+  while ((t = next.fetch_add(1, std::memory_order_relaxed)) == 0) {
+  }
+  return t;
+}
+
+// Microseconds a workgroup of the single-pass row kernel waits for the
+// other workgroups' partial maxima before computing the missing ones
+// itself (FP4_AMAX_WAIT_US; 0 makes every wait end at once).
+uint32_t amax_wait_us() {
+  const char* e = std::getenv("FP4_AMAX_WAIT_US");
+  if (!e || !*e) return 500u;
+  const long v = std::strtol(e, nullptr, 10);
+  return v < 0 ? 0u : (v > 1000000 ? 1000000u : (uint32_t)v);
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,7 +122,7 @@ size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p) {
   (void)rows;
   (void)cols;
   if (check_params(p) != FP4_OK) return 0;
-  return needs_workspace(p) ? sizeof(float) * (size_t)kAmaxPartials : 0;
+  return needs_workspace(p) ? kSinglePassWsBytes : 0;
 }
 
 uint16_t fp4_rht_signs(uint64_t rht_seed) {
@@ -145,6 +174,9 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   q.scales = scales;
   q.tensor_scale = tensor_scale;
   q.workspace = static_cast<float*>(workspace);
+  q.ws_bytes = workspace ? ws_bytes : 0;
+  q.call_tag = next_call_tag();
+  q.wait_us = amax_wait_us();
   return finish(fp4_launch_quantize(q, s), s);
 }
 
@@ -152,7 +184,9 @@ size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p)
   (void)rows;
   (void)cols;
   if (check_params(p) != FP4_OK) return 0;
-  return needs_workspace(p) ? 2 * sizeof(float) * (size_t)kAmaxPartials : 0;
+  if (!needs_workspace(p)) return 0;
+  const size_t dual = 2 * sizeof(float) * (size_t)kAmaxPartials;
+  return dual > kSinglePassWsBytes ? dual : kSinglePassWsBytes;
 }
 
 fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,

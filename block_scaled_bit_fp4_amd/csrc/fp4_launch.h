@@ -9,6 +9,11 @@
 // workspace of a two-level quantize in computed-scale mode holds this many
 // floats.
 constexpr int kAmaxPartials = 1024;
+// The single-pass row kernel's exchange: kAmaxPartials slots and one result
+// slot of 16 bytes each (two words, each half of a 64-bit call tag above
+// the binary32 maximum).
+constexpr int kAmaxSlotBytes = 16;
+constexpr size_t kSinglePassWsBytes = (size_t)(kAmaxPartials + 1) * kAmaxSlotBytes;
 
 struct QuantLaunch {
   const void* x;
@@ -22,6 +27,9 @@ struct QuantLaunch {
   uint8_t* scales;
   float* tensor_scale;
   float* workspace;
+  size_t ws_bytes;
+  uint64_t call_tag;  // unique per call (single-pass exchange)
+  uint32_t wait_us;   // single-pass wait before a workgroup computes what is missing
 };
 
 // Row-axis and column-axis quantization of one BF16 x in one pass

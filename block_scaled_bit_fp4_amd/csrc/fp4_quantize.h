@@ -366,12 +366,96 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
 }
 
 // ------------------------------------------------------------- row axis
+// Store the codes and block scales of one unit of U elements of an A-row.
+template <int B, int U>
+__device__ __forceinline__ void store_row_unit(const uint32_t (&packed)[U / 8],
+                                               const uint32_t (&sb)[U / B], int64_t row,
+                                               int64_t minor, const QuantArgs& a) {
+  constexpr int NBU = U / B;
+  uint8_t* cp = a.codes + row * (a.W / 2) + minor * (U / 2);
+  if constexpr (U >= 32) {
+#pragma unroll
+    for (int i = 0; i < U / 32; ++i)
+      store16<true>(cp + 16 * i, packed[4 * i], packed[4 * i + 1], packed[4 * i + 2],
+                    packed[4 * i + 3]);
+  } else {
+    store8<true>(cp, packed[0], packed[1]);
+  }
+  uint8_t* sp = a.scales + row * (a.W / B) + minor * NBU;
+  if constexpr (NBU == 4)
+    *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+  else if constexpr (NBU == 2)
+    *reinterpret_cast<uint16_t*>(sp) = (uint16_t)(sb[0] | (sb[1] << 8));
+  else
+    sp[0] = (uint8_t)sb[0];
+}
+
+// Code one unit of an A-row held in `cur` (A-row `row`, unit `minor` of U
+// elements within it) and store its codes and block scales.
+template <int FMT, bool SR, bool RHT, int TSM, typename T, int U>
+__device__ __forceinline__ void code_row_unit(const RowRaw<T, U>& cur, int64_t row, int64_t minor,
+                                              const QuantArgs& a, const ScaleCtx& c,
+                                              const float* inv_tab) {
+  constexpr int B = block_of<FMT>();
+  constexpr int NBU = U / B;  // blocks per unit
+  uint32_t packed[U / 8];
+  uint32_t sb[NBU];
+  // widened (and rotated) block bi of the unit, with its largest magnitude
+  auto block_values = [&](int bi, float (&t)[B], float& amax_t) {
+    amax_t = 0.0f;
+#pragma unroll
+    for (int h = 0; h < B / 16; ++h) {
+      float g[16];
+      cur.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+      if (RHT) fwht16(g);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        t[16 * h + j] = g[j];
+        amax_t = fmaxf(amax_t, fabsf(g[j]));
+      }
+    }
+  };
+  auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
+    const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * U + bi * B);
+    uint32_t pk[B / 8];
+    encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
+                                                       a.sr_k1, n0, pk, sb[bi]);
+#pragma unroll
+    for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
+  };
+  if constexpr (TSM == kTsOuter) {
+    // kOuter / U consecutive lanes hold one 128-piece of an A-row (the
+    // walk keeps them in step): their maxima combine by lane exchange.
+    constexpr int LPO = kOuter / U;
+    float t[NBU][B], am[NBU];
+    float ao = 0.0f;
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) {
+      block_values(bi, t[bi], am[bi]);
+      ao = fmaxf(ao, am[bi]);
+    }
+    ao = group_max<LPO>(ao);
+    ScaleCtx co;
+    co.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
+    co.den = co.s_t * grid_max<FMT>();
+    if (minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + minor / LPO] = co.s_t;
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) {
+      float t[B], amax_t;
+      block_values(bi, t, amax_t);
+      code(bi, t, amax_t, c);
+    }
+  }
+  store_row_unit<B, U>(packed, sb, row, minor, a);
+}
+
 // Units: major = A-row, minor = piece of U elements within it.
 template <int FMT, bool SR, bool RHT, int TSM, typename T, int U>
 __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restrict__ x,
                                                                 QuantArgs a) {
-  constexpr int B = block_of<FMT>();
-  constexpr int NBU = U / B;  // blocks per unit
   __shared__ float inv_tab[128];
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
@@ -391,79 +475,243 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
     const bool have_next = nw.major < a.n_major;
     RowRaw<T, U> nxt;
     if (have_next) nxt.load(x + row_of(nw.major) * a.ld + nw.minor * U);
-    const int64_t row = row_of(w.major);
-
-    uint32_t packed[U / 8];
-    uint32_t sb[NBU];
-    // widened (and rotated) block bi of the unit, with its largest magnitude
-    auto block_values = [&](int bi, float (&t)[B], float& amax_t) {
-      amax_t = 0.0f;
-#pragma unroll
-      for (int h = 0; h < B / 16; ++h) {
-        float g[16];
-        cur.template group<RHT>(bi * (B / 16) + h, g, a.signs);
-        if (RHT) fwht16(g);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          t[16 * h + j] = g[j];
-          amax_t = fmaxf(amax_t, fabsf(g[j]));
-        }
-      }
-    };
-    auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
-      const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(w.minor * U + bi * B);
-      uint32_t pk[B / 8];
-      encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
-                                                         a.sr_k1, n0, pk, sb[bi]);
-#pragma unroll
-      for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
-    };
-    if constexpr (TSM == kTsOuter) {
-      // kOuter / U consecutive lanes hold one 128-piece of an A-row (the
-      // walk keeps them in step): their maxima combine by lane exchange.
-      constexpr int LPO = kOuter / U;
-      float t[NBU][B], am[NBU];
-      float ao = 0.0f;
-#pragma unroll
-      for (int bi = 0; bi < NBU; ++bi) {
-        block_values(bi, t[bi], am[bi]);
-        ao = fmaxf(ao, am[bi]);
-      }
-      ao = group_max<LPO>(ao);
-      ScaleCtx co;
-      co.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
-      co.den = co.s_t * grid_max<FMT>();
-      if (w.minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + w.minor / LPO] = co.s_t;
-#pragma unroll
-      for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < NBU; ++bi) {
-        float t[B], amax_t;
-        block_values(bi, t, amax_t);
-        code(bi, t, amax_t, c);
-      }
-    }
-    uint8_t* cp = a.codes + row * (a.W / 2) + w.minor * (U / 2);
-    if constexpr (U >= 32) {
-#pragma unroll
-      for (int i = 0; i < U / 32; ++i)
-        store16<true>(cp + 16 * i, packed[4 * i], packed[4 * i + 1], packed[4 * i + 2],
-                packed[4 * i + 3]);
-    } else {
-      store8<true>(cp, packed[0], packed[1]);
-    }
-    uint8_t* sp = a.scales + row * (a.W / B) + w.minor * NBU;
-    if constexpr (NBU == 4)
-      *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-    else if constexpr (NBU == 2)
-      *reinterpret_cast<uint16_t*>(sp) = (uint16_t)(sb[0] | (sb[1] << 8));
-    else
-      sp[0] = (uint8_t)sb[0];
-
+    code_row_unit<FMT, SR, RHT, TSM, T, U>(cur, row_of(w.major), w.minor, a, c, inv_tab);
     cur = nxt;
     w = nw;
     have = have_next;
+  }
+}
+
+
+// ------------------------------------------------ row axis, single pass
+// Two-level formats with a computed tensor scale, when every unit of the
+// operand fits in the registers of one resident grid: each lane loads its
+// NU units once (unit u = global lane + k * lanes of the grid), the
+// workgroups exchange their partial maxima through the workspace, and the
+// lanes then code the units they still hold.  The input is read once, in
+// one launch, where the two-pass path reads it twice in two.
+//
+// Exchange: workgroup b posts its partial maximum in slot b; workgroup 0
+// gathers the slots and posts the tensor maximum in the result slot; the
+// others wait for it.  A slot is two 64-bit words, each holding one half of
+// the call's 64-bit tag above the maximum, written and read as relaxed
+// device-scope atomics: a slot counts as posted when both words carry this
+// call's halves and the same maximum, so no fence (and no cache write-back
+// or invalidation) is needed, and a slot half-written by a racing read is
+// simply not posted yet.  Tags are unique per call, so nothing a slot held
+// before (an earlier call's record, or any other bytes, but with chance
+// 2^-64) reads as posted, and the workspace needs no clearing.  Every wait
+// is bounded in time: a workgroup that has not seen what it waits for
+// computes the missing partial maxima from the input itself.  They are the
+// same values, so the tensor scale is the same, and the call ends even
+// when not all of its workgroups are resident at once.
+struct AmaxSlot {
+  uint64_t hi;  // tag bits 63..32, binary32 bits of the maximum
+  uint64_t lo;  // tag bits 31..0, the same maximum
+};
+static_assert(sizeof(AmaxSlot) == kAmaxSlotBytes, "slot size");
+
+__device__ __forceinline__ void post_slot(AmaxSlot* s, float v, uint64_t tag) {
+  const uint64_t m = __float_as_uint(v);
+  __hip_atomic_store(&s->hi, (tag & 0xFFFFFFFF00000000ull) | m, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&s->lo, (tag << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The slot's maximum if both words hold this call's record.
+__device__ __forceinline__ bool read_slot(AmaxSlot* s, uint64_t tag, float& v) {
+  const uint64_t hi = __hip_atomic_load(&s->hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t lo = __hip_atomic_load(&s->lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((hi >> 32) != (tag >> 32) || (lo >> 32) != (tag & 0xFFFFFFFFull) ||
+      (uint32_t)hi != (uint32_t)lo)
+    return false;
+  v = __uint_as_float((uint32_t)hi);
+  return true;
+}
+
+// Largest |H16 D a| (before the 1/4) or |a| of a row unit.
+template <bool RHT, typename T, int U>
+__device__ __forceinline__ float unit_absmax(const RowRaw<T, U>& r, uint32_t signs) {
+  float m = 0.0f;
+#pragma unroll
+  for (int h = 0; h < U / 16; ++h) {
+    float t[16];
+    r.template group<RHT>(h, t, signs);
+    if (RHT) {
+      m = fmaxf(m, fwht16_absmax(t));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(t[j]), fabsf(t[j + 1])));
+    }
+  }
+  return m;
+}
+
+// Partial maximum of workgroup j, recomputed from the input by the whole
+// calling workgroup (the value workgroup j posts).
+template <bool RHT, typename T, int U, int NU>
+__device__ float partial_of(const T* __restrict__ x, const QuantArgs& a, int64_t j,
+                            int64_t stride) {
+  const int64_t units = a.n_major * a.M;
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int64_t u = j * kThreads + threadIdx.x + k * stride;
+    if (u < units) {
+      const int64_t row = u / a.M, minor = u - row * a.M;
+      RowRaw<T, U> r;
+      r.load(x + row * a.ld + minor * U);
+      m = fmaxf(m, unit_absmax<RHT, T, U>(r, a.signs));
+    }
+  }
+  m = block_max_256(m);
+  return RHT ? m * 0.25f : m;
+}
+
+// Tensor maximum from the posted slots [0, n), waiting up to wait_ticks of
+// the constant-rate clock; slots still missing then are computed here.
+// Block-uniform control flow (partial_of synchronises the workgroup).
+template <bool RHT, typename T, int U, int NU>
+__device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxSlot* slots, int n,
+                              uint64_t tag, uint64_t wait_ticks, int64_t stride) {
+  constexpr int kPer = kAmaxPartials / kThreads;
+  __shared__ int missing[kAmaxPartials];
+  __shared__ int nmissing;
+  float m = 0.0f;
+  uint32_t pending = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if ((int)threadIdx.x + i * kThreads < n) pending |= 1u << i;
+  const uint64_t t0 = wall_clock64();
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float v;
+      if ((pending >> i) & 1u && read_slot(slots + threadIdx.x + i * kThreads, tag, v)) {
+        m = fmaxf(m, v);
+        pending &= ~(1u << i);
+      }
+    }
+    if (!__syncthreads_or(pending != 0)) break;
+    if (__syncthreads_or(wall_clock64() - t0 >= wait_ticks)) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (threadIdx.x == 0) nmissing = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if ((pending >> i) & 1u) missing[atomicAdd(&nmissing, 1)] = threadIdx.x + i * kThreads;
+  __syncthreads();
+  const int nm = nmissing;
+  for (int i = 0; i < nm; ++i) m = fmaxf(m, partial_of<RHT, T, U, NU>(x, a, missing[i], stride));
+  return block_max_256(m);
+}
+
+template <int FMT, bool SR, bool RHT, typename T, int U, int NU>
+__global__ __launch_bounds__(kThreads) void quantize_row_single_kernel(
+    const T* __restrict__ x, QuantArgs a, AmaxSlot* slots, uint64_t tag, uint64_t wait_ticks) {
+  constexpr int B = block_of<FMT>();
+  constexpr int NBU = U / B;
+  __shared__ float inv_tab[128];
+  __shared__ float shared_amax;
+  __shared__ int shared_have;
+  const int64_t units = a.n_major * a.M;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // Everything that does not depend on the tensor scale is done before the
+  // exchange: the units' widened (and rotated) values and their block
+  // maxima stay in registers for the coding after it.
+  float t[NU][NBU][B];
+  float bam[NU][NBU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int64_t u = u0 + k * stride;
+    RowRaw<T, U> raw;
+    if (u < units) {
+      const int64_t row = u / a.M, minor = u - row * a.M;
+      raw.load(x + row * a.ld + minor * U);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RowRaw<T, U>::kVec; ++i) raw.q[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) {
+      bam[k][bi] = 0.0f;
+#pragma unroll
+      for (int h = 0; h < B / 16; ++h) {
+        float g[16];
+        raw.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+        if (RHT) fwht16(g);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          t[k][bi][16 * h + j] = g[j];
+          bam[k][bi] = fmaxf(bam[k][bi], fabsf(g[j]));
+        }
+      }
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NU; ++k)
+#pragma unroll
+    for (int bi = 0; bi < NBU; ++bi) m = fmaxf(m, bam[k][bi]);  // 0 past the last unit
+  m = block_max_256(m);
+  if (threadIdx.x == 0) post_slot(slots + blockIdx.x, RHT ? m * 0.25f : m, tag);
+
+  AmaxSlot* result = slots + kAmaxPartials;
+  float amax = 0.0f;
+  bool have = false;
+  if (blockIdx.x != 0) {
+    if (threadIdx.x == 0) {
+      const uint64_t t0 = wall_clock64();
+      float v = 0.0f;
+      bool ok;
+      while (!(ok = read_slot(result, tag, v)) && wall_clock64() - t0 < wait_ticks)
+        __builtin_amdgcn_s_sleep(2);
+      shared_amax = v;
+      shared_have = ok;
+    }
+    __syncthreads();
+    have = shared_have;
+    amax = shared_amax;
+  }
+  if (!have) {
+    // workgroup 0 waits for every slot; a workgroup whose wait ran out
+    // takes what is posted and computes the rest at once
+    amax = gather_slots<RHT, T, U, NU>(x, a, slots, gridDim.x, tag,
+                                       blockIdx.x == 0 ? wait_ticks : 0, stride);
+    if (blockIdx.x == 0 && threadIdx.x == 0) post_slot(result, amax, tag);
+  }
+
+  // the two-level scale from the tensor maximum, as in scale_prologue
+  ScaleCtx c;
+  c.s_t = amax / (grid_max<FMT>() * 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
+  c.den = c.s_t * grid_max<FMT>();
+  if (threadIdx.x < 128) {
+    const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
+    const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
+    inv_tab[threadIdx.x] = d != 0.0f ? 1.0f / d : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int64_t u = u0 + k * stride;
+    if (u < units) {
+      const int64_t row = u / a.M, minor = u - row * a.M;
+      uint32_t packed[U / 8];
+      uint32_t sb[NBU];
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) {
+        const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * U + bi * B);
+        uint32_t pk[B / 8];
+        encode_block<FMT, SR, RHT, sizeof(T) == 2, B, kTsCompute>(
+            t[k][bi], bam[k][bi], c, inv_tab, a.sr_k0, a.sr_k1, n0, pk, sb[bi]);
+#pragma unroll
+        for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
+      }
+      store_row_unit<B, U>(packed, sb, row, minor, a);
+    }
   }
 }
 
@@ -1090,11 +1338,52 @@ void launch_amax(const QuantLaunch& q, hipStream_t s) {
   }
 }
 
+// Ticks of the constant-rate clock (wall_clock64) per microsecond.
+uint64_t wall_ticks_per_us() {
+  static std::mutex mu;
+  static int64_t cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int khz = 0;
+    cache[dev] = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess &&
+                         khz > 0
+                     ? (khz + 999) / 1000
+                     : 100;
+  }
+  return (uint64_t)cache[dev];
+}
+
+#ifndef FP4_SINGLE_PASS
+#define FP4_SINGLE_PASS 1
+#endif
+
+// The single-pass row path: the smallest NU whose grid (one unit per lane
+// per k) is resident at once and has at most kAmaxPartials workgroups.
+// False when the operand does not fit; nothing is launched then.
+template <int FMT, bool SR, bool RHT, typename T, int NU>
+bool try_single_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
+  constexpr int U = 32;
+  auto kernel = quantize_row_single_kernel<FMT, SR, RHT, T, U, NU>;
+  const int64_t units = q.rows * (q.cols / U);
+  const int64_t grid = (units + (int64_t)kThreads * NU - 1) / ((int64_t)kThreads * NU);
+  const int64_t cap = resident_wgs(reinterpret_cast<const void*>(kernel));
+  if (grid < 1 || grid > kAmaxPartials || grid > cap) return false;
+  a.W = q.cols;
+  a.n_major = q.rows;
+  a.M = q.cols / U;
+  AmaxSlot* slots = reinterpret_cast<AmaxSlot*>(q.workspace);
+  const uint64_t ticks = (uint64_t)q.wait_us * wall_ticks_per_us();
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(q.x), a, slots, q.call_tag, ticks);
+  return true;
+}
+
 template <int FMT, bool SR, bool RHT, int TSM, typename T>
 hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   constexpr int B = block_of<FMT>();
   const T* x = static_cast<const T*>(q.x);
-  if (!is_mx(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
   QuantArgs a{};
   a.ld = q.ld;
   a.codes = q.codes;
@@ -1106,6 +1395,15 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   a.signs = q.signs;
   a.sr_k0 = q.sr_k0;
   a.sr_k1 = q.sr_k1;
+  if constexpr (!is_mx(FMT) && FMT != kMBS && TSM == kTsCompute && sizeof(T) == 2) {
+    if (FP4_SINGLE_PASS && q.axis == 0 && q.cols % 32 == 0 &&
+        q.ws_bytes >= kSinglePassWsBytes &&
+        (try_single_pass<FMT, SR, RHT, T, 1>(q, a, s) ||
+         try_single_pass<FMT, SR, RHT, T, 2>(q, a, s) ||
+         try_single_pass<FMT, SR, RHT, T, 4>(q, a, s)))
+      return hipGetLastError();
+  }
+  if (!is_mx(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
   if (q.axis == 0) {
     a.W = q.cols;
     const bool wide = q.cols % 32 == 0;

@@ -148,14 +148,26 @@ typedef struct {
 
 /* Bytes of device workspace fp4_quantize needs for this call (0 when none:
  * the MX formats, a given tensor scale, outer scales).  Contents need no
- * initialization. */
+ * initialization.  A computed tensor scale takes the tensor maximum of the
+ * (rotated) operand before any block is coded.  With BF16 input on the row
+ * axis, W a multiple of 32 and an operand that fits the registers of one
+ * resident grid (about 16M elements with the RHT on MI355X), one kernel
+ * reads x once: its workgroups exchange partial maxima through 16-byte
+ * records in the workspace, tagged per call so that earlier contents are
+ * never taken for this call's.  Otherwise, or when ws_bytes is below the
+ * returned size but at least 4096 (1024 floats), a tensor-maximum pass
+ * precedes the quantize pass.  Both give the same bytes.  A workgroup that
+ * waits longer than FP4_AMAX_WAIT_US microseconds (environment, default
+ * 500) for the others computes what it misses from x itself, so a call
+ * whose workgroups are not all resident at once still finishes. */
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
 
 /* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
  * scales (layouts above).  tensor_scale is written (COMPUTE, OUTER128) or
  * read (GIVEN) for the two-level formats (NVFP4, UFP4, E2M1_CAP2) and may
  * be NULL for the MX formats.
- * workspace must hold fp4_workspace_bytes() bytes.  Requirements: block
+ * workspace holds ws_bytes bytes: at least 4096 for a computed tensor scale,
+ * fp4_workspace_bytes() for the single-pass kernel.  Requirements: block
  * matches the format; W divisible by the block (and by 16 when rht, by 128
  * with OUTER128); ld >= cols; x, codes, scales 16-byte aligned; ld *
  * element size a multiple of 16 bytes.  rows == 0 or cols == 0 is valid
