@@ -42,9 +42,15 @@ KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/" + f for f in (
 MX = ("mxfp4", "mxfp4_oas")
 
 
-def kernel_source_hash() -> str:
+GEMM_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_gemm.hip"]
+
+
+def kernel_source_hash(workload: str = "") -> str:
+    """Hash of the kernel sources a workload's counters depend on (the GEMM
+    kernel for the GEMM workload, the quantize and dequantize kernels for
+    the others)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (GEMM_SOURCES if workload == "gemm_mx" else KERNEL_SOURCES):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -98,7 +104,7 @@ def traffic_for(workload: str, call_index: int):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     per = t.get("per_call_bytes")
     if not per or call_index >= len(per):
@@ -126,7 +132,7 @@ def traffic_from_counters(workload: str, fetch_csv: str, write_csv: str, copy_mi
     import workloads
     wl = workloads.workload(workload)
     ncalls = len(wl.gemms) if isinstance(wl, workloads.GemmWorkload) else len(wl.calls)
-    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(workload),
            "copy_mib": copy_mib, "commands": commands}
     per = {}
     for name, path in (("fetch", fetch_csv), ("write", write_csv)):
@@ -560,7 +566,8 @@ def main():
         "kernel": "call %d (%s): %s" % (
             dom, call_label(c), "fp4_rht" if c.op == "rht" else "fp4_dequantize"
             if c.op == "dequantize" else "fp4_quantize, quantize kernel"
-            if (c.fmt in MX or c.outer) else "fp4_quantize, tensor-amax + quantize kernels"),
+            if (c.fmt in MX or c.outer) else "fp4_quantize, computed tensor scale: the single-pass "
+            "kernel when the operand fits one resident grid, else tensor-amax + quantize kernels"),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
 
     if args.copy_mib:
