@@ -175,7 +175,19 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   q.tensor_scale = tensor_scale;
   q.workspace = static_cast<float*>(workspace);
   q.ws_bytes = workspace ? ws_bytes : 0;
-  q.call_tag = next_call_tag();
+  // A launch captured into a graph replays with the tag it was captured
+  // with, so a replay would read the previous replay's records as its own:
+  // under capture the two-pass path is taken (tag 0 disables the single
+  // pass).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  bool capturing = cap != hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();  // not left for the launch check to report
+    capturing = true;
+  } else {
+    capturing = cap != hipStreamCaptureStatusNone;
+  }
+  q.call_tag = capturing ? 0 : next_call_tag();
   q.wait_us = amax_wait_us();
   return finish(fp4_launch_quantize(q, s), s);
 }

@@ -28,7 +28,7 @@ struct QuantLaunch {
   float* tensor_scale;
   float* workspace;
   size_t ws_bytes;
-  uint64_t call_tag;  // unique per call (single-pass exchange)
+  uint64_t call_tag;  // unique per call (single-pass exchange); 0: two-pass only
   uint32_t wait_us;   // single-pass wait before a workgroup computes what is missing
 };
 

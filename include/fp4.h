@@ -154,9 +154,10 @@ typedef struct {
  * resident grid (about 16M elements with the RHT on MI355X), one kernel
  * reads x once: its workgroups exchange partial maxima through 16-byte
  * records in the workspace, tagged per call so that earlier contents are
- * never taken for this call's.  Otherwise, or when ws_bytes is below the
- * returned size but at least 4096 (1024 floats), a tensor-maximum pass
- * precedes the quantize pass.  Both give the same bytes.  A workgroup that
+ * never taken for this call's.  Otherwise, when ws_bytes is below the
+ * returned size but at least 4096 (1024 floats), or when the stream is
+ * being captured into a HIP graph (a replayed launch would carry the tag it
+ * was captured with), a tensor-maximum pass precedes the quantize pass.  Both give the same bytes.  A workgroup that
  * waits longer than FP4_AMAX_WAIT_US microseconds (environment, default
  * 500) for the others computes what it misses from x itself, so a call
  * whose workgroups are not all resident at once still finishes. */
