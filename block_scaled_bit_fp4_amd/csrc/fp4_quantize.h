@@ -1395,7 +1395,7 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   a.signs = q.signs;
   a.sr_k0 = q.sr_k0;
   a.sr_k1 = q.sr_k1;
-  if constexpr (!is_mx(FMT) && FMT != kMBS && TSM == kTsCompute && sizeof(T) == 2) {
+  if constexpr (!is_mx(FMT) && FMT != kMBS && TSM == kTsCompute) {
     if (FP4_SINGLE_PASS && q.axis == 0 && q.cols % 32 == 0 && q.call_tag != 0 &&
         q.ws_bytes >= kSinglePassWsBytes &&
         (try_single_pass<FMT, SR, RHT, T, 1>(q, a, s) ||

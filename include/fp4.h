@@ -149,8 +149,8 @@ typedef struct {
 /* Bytes of device workspace fp4_quantize needs for this call (0 when none:
  * the MX formats, a given tensor scale, outer scales).  Contents need no
  * initialization.  A computed tensor scale takes the tensor maximum of the
- * (rotated) operand before any block is coded.  With BF16 input on the row
- * axis, W a multiple of 32 and an operand that fits the registers of one
+ * (rotated) operand before any block is coded.  On the row axis, with W a
+ * multiple of 32 and an operand that fits the registers of one
  * resident grid (about 16M elements with the RHT on MI355X), one kernel
  * reads x once: its workgroups exchange partial maxima through 16-byte
  * records in the workspace, tagged per call so that earlier contents are

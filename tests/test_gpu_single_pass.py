@@ -1,4 +1,4 @@
-"""The single-pass row path of a computed tensor scale (BF16 input, row axis,
+"""The single-pass row path of a computed tensor scale (row axis,
 width a multiple of 32, operand small enough to stay in the registers of one
 resident grid): byte parity with the oracle and with the two-pass path, at
 grids of 1, 2 and 4 units per lane, after the workspace held other bytes,
@@ -81,3 +81,18 @@ def test_zero_wait_computes_missing_partials(monkeypatch, shape, rounding):
     note("zero wait %s %s" % (shape, rounding))
     for _ in range(3):
         quantize_both(x, "nvfp4", "row", rounding, True, 7, 11)
+
+
+@pytest.mark.parametrize("shape", [(1056, 352), (2048, 2048)])
+@pytest.mark.parametrize("rounding,rht", [("rtne", True), ("sr", True), ("rtne", False)])
+def test_single_pass_fp32_input(shape, rounding, rht):
+    x = workloads.small_case("normal", shape[0], shape[1], 500 + shape[1] % 89)
+    note("single pass f32 %s rht=%s %s" % (rounding, rht, shape))
+    quantize_both(x, "nvfp4", "row", rounding, rht, 7, 11)
+    xd = to_device(x)
+    two = torch.empty(TWO_PASS_WS, dtype=torch.uint8, device=DEV)
+    a = _run(xd, "nvfp4", rounding, rht, None)
+    b = _run(xd, "nvfp4", rounding, rht, two)
+    assert_bytes_equal(a[0], b[0], "codes single vs two-pass")
+    assert_bytes_equal(a[1], b[1], "scales single vs two-pass")
+    assert a[2] == b[2]
