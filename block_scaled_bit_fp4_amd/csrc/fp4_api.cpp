@@ -93,8 +93,12 @@ bool needs_workspace(const fp4_params* p) {
 // used the same device memory.  Never 0.
 uint64_t next_call_tag() {
   static std::atomic<uint64_t> next{[] {
-    std::random_device rd;
-    uint64_t v = ((uint64_t)rd() << 32) ^ rd();
+    uint64_t v = (uint64_t)(uintptr_t)&next;
+    try {
+      std::random_device rd;  // may throw where no entropy source exists
+      v ^= ((uint64_t)rd() << 32) ^ rd();
+    } catch (...) {
+    }
     v ^= (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull;
     return v;
   }()};
