@@ -11,7 +11,7 @@
 constexpr int kAmaxPartials = 1024;
 // The single-pass row kernel's exchange: kAmaxPartials slots and one result
 // slot of 16 bytes each (two words, each half of a 64-bit call tag above
-// the binary32 maximum).
+// the binary32 maximum XOR-ed with the other half).
 constexpr int kAmaxSlotBytes = 16;
 constexpr size_t kSinglePassWsBytes = (size_t)(kAmaxPartials + 1) * kAmaxSlotBytes;
 

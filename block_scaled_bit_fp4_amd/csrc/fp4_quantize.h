@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
 // Exchange: workgroup b posts its partial maximum in slot b; workgroup 0
 // gathers the slots and posts the tensor maximum in the result slot; the
 // others wait for it.  A slot is two 64-bit words, each holding one half of
-// the call's 64-bit tag above the maximum, written and read as relaxed
+// the call's 64-bit tag above the (masked) maximum, written and read as relaxed
 // device-scope atomics: a slot counts as posted when both words carry this
 // call's halves and the same maximum, so no fence (and no cache write-back
 // or invalidation) is needed, and a slot half-written by a racing read is
@@ -505,27 +505,36 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
 // computes the missing partial maxima from the input itself.  They are the
 // same values, so the tensor scale is the same, and the call ends even
 // when not all of its workgroups are resident at once.
+// Each word's low half is the maximum XOR the other word's tag half, so a
+// 64-bit access torn into its dwords cannot pass for a record.  When one word
+// reads whole, a slot is accepted only with that word's maximum.  When both
+// read as new tag half over an earlier record's value, they decode to two
+// maxima that differ unless the halves of (old tag XOR new tag) are equal:
+// never for two tags of one process with the same high half, with chance
+// 2^-32 otherwise.
 struct AmaxSlot {
-  uint64_t hi;  // tag bits 63..32, binary32 bits of the maximum
-  uint64_t lo;  // tag bits 31..0, the same maximum
+  uint64_t hi;  // tag bits 63..32 | maximum ^ tag bits 31..0
+  uint64_t lo;  // tag bits 31..0  | maximum ^ tag bits 63..32
 };
 static_assert(sizeof(AmaxSlot) == kAmaxSlotBytes, "slot size");
 
 __device__ __forceinline__ void post_slot(AmaxSlot* s, float v, uint64_t tag) {
-  const uint64_t m = __float_as_uint(v);
-  __hip_atomic_store(&s->hi, (tag & 0xFFFFFFFF00000000ull) | m, __ATOMIC_RELAXED,
+  const uint32_t m = __float_as_uint(v), th = (uint32_t)(tag >> 32), tl = (uint32_t)tag;
+  __hip_atomic_store(&s->hi, ((uint64_t)th << 32) | (m ^ tl), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&s->lo, (tag << 32) | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&s->lo, ((uint64_t)tl << 32) | (m ^ th), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The slot's maximum if both words hold this call's record.
 __device__ __forceinline__ bool read_slot(AmaxSlot* s, uint64_t tag, float& v) {
+  const uint32_t th = (uint32_t)(tag >> 32), tl = (uint32_t)tag;
   const uint64_t hi = __hip_atomic_load(&s->hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t lo = __hip_atomic_load(&s->lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((hi >> 32) != (tag >> 32) || (lo >> 32) != (tag & 0xFFFFFFFFull) ||
-      (uint32_t)hi != (uint32_t)lo)
+  const uint32_t m = (uint32_t)hi ^ tl;
+  if ((uint32_t)(hi >> 32) != th || (uint32_t)(lo >> 32) != tl || ((uint32_t)lo ^ th) != m)
     return false;
-  v = __uint_as_float((uint32_t)hi);
+  v = __uint_as_float(m);
   return true;
 }
 
