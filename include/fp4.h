@@ -53,11 +53,14 @@
  *    3.5 < amax_b / 2^e <= 7, same clamp and byte.  MXFP4_MBS: see its
  *    #define below (macro scale in the outer-scale slot, E8M0 per 16).
  *  - Grids: E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6}; E2M1_CAP2 {0, .5, 1, 1.5, 2};
- *    UFP4 {0, 1, ..., 7}; values past the top level saturate.  RTNE ties go to the even code.  SR rounds
- *    up iff u16 < p * 65536, p = (m - L[k]) / (L[k+1] - L[k]); u16 is half of
- *    a Philox4x32-10 word (Salmon et al., SC'11) with key = sr_seed and
- *    counter (g, 0, 0), g = n / 8, n = row_A * W + col_A; element n % 8 takes
- *    half (n % 2) of word (n % 8) / 2.
+ *    UFP4 {0, 1, ..., 7}; values past the top level saturate.  RTNE ties
+ *    go to the even code.  SR (unbiased: E[round(m)] = m, TetraJet-v2 page,
+ *    Riepilogo Tecnico 2.A) rounds m in [L[k], L[k+1]) up iff the draw
+ *    U = (u16 + 2^-6) * 2^-16 is at most p = (m - L[k]) / (L[k+1] - L[k]),
+ *    i.e. iff p * 2^22 >= 64 * u16 + 1; u16 is half of a Philox4x32-10 word
+ *    (Salmon et al., SC'11) with key = sr_seed and counter (g, 0, 0),
+ *    g = n / 8, n = row_A * W + col_A; element n % 8 takes half (n % 2) of
+ *    word (n % 8) / 2.
  *  - Codes: 4 bits, bit 3 = sign of y, bits 0-2 = level index.
  *
  * Layouts (all row-major, owned and allocated by the caller):

@@ -132,6 +132,7 @@ def lib():
                                    ctypes.POINTER(ctypes.c_uint32), u8p]
         L.fp4r_sr_u16_n.argtypes = [ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64), i64,
                                     ctypes.POINTER(ctypes.c_uint32)]
+        L.fp4r_f32_to_bf16_n.argtypes = [f32p, i64, ctypes.POINTER(ctypes.c_uint16)]
         L.fp4r_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -212,6 +213,15 @@ def round_grid(m, grid="e2m1", rounding="rtne", u16=None) -> np.ndarray:
     out = np.zeros(m.size, dtype=np.uint8)
     lib().fp4r_round_n(_ptr(m, ctypes.c_float), m.size, GRIDS[grid], ROUNDINGS[rounding],
                        _ptr(u16, ctypes.c_uint32), _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    """The conversion behind dequantize's BF16 output, on an array of float32
+    values; returns BF16 bit patterns (uint16)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32).ravel())
+    out = np.zeros(v.size, dtype=np.uint16)
+    lib().fp4r_f32_to_bf16_n(_ptr(v, ctypes.c_float), v.size, _ptr(out, ctypes.c_uint16))
     return out
 
 

@@ -557,6 +557,11 @@ void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
                                              : fp4r_round_rtne(m[i], grid));
 }
 
+void fp4r_f32_to_bf16_n(const float* in, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
+}
+
 void fp4r_sr_u16_n(uint64_t seed, const uint64_t* idx, int64_t n,
                    uint32_t* out) {
 #pragma omp parallel for schedule(static)

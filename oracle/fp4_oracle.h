@@ -153,6 +153,9 @@ void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
                   const uint32_t* u16, uint8_t* k_out);
 void fp4r_sr_u16_n(uint64_t seed, const uint64_t* idx, int64_t n,
                    uint32_t* out);
+/* The binary32 -> BF16 conversion of fp4r_dequantize's BF16 output (round
+ * to nearest even; NaN stays NaN), element by element. */
+void fp4r_f32_to_bf16_n(const float* in, int64_t n, uint16_t* out);
 int fp4r_max_threads(void);
 
 #ifdef __cplusplus

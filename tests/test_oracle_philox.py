@@ -1,36 +1,13 @@
 """Pins for the oracle's Philox4x32-10 generator and its use (CPU only).
 
 Known answers come live from rocRAND's header implementation of the same
-published generator (compiled here as a host-only test helper; it is never
-linked into the oracle or the HIP library).  Nothing from it is stored.
+published generator (the ``rocrand_kat`` fixture of conftest.py: a host-only
+test helper, never linked into the oracle or the HIP library).  Nothing from
+it is stored.
 """
-import os
-import shutil
-import subprocess
-
 import numpy as np
-import pytest
 
 import oracle
-
-HERE = os.path.dirname(os.path.abspath(__file__))
-KAT_SRC = os.path.join(HERE, "philox_kat", "rocrand_philox_kat.cpp")
-
-
-@pytest.fixture(scope="module")
-def rocrand_kat(tmp_path_factory):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand"):
-        pytest.skip("rocRAND headers / hipcc not available")
-    exe = str(tmp_path_factory.mktemp("kat") / "kat")
-    subprocess.run([hipcc, "--offload-host-only", "-O1", KAT_SRC, "-o", exe], check=True,
-                   capture_output=True)
-
-    def run(rows):
-        inp = "".join("%d %d %d %d %d\n" % tuple(r) for r in rows)
-        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True)
-        return [list(map(int, line.split())) for line in out.stdout.strip().splitlines()]
-    return run
 
 
 def test_philox_matches_rocrand(rocrand_kat):

@@ -2,10 +2,13 @@
 
 Closed-form worked examples of RHT + quantization, exact round trips of
 on-grid blocks, the transpose invariant, a brute-force quantizer for tiny
-tensors (argmin over candidate sets built from torch's E4M3 table), the
-nearest-level property, and the pages' directional claims.
+tensors (argmin over candidate sets built from torch's E4M3 table; the RHT
+as a float64 product with scipy's Hadamard matrix; SR decided in exact
+rationals on draws from rocRAND's Philox), the nearest-level property, and
+the pages' directional claims.
 """
 import ctypes
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -143,20 +146,72 @@ def _levels(fmt):
     return E2M1[:5] if fmt == "e2m1_cap2" else E2M1
 
 
-def _brute_quantize(x: np.ndarray, fmt: str):
-    """Independent scalar quantizer (no RHT, RTNE, row axis) for tiny inputs."""
+def _levels_exact(levels):
+    return [Fraction(float(v)) for v in levels]
+
+
+def _sr_up(m: np.float32, levels, u16: int) -> int:
+    """Magnitude code of m under SR with draw u16, in exact rationals: with
+    L[k] <= m < L[k+1] and p = (m - L[k]) / (L[k+1] - L[k]), the draw
+    U = (u16 + 2^-6) 2^-16 rounds up iff U <= p (TetraJet-v2 page, 2.A:
+    E[round(x)] = x); m past the top level saturates."""
+    L = _levels_exact(levels)
+    top = len(L) - 1
+    mf = Fraction(float(m))
+    if mf >= L[top]:
+        return top
+    k = max(i for i in range(top) if L[i] <= mf)
+    p = (mf - L[k]) / (L[k + 1] - L[k])
+    return k + 1 if Fraction(64 * u16 + 1, 1 << 22) <= p else k
+
+
+def _kat_signs(kat, seed):
+    """The RHT's 16 signs from rocRAND's generator: word 0 of Philox(key =
+    seed, counter = (0, 0, 1, 0)), bit j set: d_j = -1."""
+    w0 = kat([(seed, 0, 0, 1, 0)])[0][0]
+    return np.array([-1.0 if (w0 >> j) & 1 else 1.0 for j in range(16)])
+
+
+def _kat_draws(kat, seed, n_elems):
+    """16-bit SR draws of logical elements 0..n-1 from rocRAND's generator:
+    element n takes half n % 2 of word (n % 8) / 2 of Philox(key = seed,
+    counter = (n / 8, 0, 0))."""
+    groups = (n_elems + 7) // 8
+    words = kat([(seed, g & 0xFFFFFFFF, g >> 32, 0, 0) for g in range(groups)])
+    u = np.zeros(groups * 8, dtype=np.int64)
+    for g, w in enumerate(words):
+        for l in range(8):
+            u[8 * g + l] = (w[l >> 1] >> (16 * (l & 1))) & 0xFFFF
+    return u[:n_elems]
+
+
+def _brute_quantize(x: np.ndarray, fmt: str, rht: bool = False, signs=None,
+                    rounding: str = "rtne", draws=None):
+    """Independent scalar quantizer (row axis) for tiny inputs: the RHT as a
+    float64 product with scipy's Hadamard matrix (inputs are chosen so that
+    it is exact in binary32), E4M3 by nearest search in torch's table, E8M0
+    from log2, element codes by nearest level with ties to the even code or,
+    for SR, by the exact-rational rule of _sr_up on the given draws."""
     R, C = x.shape
     levels = _levels(fmt)
     B = 32 if fmt == "mxfp4" else 16
     table = _e4m3_table()
     G = np.float32(levels[-1])
-    s_t = np.float32(np.float32(np.abs(x).max()) / np.float32(G * np.float32(448)))
+    if rht:
+        a = x.astype(np.float64).reshape(R, C // 16, 16) * signs
+        y64 = 0.25 * np.einsum("rgj,ij->rgi", a, H16)
+        y = y64.astype(np.float32)
+        assert np.array_equal(y.astype(np.float64), y64), "input not exact under the RHT"
+        y = y.reshape(R, C)
+    else:
+        y = x.astype(np.float32)
+    s_t = np.float32(np.float32(np.abs(y).max()) / np.float32(G * np.float32(448)))
     codes = np.zeros((R, C), dtype=np.uint8)
     scales = np.zeros((R, C // B), dtype=np.uint8)
     for i in range(R):
         for b in range(C // B):
-            y = x[i, b * B:(b + 1) * B]
-            amax = np.float32(np.abs(y).max())
+            yb = y[i, b * B:(b + 1) * B]
+            amax = np.float32(np.abs(yb).max())
             if fmt == "mxfp4":
                 e = -127 if amax == 0 else max(-127, int(np.floor(np.log2(np.float64(amax)))) - 2)
                 S, d = e + 127, np.float32(2.0 ** e)
@@ -169,12 +224,16 @@ def _brute_quantize(x: np.ndarray, fmt: str):
                 d = np.float32(s_t * table[S]) if S else np.float32(0)
             scales[i, b] = S
             for j in range(B):
-                yj = y[j]
+                yj = yb[j]
                 k = 0
                 if d != 0 and yj != 0:
                     v = np.float32(yj * np.float32(np.float32(1) / d))
                     top = len(levels) - 1
-                    k = top if abs(v) >= levels[-1] else _nearest_tie_even(abs(float(v)), levels)
+                    if rounding == "sr":
+                        k = _sr_up(np.float32(abs(v)), levels, int(draws[i * C + b * B + j]))
+                    else:
+                        k = top if abs(v) >= levels[-1] else _nearest_tie_even(abs(float(v)),
+                                                                               levels)
                 codes[i, b * B + j] = (8 if np.signbit(yj) else 0) | k
     return codes, scales, s_t
 
@@ -189,6 +248,64 @@ def test_brute_force_tiny(fmt, kind):
     assert np.array_equal(scales, bs)
     if fmt != "mxfp4":
         assert ts == bts
+
+
+def _rht_exact_bf16(rows, cols, seed, spikes=False):
+    """BF16 inputs whose 16-point Hadamard sums are exact in binary32 in any
+    order: +-(1 + j/128) 2^e with e in [-4, 5] (every partial sum is a
+    multiple of 2^-11 below 2^11, within binary32's 24 bits), 10% zeros;
+    with spikes, 1% of entries at 2^8..2^9 and the rest at 2^-2 and up."""
+    rng = np.random.default_rng(seed)
+    lo = -2 if spikes else -4
+    mant = 1.0 + rng.integers(0, 128, (rows, cols)) / 128.0
+    e = rng.integers(lo, 6, (rows, cols))
+    a = mant * np.exp2(e) * rng.choice([-1.0, 1.0], (rows, cols))
+    a[rng.random((rows, cols)) < 0.1] = 0.0
+    if spikes:
+        sp = rng.random((rows, cols)) < 0.01
+        a[sp] = np.sign(rng.standard_normal(sp.sum())) * (1.0 + rng.integers(0, 128, sp.sum())
+                                                          / 128.0) * 256.0
+    return workloads.to_bf16_bits(a.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+@pytest.mark.parametrize("spikes", [False, True])
+def test_brute_force_tiny_rht_and_sr(rocrand_kat, fmt, rounding, spikes):
+    """RHT on (signs and SR draws taken from rocRAND's Philox, not the
+    oracle's), RTNE and SR: the oracle's codes, scale bytes and tensor scale
+    equal the brute-force quantizer's."""
+    rht_seed, sr_seed = 0x1234_5678_9AB, 0xFEDC_BA98_7654_3210
+    x = _rht_exact_bf16(4, 96 if fmt != "mxfp4" else 128, 31 + int(spikes), spikes)
+    R, C = x.shape
+    signs = _kat_signs(rocrand_kat, rht_seed)
+    draws = _kat_draws(rocrand_kat, sr_seed, R * C) if rounding == "sr" else None
+    codes, scales, ts = oracle.quantize(x, fmt, "row", rounding, True, rht_seed, sr_seed)
+    bc, bs, bts = _brute_quantize(workloads.bf16_bits_to_f32(x), fmt, True, signs, rounding,
+                                  draws)
+    assert np.array_equal(scales, bs)
+    assert np.array_equal(oracle.unpack_codes(codes), bc)
+    if fmt != "mxfp4":
+        assert ts == bts
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4"])
+def test_brute_force_tiny_sr_without_rht(rocrand_kat, fmt):
+    x = workloads.small_case("normal", 4, 64, 5)
+    draws = _kat_draws(rocrand_kat, 77, x.size)
+    codes, scales, ts = oracle.quantize(x, fmt, "row", "sr", False, 0, 77)
+    bc, bs, bts = _brute_quantize(x, fmt, rounding="sr", draws=draws)
+    assert np.array_equal(oracle.unpack_codes(codes), bc) and np.array_equal(scales, bs)
+    assert ts == bts
+
+
+def test_sr_draws_flip_codes():
+    """The SR brute-force check is not vacuous: on these inputs SR and RTNE
+    codes differ on a sizeable share of elements."""
+    x = _rht_exact_bf16(4, 96, 31)
+    rt = oracle.quantize(x, "nvfp4", "row", "rtne", True, 1, 2)[0]
+    sr = oracle.quantize(x, "nvfp4", "row", "sr", True, 1, 2)[0]
+    assert (oracle.unpack_codes(rt) != oracle.unpack_codes(sr)).mean() > 0.2
 
 
 # --------------------------------------------------------------------- properties
