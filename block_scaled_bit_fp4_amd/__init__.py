@@ -18,9 +18,17 @@ macro-scale array as its third result, as ``outer=True`` does).
 The two-level formats (NVFP4, the uniform grid, the cut E2M1) also take
 double-block scales (``outer=True``): one FP32 outer scale per 128 elements
 of each row of the quantized operand instead of the tensor scale.
+
+``stream`` (every call): None launches on torch's current stream; a
+``torch.cuda.Stream`` launches on it, and whatever the call allocates
+(outputs, the workspace, an uploaded tensor scale) is allocated with that
+stream current, so torch's caching allocator does not reuse those blocks
+while the kernels are queued; a raw ``hipStream_t`` handle (an int) is
+accepted only when every such buffer is passed in.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -120,6 +128,40 @@ def _stream(stream) -> int:
     return getattr(stream, "cuda_stream", stream)
 
 
+class _Alloc:
+    """Where a call's own buffers (outputs, workspace, an uploaded tensor
+    scale) come from.  They are allocated with ``stream`` current, so the
+    caching allocator ties each block to the stream the kernels run on and
+    does not hand it to other work while they are queued.  With a raw stream
+    handle the binding cannot do that, so such a call must bring every buffer
+    itself."""
+
+    def __init__(self, stream):
+        self.raw = stream is not None and not isinstance(stream, torch.cuda.Stream)
+        self.ctx = (torch.cuda.stream(stream) if isinstance(stream, torch.cuda.Stream)
+                    else contextlib.nullcontext())
+
+    def __enter__(self):
+        self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        return self.ctx.__exit__(*exc)
+
+    def _check(self, what):
+        if self.raw:
+            raise ValueError("%s would be allocated for a launch on a raw stream handle: pass a "
+                             "torch.cuda.Stream, or preallocate it" % what)
+
+    def empty(self, shape, dtype, device, what):
+        self._check(what)
+        return torch.empty(shape, dtype=dtype, device=device)
+
+    def scalar(self, v, device, what):
+        self._check(what)
+        return torch.tensor([float(v)], dtype=torch.float32, device=device)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -186,26 +228,28 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
     cshape, sshape = output_shapes(rows, cols, fmt, axis)
     dev = x.device
-    if codes is None:
-        codes = torch.empty(cshape, dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty(sshape, dtype=torch.uint8, device=dev)
-    ts = None
-    if outer:
-        ts = ts_out if ts_out is not None else torch.empty(
-            outer_shape(rows, cols, axis), dtype=torch.float32, device=dev)
-    elif fmt not in MX:
-        if given:
-            ts = tensor_scale if torch.is_tensor(tensor_scale) else torch.tensor(
-                [float(tensor_scale)], dtype=torch.float32, device=dev)
-        else:
-            ts = ts_out if ts_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
-    nws = workspace_bytes(rows, cols, p)
-    if nws and workspace is None:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-    st = load().fp4_quantize(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
-                             ctypes.byref(p), codes.data_ptr(), scales.data_ptr(), _ptr(ts),
-                             _ptr(workspace), _nbytes(workspace), _stream(stream))
+    with _Alloc(stream) as al:
+        if codes is None:
+            codes = al.empty(cshape, torch.uint8, dev, "codes")
+        if scales is None:
+            scales = al.empty(sshape, torch.uint8, dev, "scales")
+        ts = None
+        if outer:
+            ts = ts_out if ts_out is not None else al.empty(
+                outer_shape(rows, cols, axis), torch.float32, dev, "the outer-scale array")
+        elif fmt not in MX:
+            if given:
+                ts = tensor_scale if torch.is_tensor(tensor_scale) else al.scalar(
+                    tensor_scale, dev, "the given tensor scale")
+            else:
+                ts = ts_out if ts_out is not None else al.empty(1, torch.float32, dev,
+                                                                "the tensor scale")
+        nws = workspace_bytes(rows, cols, p)
+        if nws and workspace is None:
+            workspace = al.empty(nws, torch.uint8, dev, "the workspace")
+        st = load().fp4_quantize(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
+                                 ctypes.byref(p), codes.data_ptr(), scales.data_ptr(), _ptr(ts),
+                                 _ptr(workspace), _nbytes(workspace), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize")
     return codes, scales, ts
@@ -229,31 +273,32 @@ def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", r
     p = make_params(fmt, "row", rounding, rht, rht_seed, sr_seed, given, outer)
     dev = x.device
     outs = []
-    for axis, pre in (("row", out_row), ("col", out_col)):
-        if pre is not None:
-            outs.append(tuple(pre))
-            continue
-        cshape, sshape = output_shapes(rows, cols, fmt, axis)
-        ts = None
-        if outer:
-            ts = torch.empty(outer_shape(rows, cols, axis), dtype=torch.float32, device=dev)
-        elif fmt not in MX:
-            if given:
-                v = tensor_scale[0 if axis == "row" else 1]
-                ts = v if torch.is_tensor(v) else torch.tensor([float(v)], dtype=torch.float32,
-                                                                device=dev)
-            else:
-                ts = torch.empty(1, dtype=torch.float32, device=dev)
-        outs.append((torch.empty(cshape, dtype=torch.uint8, device=dev),
-                     torch.empty(sshape, dtype=torch.uint8, device=dev), ts))
-    nws = workspace_bytes_dual(rows, cols, p)
-    if nws and workspace is None:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
-    (cr, sr_, tr), (cc, sc, tc) = outs
-    st = load().fp4_quantize_dual(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
-                                  ctypes.byref(p), cr.data_ptr(), sr_.data_ptr(), _ptr(tr),
-                                  cc.data_ptr(), sc.data_ptr(), _ptr(tc), _ptr(workspace),
-                                  _nbytes(workspace), _stream(stream))
+    with _Alloc(stream) as al:
+        for axis, pre in (("row", out_row), ("col", out_col)):
+            if pre is not None:
+                outs.append(tuple(pre))
+                continue
+            cshape, sshape = output_shapes(rows, cols, fmt, axis)
+            ts = None
+            if outer:
+                ts = al.empty(outer_shape(rows, cols, axis), torch.float32, dev,
+                              "the outer-scale array")
+            elif fmt not in MX:
+                if given:
+                    v = tensor_scale[0 if axis == "row" else 1]
+                    ts = v if torch.is_tensor(v) else al.scalar(v, dev, "the given tensor scale")
+                else:
+                    ts = al.empty(1, torch.float32, dev, "the tensor scale")
+            outs.append((al.empty(cshape, torch.uint8, dev, "codes"),
+                         al.empty(sshape, torch.uint8, dev, "scales"), ts))
+        nws = workspace_bytes_dual(rows, cols, p)
+        if nws and workspace is None:
+            workspace = al.empty(nws, torch.uint8, dev, "the workspace")
+        (cr, sr_, tr), (cc, sc, tc) = outs
+        st = load().fp4_quantize_dual(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0),
+                                      ctypes.byref(p), cr.data_ptr(), sr_.data_ptr(), _ptr(tr),
+                                      cc.data_ptr(), sc.data_ptr(), _ptr(tc), _ptr(workspace),
+                                      _nbytes(workspace), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize_dual")
     return outs[0], outs[1]
@@ -267,8 +312,9 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: in
     ``tensor_scale`` is the outer-scale array of the double-block mode."""
     outer = torch.is_tensor(tensor_scale) and tensor_scale.dim() == 2
     p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, not outer, outer)
-    if out is None:
-        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    with _Alloc(stream) as al:
+        if out is None:
+            out = al.empty((rows, cols), out_dtype, codes.device, "out")
     if out.dtype not in DTYPES:
         raise TypeError("out must be bfloat16 or float32")
     st = load().fp4_dequantize(codes.data_ptr(), scales.data_ptr(), _ptr(tensor_scale), rows,
@@ -290,8 +336,9 @@ def gemm_mx(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor
     if kh != kh2:
         raise ValueError("A and B must have the same K")
     K = 2 * kh
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    with _Alloc(stream) as al:
+        if out is None:
+            out = al.empty((M, N), out_dtype, a_codes.device, "out")
     if out.dtype not in DTYPES:
         raise TypeError("out must be bfloat16 or float32")
     st = load().fp4_gemm_mx(a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(),
@@ -307,8 +354,9 @@ def rht(x: torch.Tensor, axis: str = "row", seed: int = 0, inverse: bool = False
     """Standalone 16-point RHT (or its inverse) along an axis; FP32 output."""
     _check_2d(x, "x")
     rows, cols = x.shape
-    if out is None:
-        out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    with _Alloc(stream) as al:
+        if out is None:
+            out = al.empty((rows, cols), torch.float32, x.device, "out")
     st = load().fp4_rht(x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0), AXES[axis],
                         int(seed) & (2**64 - 1), int(bool(inverse)), out.data_ptr(),
                         _stream(stream))

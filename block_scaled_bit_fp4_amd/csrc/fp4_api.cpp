@@ -108,12 +108,15 @@ uint64_t next_call_tag() {
   return t;
 }
 
-// Microseconds a workgroup of the single-pass row kernel waits for the
+// Microseconds workgroup 0 of the single-pass row kernel waits for the
 // other workgroups' partial maxima before computing the missing ones
-// itself (FP4_AMAX_WAIT_US; 0 makes every wait end at once).
-uint32_t amax_wait_us() {
+// itself: FP4_AMAX_WAIT_US if set (0 makes every wait end at once), else
+// 10 us plus the time to read the operand at 2.5 TB/s, several times what
+// the loads take when the whole grid is resident (about 6 us for a
+// 4096 x 4096 BF16 operand).
+uint32_t amax_wait_us(int64_t operand_bytes) {
   const char* e = std::getenv("FP4_AMAX_WAIT_US");
-  if (!e || !*e) return 500u;
+  if (!e || !*e) return 10u + (uint32_t)(operand_bytes / 2500000);
   const long v = std::strtol(e, nullptr, 10);
   return v < 0 ? 0u : (v > 1000000 ? 1000000u : (uint32_t)v);
 }
@@ -192,7 +195,7 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
     capturing = cap != hipStreamCaptureStatusNone;
   }
   q.call_tag = capturing ? 0 : next_call_tag();
-  q.wait_us = amax_wait_us();
+  q.wait_us = amax_wait_us(rows * cols * (int64_t)elem_size(in_dtype));
   return finish(fp4_launch_quantize(q, s), s);
 }
 

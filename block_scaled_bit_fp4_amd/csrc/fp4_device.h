@@ -335,16 +335,23 @@ __device__ __forceinline__ uint32_t swap_lane_pair(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
-// Block-wide max over a 256-thread workgroup; every thread gets the result.
-__device__ __forceinline__ float block_max_256(float v) {
-  __shared__ float red[4];
+// Block-wide max over a workgroup of NT threads (a multiple of 64, at most
+// 1024); every thread gets the result.
+template <int NT>
+__device__ __forceinline__ float block_max(float v) {
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
+  constexpr int kWaves = NT / 64;
+  __shared__ float red[kWaves];
   v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
   __syncthreads();
-  return v;
+  return m;
 }
+
+__device__ __forceinline__ float block_max_256(float v) { return block_max<256>(v); }
 
 }  // namespace fp4dev

@@ -29,7 +29,7 @@ struct QuantLaunch {
   float* workspace;
   size_t ws_bytes;
   uint64_t call_tag;  // unique per call (single-pass exchange); 0: two-pass only
-  uint32_t wait_us;   // single-pass wait before a workgroup computes what is missing
+  uint32_t wait_us;   // single-pass: workgroup 0's wait before it computes what is missing
 };
 
 // Row-axis and column-axis quantization of one BF16 x in one pass

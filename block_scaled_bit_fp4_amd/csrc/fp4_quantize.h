@@ -304,11 +304,13 @@ __device__ __forceinline__ uint32_t encode8_careful(const float* y, float inv,
 // ([MXFP4] 2.A): e places amax_b / 2^e in (3.5, 7].
 // With BF16 input every RHT partial sum is a multiple of 2^-133, so y = t/4
 // is exact and, while inv >= 2^-124, v = t * (inv / 4) equals y * inv.
-template <int FMT, bool SR, bool RHT, bool BF16IN, int B, int TSM>
+// SR draws: computed here from (k0, k1, n0), or with PRE taken from pre[],
+// the Philox words of the block's B/8 groups, drawn earlier by the caller.
+template <int FMT, bool SR, bool RHT, bool BF16IN, int B, int TSM, bool PRE = false>
 __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, const ScaleCtx& c,
                                              const float* inv_tab, uint32_t k0, uint32_t k1,
                                              uint64_t n0, uint32_t (&packed)[B / 8],
-                                             uint32_t& sbyte) {
+                                             uint32_t& sbyte, const uint32_t* pre = nullptr) {
   constexpr bool kFold = RHT && BF16IN;
   const float amax_b = RHT ? amax_t * 0.25f : amax_t;
   float inv;
@@ -345,7 +347,9 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
 #pragma unroll
   for (int q = 0; q < B / 8; ++q) {
     uint32_t r[4] = {0u, 0u, 0u, 0u};
-    if constexpr (SR) {
+    if constexpr (SR && PRE) {
+      r[0] = pre[4 * q]; r[1] = pre[4 * q + 1]; r[2] = pre[4 * q + 2]; r[3] = pre[4 * q + 3];
+    } else if constexpr (SR) {
       const uint64_t g = (n0 >> 3) + (uint64_t)q;
       const u32x4 o = philox4x32_10(k0, k1, (uint32_t)g, (uint32_t)(g >> 32), 0u, 0u);
       r[0] = o.x; r[1] = o.y; r[2] = o.z; r[3] = o.w;
@@ -558,14 +562,14 @@ __device__ __forceinline__ float unit_absmax(const RowRaw<T, U>& r, uint32_t sig
 
 // Partial maximum of workgroup j, recomputed from the input by the whole
 // calling workgroup (the value workgroup j posts).
-template <bool RHT, typename T, int U, int NU>
+template <bool RHT, typename T, int U, int NU, int NT>
 __device__ float partial_of(const T* __restrict__ x, const QuantArgs& a, int64_t j,
                             int64_t stride) {
   const int64_t units = a.n_major * a.M;
   float m = 0.0f;
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const int64_t u = j * kThreads + threadIdx.x + k * stride;
+    const int64_t u = j * NT + threadIdx.x + k * stride;
     if (u < units) {
       const int64_t row = u / a.M, minor = u - row * a.M;
       RowRaw<T, U> r;
@@ -573,30 +577,30 @@ __device__ float partial_of(const T* __restrict__ x, const QuantArgs& a, int64_t
       m = fmaxf(m, unit_absmax<RHT, T, U>(r, a.signs));
     }
   }
-  m = block_max_256(m);
+  m = block_max<NT>(m);
   return RHT ? m * 0.25f : m;
 }
 
 // Tensor maximum from the posted slots [0, n), waiting up to wait_ticks of
 // the constant-rate clock; slots still missing then are computed here.
 // Block-uniform control flow (partial_of synchronises the workgroup).
-template <bool RHT, typename T, int U, int NU>
+template <bool RHT, typename T, int U, int NU, int NT>
 __device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxSlot* slots, int n,
                               uint64_t tag, uint64_t wait_ticks, int64_t stride) {
-  constexpr int kPer = kAmaxPartials / kThreads;
+  constexpr int kPer = (kAmaxPartials + NT - 1) / NT;
   __shared__ int missing[kAmaxPartials];
   __shared__ int nmissing;
   float m = 0.0f;
   uint32_t pending = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if ((int)threadIdx.x + i * kThreads < n) pending |= 1u << i;
+    if ((int)threadIdx.x + i * NT < n) pending |= 1u << i;
   const uint64_t t0 = wall_clock64();
   while (true) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       float v;
-      if ((pending >> i) & 1u && read_slot(slots + threadIdx.x + i * kThreads, tag, v)) {
+      if ((pending >> i) & 1u && read_slot(slots + threadIdx.x + i * NT, tag, v)) {
         m = fmaxf(m, v);
         pending &= ~(1u << i);
       }
@@ -609,51 +613,87 @@ __device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxS
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if ((pending >> i) & 1u) missing[atomicAdd(&nmissing, 1)] = threadIdx.x + i * kThreads;
+    if ((pending >> i) & 1u) missing[atomicAdd(&nmissing, 1)] = threadIdx.x + i * NT;
   __syncthreads();
   const int nm = nmissing;
-  for (int i = 0; i < nm; ++i) m = fmaxf(m, partial_of<RHT, T, U, NU>(x, a, missing[i], stride));
-  return block_max_256(m);
+  for (int i = 0; i < nm; ++i)
+    m = fmaxf(m, partial_of<RHT, T, U, NU, NT>(x, a, missing[i], stride));
+  return block_max<NT>(m);
 }
 
-template <int FMT, bool SR, bool RHT, typename T, int U, int NU>
-__global__ __launch_bounds__(kThreads) void quantize_row_single_kernel(
-    const T* __restrict__ x, QuantArgs a, AmaxSlot* slots, uint64_t tag, uint64_t wait_ticks) {
+// NT lanes per workgroup, NU units of U elements per lane.  With stochastic
+// rounding the Philox words of a lane's units are drawn into LDS (dynamic,
+// NT * NU * U / 8 * 16 bytes) right after its loads are issued: that VALU
+// work then runs while the loads are in flight instead of after the
+// exchange.  Layout [group of 8 elements][lane], 16 bytes per entry, so the
+// writes and reads of a wave are contiguous.
+//
+// Waits: workgroup 0 waits wait_ticks for every slot, then computes the
+// missing partial maxima itself and posts the tensor maximum; the other
+// workgroups wait up to long_ticks (longer) for that result, so that in the
+// normal course only workgroup 0 recomputes anything, and compute what they
+// miss themselves only if it never comes (workgroup 0 not resident).
+template <int FMT, bool SR, bool RHT, typename T, int U, int NU, int NT>
+__global__ __launch_bounds__(NT) void quantize_row_single_kernel(
+    const T* __restrict__ x, QuantArgs a, AmaxSlot* slots, uint64_t tag, uint64_t wait_ticks,
+    uint64_t long_ticks) {
   constexpr int B = block_of<FMT>();
   constexpr int NBU = U / B;
+  constexpr int GPU = U / 8;  // Philox groups (8 elements each) per unit
+  extern __shared__ uint4 draws[];
   __shared__ float inv_tab[128];
   __shared__ float shared_amax;
   __shared__ int shared_have;
   const int64_t units = a.n_major * a.M;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t u0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * NT;
+  const int64_t u0 = (int64_t)blockIdx.x * NT + threadIdx.x;
   // Everything that does not depend on the tensor scale is done before the
   // exchange: the units' widened (and rotated) values and their block
   // maxima stay in registers for the coding after it.
+  RowRaw<T, U> raw[NU];
+  int64_t rowk[NU], minork[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int64_t u = u0 + k * stride;
+    rowk[k] = u / a.M;
+    minork[k] = u - rowk[k] * a.M;
+    if (u < units) {
+      raw[k].load(x + rowk[k] * a.ld + minork[k] * U);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RowRaw<T, U>::kVec; ++i) raw[k].q[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if constexpr (SR) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const uint64_t g0 = ((uint64_t)rowk[k] * (uint64_t)a.W + (uint64_t)(minork[k] * U)) >> 3;
+#pragma unroll
+      for (int q = 0; q < GPU; ++q) {
+        const uint64_t g = g0 + (uint64_t)q;
+        const u32x4 o = philox4x32_10(a.sr_k0, a.sr_k1, (uint32_t)g, (uint32_t)(g >> 32), 0u, 0u);
+        draws[(k * GPU + q) * NT + threadIdx.x] = make_uint4(o.x, o.y, o.z, o.w);
+      }
+    }
+  }
+  // With the RHT the rotated values are kept (the butterfly is not redone);
+  // without it the raw words are kept and widened again for the coding
+  // (half the registers for BF16).
   float t[NU][NBU][B];
   float bam[NU][NBU];
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
-    const int64_t u = u0 + k * stride;
-    RowRaw<T, U> raw;
-    if (u < units) {
-      const int64_t row = u / a.M, minor = u - row * a.M;
-      raw.load(x + row * a.ld + minor * U);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RowRaw<T, U>::kVec; ++i) raw.q[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
 #pragma unroll
     for (int bi = 0; bi < NBU; ++bi) {
       bam[k][bi] = 0.0f;
 #pragma unroll
       for (int h = 0; h < B / 16; ++h) {
         float g[16];
-        raw.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+        raw[k].template group<RHT>(bi * (B / 16) + h, g, a.signs);
         if (RHT) fwht16(g);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          t[k][bi][16 * h + j] = g[j];
+          if (RHT) t[k][bi][16 * h + j] = g[j];
           bam[k][bi] = fmaxf(bam[k][bi], fabsf(g[j]));
         }
       }
@@ -664,32 +704,39 @@ __global__ __launch_bounds__(kThreads) void quantize_row_single_kernel(
   for (int k = 0; k < NU; ++k)
 #pragma unroll
     for (int bi = 0; bi < NBU; ++bi) m = fmaxf(m, bam[k][bi]);  // 0 past the last unit
-  m = block_max_256(m);
+  m = block_max<NT>(m);
   if (threadIdx.x == 0) post_slot(slots + blockIdx.x, RHT ? m * 0.25f : m, tag);
 
   AmaxSlot* result = slots + kAmaxPartials;
-  float amax = 0.0f;
-  bool have = false;
-  if (blockIdx.x != 0) {
+  float amax;
+  if (blockIdx.x == 0) {
+    amax = gather_slots<RHT, T, U, NU, NT>(x, a, slots, gridDim.x, tag, wait_ticks, stride);
+    if (threadIdx.x == 0) post_slot(result, amax, tag);
+  } else {
     if (threadIdx.x == 0) {
       const uint64_t t0 = wall_clock64();
       float v = 0.0f;
       bool ok;
-      while (!(ok = read_slot(result, tag, v)) && wall_clock64() - t0 < wait_ticks)
+      while (!(ok = read_slot(result, tag, v)) && wall_clock64() - t0 < long_ticks)
         __builtin_amdgcn_s_sleep(2);
       shared_amax = v;
       shared_have = ok;
     }
     __syncthreads();
-    have = shared_have;
     amax = shared_amax;
+    if (!shared_have)  // workgroup 0 never posted: take what is posted, compute the rest
+      amax = gather_slots<RHT, T, U, NU, NT>(x, a, slots, gridDim.x, tag, 0, stride);
   }
-  if (!have) {
-    // workgroup 0 waits for every slot; a workgroup whose wait ran out
-    // takes what is posted and computes the rest at once
-    amax = gather_slots<RHT, T, U, NU>(x, a, slots, gridDim.x, tag,
-                                       blockIdx.x == 0 ? wait_ticks : 0, stride);
-    if (blockIdx.x == 0 && threadIdx.x == 0) post_slot(result, amax, tag);
+
+  if constexpr (!RHT) {
+    // opaque to the compiler, so that it widens the raw words again below
+    // instead of keeping the widened values of the first pass alive
+#pragma unroll
+    for (int k = 0; k < NU; ++k)
+#pragma unroll
+      for (int i = 0; i < RowRaw<T, U>::kVec; ++i)
+        asm volatile("" : "+v"(raw[k].q[i].x), "+v"(raw[k].q[i].y), "+v"(raw[k].q[i].z),
+                     "+v"(raw[k].q[i].w));
   }
 
   // the two-level scale from the tensor maximum, as in scale_prologue
@@ -707,15 +754,36 @@ __global__ __launch_bounds__(kThreads) void quantize_row_single_kernel(
   for (int k = 0; k < NU; ++k) {
     const int64_t u = u0 + k * stride;
     if (u < units) {
-      const int64_t row = u / a.M, minor = u - row * a.M;
+      const int64_t row = rowk[k], minor = minork[k];
       uint32_t packed[U / 8];
       uint32_t sb[NBU];
 #pragma unroll
       for (int bi = 0; bi < NBU; ++bi) {
         const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * U + bi * B);
+        uint32_t pre[B / 2];
+        if constexpr (SR) {
+#pragma unroll
+          for (int q = 0; q < B / 8; ++q) {
+            const uint4 w = draws[(k * GPU + bi * (B / 8) + q) * NT + threadIdx.x];
+            pre[4 * q] = w.x; pre[4 * q + 1] = w.y; pre[4 * q + 2] = w.z; pre[4 * q + 3] = w.w;
+          }
+        }
         uint32_t pk[B / 8];
-        encode_block<FMT, SR, RHT, sizeof(T) == 2, B, kTsCompute>(
-            t[k][bi], bam[k][bi], c, inv_tab, a.sr_k0, a.sr_k1, n0, pk, sb[bi]);
+        if constexpr (RHT) {
+          encode_block<FMT, SR, RHT, sizeof(T) == 2, B, kTsCompute, true>(
+              t[k][bi], bam[k][bi], c, inv_tab, a.sr_k0, a.sr_k1, n0, pk, sb[bi], pre);
+        } else {
+          float tb[B];
+#pragma unroll
+          for (int h = 0; h < B / 16; ++h) {
+            float g[16];
+            raw[k].template group<false>(bi * (B / 16) + h, g, 0u);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) tb[16 * h + j] = g[j];
+          }
+          encode_block<FMT, SR, RHT, sizeof(T) == 2, B, kTsCompute, true>(
+              tb, bam[k][bi], c, inv_tab, a.sr_k0, a.sr_k1, n0, pk, sb[bi], pre);
+        }
 #pragma unroll
         for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
       }
@@ -1368,24 +1436,61 @@ uint64_t wall_ticks_per_us() {
 #define FP4_SINGLE_PASS 1
 #endif
 
-// The single-pass row path: the smallest NU whose grid (one unit per lane
-// per k) is resident at once and has at most kAmaxPartials workgroups.
-// False when the operand does not fit; nothing is launched then.
-template <int FMT, bool SR, bool RHT, typename T, int NU>
+// Dynamic LDS of the single-pass kernel: the SR draws of every lane.
+template <bool SR, int U, int NU, int NT>
+constexpr size_t single_pass_lds() {
+  return SR ? (size_t)NT * NU * (U / 8) * 16 : 0;
+}
+
+// Workgroups of a kernel with NT lanes and `lds` bytes of dynamic LDS that
+// the device holds at once; cached per kernel and device (0: unknown).
+int64_t resident_wgs_nt(const void* kernel, int nt, size_t lds) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache[dev].find(kernel);
+  if (it != cache[dev].end()) return it->second;
+  if (lds > 65536 &&
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+          hipSuccess)
+    (void)hipGetLastError();  // the launch itself reports a real limit
+  int per_cu = 0, cus = 0;
+  int64_t n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, lds) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    n = (int64_t)per_cu * cus;
+  else
+    (void)hipGetLastError();
+  cache[dev][kernel] = n;
+  return n;
+}
+
+// The single-pass row path with NT lanes per workgroup and NU units per
+// lane, when its grid (one unit per lane per k) is resident at once and has
+// at most kAmaxPartials workgroups.  False when the operand does not fit;
+// nothing is launched then.
+template <int FMT, bool SR, bool RHT, typename T, int NU, int NT>
 bool try_single_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   constexpr int U = 32;
-  auto kernel = quantize_row_single_kernel<FMT, SR, RHT, T, U, NU>;
+  auto kernel = quantize_row_single_kernel<FMT, SR, RHT, T, U, NU, NT>;
+  constexpr size_t lds = single_pass_lds<SR, U, NU, NT>();
   const int64_t units = q.rows * (q.cols / U);
-  const int64_t grid = (units + (int64_t)kThreads * NU - 1) / ((int64_t)kThreads * NU);
-  const int64_t cap = resident_wgs(reinterpret_cast<const void*>(kernel));
+  const int64_t grid = (units + (int64_t)NT * NU - 1) / ((int64_t)NT * NU);
+  const int64_t cap = resident_wgs_nt(reinterpret_cast<const void*>(kernel), NT, lds);
   if (grid < 1 || grid > kAmaxPartials || grid > cap) return false;
   a.W = q.cols;
   a.n_major = q.rows;
   a.M = q.cols / U;
   AmaxSlot* slots = reinterpret_cast<AmaxSlot*>(q.workspace);
-  const uint64_t ticks = (uint64_t)q.wait_us * wall_ticks_per_us();
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     static_cast<const T*>(q.x), a, slots, q.call_tag, ticks);
+  const uint64_t per_us = wall_ticks_per_us();
+  const uint64_t ticks = (uint64_t)q.wait_us * per_us;
+  // the other workgroups wait for workgroup 0's result past its own
+  // deadline plus time to recompute up to every partial maximum
+  const uint64_t long_ticks = 4 * ticks + 64 * per_us;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), lds, s,
+                     static_cast<const T*>(q.x), a, slots, q.call_tag, ticks, long_ticks);
   return true;
 }
 
@@ -1407,9 +1512,9 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   if constexpr (!is_mx(FMT) && FMT != kMBS && TSM == kTsCompute) {
     if (FP4_SINGLE_PASS && q.axis == 0 && q.cols % 32 == 0 && q.call_tag != 0 &&
         q.ws_bytes >= kSinglePassWsBytes &&
-        (try_single_pass<FMT, SR, RHT, T, 1>(q, a, s) ||
-         try_single_pass<FMT, SR, RHT, T, 2>(q, a, s) ||
-         try_single_pass<FMT, SR, RHT, T, 4>(q, a, s)))
+        (try_single_pass<FMT, SR, RHT, T, 1, 1024>(q, a, s) ||
+         (sizeof(T) == 2 && try_single_pass<FMT, SR, RHT, T, 2, 1024>(q, a, s)) ||
+         try_single_pass<FMT, SR, RHT, T, 4, 256>(q, a, s)))
       return hipGetLastError();
   }
   if (!is_mx(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);

@@ -1,10 +1,12 @@
 """The single-pass row path of a computed tensor scale (row axis,
 width a multiple of 32, operand small enough to stay in the registers of one
 resident grid): byte parity with the oracle and with the two-pass path, at
-grids of 1, 2 and 4 units per lane, after the workspace held other bytes,
-and with the waits cut to zero so that workgroups compute the partial
-maxima they did not see posted.  The two-pass path is selected by a
-workspace of kAmaxPartials floats, too small for the slot exchange."""
+grids of 1 and 2 units per lane, after the workspace held other bytes, with
+the waits cut to zero so that workgroups compute the partial maxima they did
+not see posted, and beside long kernels on another stream that hold the
+compute units (not every workgroup resident at once): parity and a bounded
+call time.  The two-pass path is selected by a workspace of kAmaxPartials
+floats, too small for the slot exchange."""
 import numpy as np
 import pytest
 import torch
@@ -29,11 +31,10 @@ def _bf16(shape, seed, kind="normal"):
     return workloads.to_bf16_bits(workloads.small_case(kind, shape[0], shape[1], seed))
 
 
-# With the RHT: (2048, 4096) one unit per lane on 1024 workgroups, (4096,
-# 4096) two; without it (more registers per unit) the uniform grid takes
-# four units per lane at (4096, 4096).  (4096, 8192) does not fit one
-# resident grid: both sides are the two-pass path there.  (1056, 352): a
-# ragged last workgroup.
+# 1024-lane workgroups: (2048, 4096) one unit per lane on 256 workgroups,
+# (4096, 4096) two units per lane (with and without the RHT).  (4096, 8192)
+# does not fit one resident grid: both sides are the two-pass path there.
+# (1056, 352): a ragged last workgroup.
 @pytest.mark.parametrize("shape", [(1056, 352), (2048, 4096), (4096, 4096), (4096, 8192)])
 @pytest.mark.parametrize("fmt,rounding,rht", [("nvfp4", "rtne", True), ("nvfp4", "sr", True),
                                               ("ufp4", "rtne", False), ("e2m1_cap2", "sr", True)])
@@ -96,3 +97,42 @@ def test_single_pass_fp32_input(shape, rounding, rht):
     assert_bytes_equal(a[0], b[0], "codes single vs two-pass")
     assert_bytes_equal(a[1], b[1], "scales single vs two-pass")
     assert a[2] == b[2]
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+@pytest.mark.parametrize("wait_us", [None, "1"])
+def test_single_pass_beside_a_busy_stream(monkeypatch, rounding, wait_us):
+    """A same-priority stream runs a sequence of float32 matrix products
+    (finite kernels, a few milliseconds in all) that hold compute units while
+    the single-pass call is launched on the current stream.  Workgroups that
+    are not resident at first, and waits that give up (a 1 us wait forces
+    the recomputation of missing partial maxima), still give the oracle's
+    bytes, and the call ends within the products' time plus a margin."""
+    if wait_us is not None:
+        monkeypatch.setenv("FP4_AMAX_WAIT_US", wait_us)
+    x = _bf16((4096, 4096), 77, "outlier_cols")
+    xd = to_device(x)
+    a = torch.randn(4096, 4096, device=DEV)
+    b = torch.randn(4096, 4096, device=DEV)
+    busy = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    note("single pass beside a busy stream: %s wait=%s" % (rounding, wait_us))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    with torch.cuda.stream(busy):
+        ev[0].record(busy)
+        for _ in range(6):
+            torch.mm(a, b)
+        ev[1].record(busy)
+    cur = torch.cuda.current_stream()
+    ev[2].record(cur)
+    c, s, ts = fp4.quantize(xd, "nvfp4", "row", rounding, True, 7, 11)
+    ev[3].record(cur)
+    torch.cuda.synchronize()
+    busy_ms = ev[0].elapsed_time(ev[1])
+    call_ms = ev[2].elapsed_time(ev[3])
+    note("  products %.2f ms, quantize call %.3f ms" % (busy_ms, call_ms))
+    oc, osc, ots = oracle.quantize(x, "nvfp4", "row", rounding, True, 7, 11)
+    assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots)
+    assert_bytes_equal(to_host(s), osc, "scales beside a busy stream")
+    assert_bytes_equal(to_host(c), oc, "codes beside a busy stream")
+    assert call_ms < busy_ms + 20.0
