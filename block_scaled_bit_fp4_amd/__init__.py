@@ -57,7 +57,7 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_NULL", -2: "FP4_ERR_FORMAT", -3: "FP4_ERR_SH
 # every symbol include/fp4.h declares
 EXPORTS = ("fp4_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_rht",
            "fp4_rht_signs", "fp4_status_str", "fp4_workspace_bytes_dual", "fp4_quantize_dual",
-           "fp4_gemm_mx")
+           "fp4_gemm_mx", "fp4_quantize_noalloc")
 
 
 class FP4Error(RuntimeError):
@@ -96,6 +96,8 @@ def load():
         L.fp4_workspace_bytes.restype = sz
         L.fp4_quantize.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, sz, vp]
         L.fp4_quantize.restype = i32
+        L.fp4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp]
+        L.fp4_quantize_noalloc.restype = i32
         L.fp4_workspace_bytes_dual.argtypes = [i64, i64, P]
         L.fp4_workspace_bytes_dual.restype = sz
         L.fp4_quantize_dual.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, vp, vp, vp,
@@ -252,6 +254,50 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
                                  _ptr(workspace), _nbytes(workspace), _stream(stream))
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize")
+    return codes, scales, ts
+
+
+def quantize_noalloc(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row",
+                     rounding: str = "rtne", rht: bool = False, rht_seed: int = 0,
+                     sr_seed: int = 0, tensor_scale=None, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None,
+                     ts_out: Optional[torch.Tensor] = None, stream=None, outer: bool = False):
+    """``quantize`` through the allocation-free entry point: the library
+    takes no workspace and allocates nothing (its records live in a fixed
+    per-device array, shared by every such call on the device, so calls
+    that overlap in time on one device race).  Outputs not passed in are
+    allocated here, as ``quantize`` does; a caller that must not allocate
+    passes all of them (and a device tensor as a given tensor scale)."""
+    _check_2d(x, "x")
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
+    given = tensor_scale is not None and not outer
+    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
+    cshape, sshape = output_shapes(rows, cols, fmt, axis)
+    dev = x.device
+    with _Alloc(stream) as al:
+        if codes is None:
+            codes = al.empty(cshape, torch.uint8, dev, "codes")
+        if scales is None:
+            scales = al.empty(sshape, torch.uint8, dev, "scales")
+        ts = None
+        if outer:
+            ts = ts_out if ts_out is not None else al.empty(
+                outer_shape(rows, cols, axis), torch.float32, dev, "the outer-scale array")
+        elif fmt not in MX:
+            if given:
+                ts = tensor_scale if torch.is_tensor(tensor_scale) else al.scalar(
+                    tensor_scale, dev, "the given tensor scale")
+            else:
+                ts = ts_out if ts_out is not None else al.empty(1, torch.float32, dev,
+                                                                "the tensor scale")
+        st = load().fp4_quantize_noalloc(x.data_ptr(), DTYPES[x.dtype], rows, cols,
+                                         x.stride(0), ctypes.byref(p), codes.data_ptr(),
+                                         scales.data_ptr(), _ptr(ts), _stream(stream))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_quantize_noalloc")
     return codes, scales, ts
 
 

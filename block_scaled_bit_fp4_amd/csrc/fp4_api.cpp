@@ -7,6 +7,7 @@
 #include <chrono>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <random>
 
 #include "fp4.h"
@@ -121,6 +122,56 @@ uint32_t amax_wait_us(int64_t operand_bytes) {
   return v < 0 ? 0u : (v > 1000000 ? 1000000u : (uint32_t)v);
 }
 
+// Every argument check of fp4_quantize but the workspace's.
+fp4_status check_quantize_args(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                               int64_t ld, const fp4_params* p, const uint8_t* codes,
+                               const uint8_t* scales, const float* tensor_scale) {
+  fp4_status st = check_params(p);
+  if (st != FP4_OK) return st;
+  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if ((st = check_shape(p, rows, cols, ld)) != FP4_OK) return st;
+  const bool empty = rows == 0 || cols == 0;
+  if (two_level(p) && !tensor_scale) return FP4_ERR_NULL;
+  if (!empty) {
+    if (!x || !codes || !scales) return FP4_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FP4_ERR_ALIGN;
+    if ((ld * (int64_t)elem_size(in_dtype)) % 16) return FP4_ERR_ALIGN;
+  }
+  return FP4_OK;
+}
+
+// The allocation-free entry point's workspace: a fixed array in the
+// library's device memory (each device holds its own copy until the process
+// ends).  Host code never passes `scratch` itself to a kernel -- on the host
+// that name is a stand-in, not a device address -- but the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on its first call.
+static __device__ __align__(256) unsigned char scratch[FP4_NOALLOC_SCRATCH_BYTES];
+static_assert(FP4_NOALLOC_SCRATCH_BYTES >= kSinglePassWsBytes,
+              "the scratch holds the single-pass exchange records");
+static_assert(FP4_NOALLOC_SCRATCH_BYTES >= sizeof(float) * (size_t)kAmaxPartials,
+              "the scratch holds the two-pass partial maxima");
+
+void* scratch_address() {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,17 +193,10 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
                         int64_t ld, const fp4_params* p, uint8_t* codes, uint8_t* scales,
                         float* tensor_scale, void* workspace, size_t ws_bytes,
                         void* stream) {
-  fp4_status st = check_params(p);
+  fp4_status st = check_quantize_args(x, in_dtype, rows, cols, ld, p, codes, scales,
+                                      tensor_scale);
   if (st != FP4_OK) return st;
-  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
-  if ((st = check_shape(p, rows, cols, ld)) != FP4_OK) return st;
   const bool empty = rows == 0 || cols == 0;
-  if (two_level(p) && !tensor_scale) return FP4_ERR_NULL;
-  if (!empty) {
-    if (!x || !codes || !scales) return FP4_ERR_NULL;
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FP4_ERR_ALIGN;
-    if ((ld * (int64_t)elem_size(in_dtype)) % 16) return FP4_ERR_ALIGN;
-  }
   if (needs_workspace(p)) {
     if (!workspace) return FP4_ERR_WORKSPACE;
     if (ws_bytes < sizeof(float) * (size_t)kAmaxPartials) return FP4_ERR_WORKSPACE;
@@ -197,6 +241,23 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   q.call_tag = capturing ? 0 : next_call_tag();
   q.wait_us = amax_wait_us(rows * cols * (int64_t)elem_size(in_dtype));
   return finish(fp4_launch_quantize(q, s), s);
+}
+
+fp4_status fp4_quantize_noalloc(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                                int64_t ld, const fp4_params* p, uint8_t* codes,
+                                uint8_t* scales, float* tensor_scale, void* stream) {
+  fp4_status st = check_quantize_args(x, in_dtype, rows, cols, ld, p, codes, scales,
+                                      tensor_scale);
+  if (st != FP4_OK) return st;
+  const size_t need = fp4_workspace_bytes(rows, cols, p);
+  if (need > FP4_NOALLOC_SCRATCH_BYTES) return FP4_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) {
+    ws = scratch_address();
+    if (!ws) return FP4_ERR_DEVICE;
+  }
+  return fp4_quantize(x, in_dtype, rows, cols, ld, p, codes, scales, tensor_scale, ws,
+                      ws ? (size_t)FP4_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p) {

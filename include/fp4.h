@@ -181,6 +181,27 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
                         float* tensor_scale, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* Allocation-free fp4_quantize, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, checks and results as fp4_quantize
+ * without the workspace: the computed tensor scale's records (single-pass
+ * exchange, or two-pass partial maxima) go to a fixed array of
+ * FP4_NOALLOC_SCRATCH_BYTES bytes in the library's device memory, one per
+ * device, held until the process ends; its address is looked up on the
+ * first call on each device.  The call allocates nothing (no hipMalloc or
+ * allocating library routine).  The array needs no clearing between calls:
+ * single-pass records carry a per-call tag and the two-pass partial maxima
+ * are all rewritten by each call.  Every call on one device shares the
+ * array, so calls that overlap in time on one device (different streams,
+ * or different host threads) race and may produce wrong tensor scales:
+ * serialize them.  Returns FP4_ERR_WORKSPACE if a call would need more than
+ * the array (none does: the exchange takes fp4_workspace_bytes(), at most
+ * 16400 bytes) and FP4_ERR_DEVICE if the array's address cannot be found. */
+#define FP4_NOALLOC_SCRATCH_BYTES 16640
+fp4_status fp4_quantize_noalloc(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
+                                int64_t ld, const fp4_params* p, uint8_t* codes,
+                                uint8_t* scales, float* tensor_scale, void* stream);
+
 /* Bytes of device workspace fp4_quantize_dual needs (0 when none). */
 size_t fp4_workspace_bytes_dual(int64_t rows, int64_t cols, const fp4_params* p);
 

@@ -166,3 +166,27 @@ def test_dual_validation(lib):
     assert dq(P("nvfp4"), sc=0) == -1
     assert dq(P("nvfp4"), nws=4096) == -6           # needs two partial arrays
     assert dq(P("nvfp4"), ws=0) == -6
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free entry point checks its arguments on the host, as
+    fp4_quantize does, before any HIP call (there is no GPU here)."""
+    P = fp4.make_params
+
+    def nq(p, x=A, dt=0, rows=64, cols=64, ld=64, codes=A, scales=A, ts=A):
+        return lib.fp4_quantize_noalloc(x, dt, rows, cols, ld,
+                                        ctypes.byref(p) if p is not None else None,
+                                        codes, scales, ts, None)
+    assert nq(None) == -1
+    bad = P("nvfp4"); bad.block = 32
+    assert nq(bad) == -2
+    assert nq(P("nvfp4"), dt=9) == -5
+    assert nq(P("nvfp4"), cols=24, ld=24) == -3
+    assert nq(P("nvfp4"), x=0) == -1
+    assert nq(P("nvfp4"), ts=0) == -1
+    assert nq(P("nvfp4"), codes=MIS) == -4
+    assert nq(P("mxfp4_mbs")) == -2
+    # the scratch array holds every workspace the library asks for
+    for shape in ((64, 64), (16384, 14336)):
+        for fmt in ("nvfp4", "ufp4", "e2m1_cap2"):
+            assert fp4.workspace_bytes(*shape, P(fmt)) <= 16640
