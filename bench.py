@@ -4,12 +4,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the hot path over one batch of synthetic input: every
-quantize call of the workload (default: the 4096x4096 BF16 Student-t
-activation with outlier channels, 16-point RHT + NVFP4, row axis, once with
-RTNE and once with stochastic rounding).  Inputs are resident in device
-memory before timing starts.  W untimed warmup steps, then exactly K steps
-between device synchronizations, timed with HIP events on the stream the
-kernels run on.  Prints one JSON line.
+quantize call of the workload (default: the training operands of one linear
+layer at hidden 4096, FFN 14336 and 16384 tokens -- X and W along rows, dY
+along columns with stochastic rounding and X along columns, 16-point RHT +
+NVFP4 with a computed tensor scale; `--workload activation` is the 4096 x
+4096 activation, RTNE and SR).  Inputs are resident in device memory before
+timing starts.  W untimed warmup steps, then exactly K steps between device
+synchronizations, timed with HIP events on the stream the kernels run on.
+Prints one JSON line.
 
 `value` is input GB/s over the whole step (bytes of BF16 input of every call
 / step time), warm: the same tensors are quantized every step, so inputs of
@@ -19,7 +21,15 @@ times each call after reading a 512 MiB buffer, which evicts L2 and MALL
 dominant call: its algorithmic bytes (input + codes + scale bytes + 4-byte
 tensor scale) over its mean duration, against the 8 TB/s HBM peak.
 `cpu_baseline` times the scalar oracle on the host on a bounded sample of
-the same workload.
+the same workload.  Beside the per-call fractions of the 8 TB/s peak
+(single-read algorithmic bytes, bytes as moved with the tensor-amax pass's
+second read, counter-measured bytes) the line carries the rate of a plain
+device copy (`copy_ceiling_gbs`, the practical ceiling) and, for the
+workloads with a fused RHT, the plain / fused / unfused quantize times of
+the first operand (the ratio the shrinkage-bias page reports in
+"Eficiencia").  The 256x256 FP32 and 8192x28672 workloads add their error
+reports (per-block error, signed errors, SQNR, flush-to-zero rate) from the
+GPU outputs, checked against the same report on the oracle's outputs.
 """
 from __future__ import annotations
 
@@ -180,10 +190,198 @@ def cpu_baseline(w, tensors, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d full step(s) of the workload (%d calls each) in %.1f s" % (
                 reps, len(w.calls), dt)}
 
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_ceiling_gbs(dev, mib=512, reps=10) -> float:
+    """Bytes moved (read + write) per second by a plain device-to-device copy
+    of `mib` MiB: the practical HBM ceiling the fractions are set beside."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
+def fused_ratio(x, stream, reps=30):
+    """NVFP4 quantize of x (row axis, RTNE, computed tensor scale) timed
+    three ways: plain (no RHT), fused (the RHT inside the quantize call) and
+    unfused (the standalone RHT to FP32, then the plain quantize of its
+    output, which gives the same bytes as the fused call).  The
+    shrinkage-bias page ("Eficiencia") reports fused ~1.06-1.07x and unfused
+    ~1.4-1.6x the plain quantize on NVIDIA SM90/SM100."""
+    import torch
+    import block_scaled_bit_fp4_amd as fp4
+    rows, cols = x.shape
+    cs, ss = fp4.output_shapes(rows, cols, "nvfp4", "row")
+    outs = [(torch.empty(cs, dtype=torch.uint8, device=x.device),
+             torch.empty(ss, dtype=torch.uint8, device=x.device),
+             torch.empty(1, dtype=torch.float32, device=x.device)) for _ in range(2)]
+    ws = fp4.new_workspace(rows, cols, fp4.make_params("nvfp4"), x.device)
+    y = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+
+    def q(inp, rht, o):
+        fp4.quantize(inp, "nvfp4", "row", "rtne", rht, 0, 0, codes=o[0], scales=o[1],
+                     ts_out=o[2], workspace=ws, stream=stream)
+
+    arms = {"plain": lambda: q(x, False, outs[0]),
+            "fused": lambda: q(x, True, outs[0]),
+            "unfused": lambda: (fp4.rht(x, "row", 0, out=y, stream=stream), q(y, False, outs[1]))}
+    us = {}
+    for name, fn in arms.items():
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us[name] = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    # the unfused arm's codes equal the fused call's
+    arms["fused"]()
+    torch.cuda.synchronize()
+    same = all(bool(torch.equal(a, b)) for a, b in zip(outs[0], outs[1]))
+    return {"operand": list(x.shape), "format": "nvfp4 row rtne, computed tensor scale",
+            "plain_us": round(us["plain"], 2), "fused_us": round(us["fused"], 2),
+            "unfused_us": round(us["unfused"], 2),
+            "fused_over_plain": round(us["fused"] / us["plain"], 3),
+            "unfused_over_plain": round(us["unfused"] / us["plain"], 3),
+            "unfused_bytes_equal_fused": same}
+
+
+def error_report(x, y, xhat, xhat_rot, d_b, block):
+    """Quantization-error figures of one call (torch float64, any device).
+    x: the input (original domain); y: what was quantized (x, or its RHT);
+    xhat / xhat_rot: the dequantized values in the original / quantized
+    domain; d_b: each element's block scale (0 where the block codes zeros),
+    all of the logical operand's shape.  Readings of the pages' quantities:
+      - signed errors: mean(sign(x) (xhat - x)) and mean(xhat - x) in the
+        original domain; the normalized magnitude bias mean(|q| - |v|), v =
+        y / d_b and q its level, over elements of blocks with d_b > 0 (the
+        shrinkage-bias page, Metodologia 1);
+      - gain <xhat, x> / <x, x>; SQNR 10 log10(sum x^2 / sum (xhat - x)^2);
+      - flush to zero: share of nonzero y coded as zero;
+      - per block (quantized domain): MSE, max |error| and signed magnitude
+        mean, each at p50 / p90 / p99 / max, with the worst block."""
+    import torch
+    x, y, xhat, xhat_rot, d_b = (t.double() for t in (x, y, xhat, xhat_rot, d_b))
+    err = xhat - x
+    ok = d_b > 0
+    v = torch.where(ok, y.abs() / torch.where(ok, d_b, 1.0), 0.0)
+    q = torch.where(ok, xhat_rot.abs() / torch.where(ok, d_b, 1.0), 0.0)
+    e_rot = xhat_rot - y
+    R, W = y.shape
+    blk = lambda t: t.reshape(R, W // block, block)
+    mse = (blk(e_rot) ** 2).mean(-1).flatten()
+    mx = blk(e_rot).abs().amax(-1).flatten()
+    smag = (blk(torch.sign(y) * e_rot)).mean(-1).flatten()
+
+    def pct(t):
+        qs = torch.quantile(t.float().cpu(), torch.tensor([0.5, 0.9, 0.99]))
+        return {"p50": float(qs[0]), "p90": float(qs[1]), "p99": float(qs[2]),
+                "max": float(t.max())}
+    nz = y != 0
+    return {
+        "mean_signed_error_magnitude": float((torch.sign(x) * err).mean()),
+        "mean_error": float(err.mean()),
+        "normalized_magnitude_bias": float((q[ok] - v[ok]).mean()) if bool(ok.any()) else None,
+        "gain": float((xhat * x).sum() / (x * x).sum()),
+        "sqnr_db": float(10.0 * torch.log10((x * x).sum() / (err * err).sum())),
+        "flush_to_zero_rate": float(((xhat_rot == 0) & nz).sum() / max(int(nz.sum()), 1)),
+        "per_block_mse": pct(mse), "per_block_max_abs_error": pct(mx),
+        "per_block_signed_magnitude_mean": pct(smag),
+        "worst_block_mse": {"block": int(mse.argmax()), "row": int(mse.argmax()) // (W // block),
+                            "mse": float(mse.max())},
+    }
+
+
+def block_scales(scales, ts, fmt, block, shape):
+    """Each element's decoded block scale (torch float64): E4M3 byte times the
+    tensor scale (two-level formats), 2^(S - 127) (MX formats)."""
+    import torch
+    MX_ = ("mxfp4", "mxfp4_oas")
+    s = scales.to(torch.int64)
+    if fmt in MX_:
+        d = torch.ldexp(torch.ones_like(s, dtype=torch.float64), s - 127)
+    else:
+        e4 = scales.view(torch.float8_e4m3fn).double()
+        d = torch.where(s == 0, 0.0, e4 * float(ts))
+    return d.repeat_interleave(block, dim=1).reshape(shape)
+
+
+def call_report(x_bits, x_dev, call, codes, scales, ts, oracle_out=None):
+    """error_report of one call from the GPU's codes (dequantized by the
+    library on the GPU) and, when oracle_out is given, the same report from
+    the oracle's codes on the host; the two must agree (the bytes are
+    identical; only the order of the float64 sums differs)."""
+    import numpy as np
+    import torch
+    import block_scaled_bit_fp4_amd as fp4
+    rows, cols = x_dev.shape
+    B = fp4.BLOCK[call.fmt]
+    xf = x_dev.float()
+    y = fp4.rht(x_dev, "row", call.rht_seed) if call.rht else xf
+    xr = fp4.dequantize(codes, scales, ts, rows, cols, call.fmt, "row", call.rht, call.rht_seed,
+                        False, torch.float32)
+    xh = fp4.dequantize(codes, scales, ts, rows, cols, call.fmt, "row", call.rht, call.rht_seed,
+                        True, torch.float32) if call.rht else xr
+    tsv = float(ts.item()) if ts is not None else None
+    rep = error_report(xf, y, xh, xr, block_scales(scales, tsv, call.fmt, B, (rows, cols)), B)
+    if oracle_out is not None:
+        import oracle
+        oc, osc, ots = oracle_out
+        xo = torch.from_numpy(x_bits.astype(np.float32) if x_bits.dtype == np.float32
+                              else oracle.bf16_bits_to_f32(x_bits))
+        yo = torch.from_numpy(oracle.rht(x_bits, "row", call.rht_seed)) if call.rht else xo
+        xro = torch.from_numpy(oracle.dequantize(oc, osc, ots, rows, cols, call.fmt, "row",
+                                                 call.rht, call.rht_seed, False))
+        xho = torch.from_numpy(oracle.dequantize(oc, osc, ots, rows, cols, call.fmt, "row",
+                                                 call.rht, call.rht_seed, True)) \
+            if call.rht else xro
+        ro = error_report(xo, yo, xho, xro, block_scales(torch.from_numpy(osc), ots, call.fmt, B,
+                                                         (rows, cols)), B)
+        rep["oracle_check"] = "agrees" if _reports_close(rep, ro) else {"oracle": ro}
+    return rep
+
+
+def _reports_close(a, b, rtol=1e-6):
+    if isinstance(a, dict):
+        return all(_reports_close(a[k], b[k], rtol) for k in a)
+    if isinstance(a, float) and isinstance(b, float):
+        return abs(a - b) <= rtol * max(abs(a), abs(b), 1e-30)
+    return a == b
+
+
+# workloads whose error figures the line reports: the 256x256 FP32 tensor
+# (per-block error, signed errors) and the 8192x28672 up-projection weight
+# (signed bias per format)
+REPORTED = ("nvfp4_fp32_256x256", "ufp4_vs_nvfp4_upproj_8192x28672")
 
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
 # formats whose GEMM-level quality the GEMM workload reports through
@@ -390,7 +588,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="activation")
+    ap.add_argument("--workload", default="linear_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache per-call timing (512 MiB eviction before each call)")
@@ -585,6 +783,40 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # beside the timing: the copy ceiling, the fused-RHT ratio of the first
+    # operand, and the error reports of the workloads that ask for them
+    ceiling = copy_ceiling_gbs(dev)
+    c0 = plans[0]["call"]
+    fused = None
+    if (c0.op == "quantize" and c0.fmt == "nvfp4" and c0.rht and c0.axis == "row"
+            and plans[0]["x"].dtype == torch.bfloat16):
+        fused = fused_ratio(plans[0]["x"], stream)
+    reports = None
+    if w.name in REPORTED:
+        import oracle
+        reports = {}
+        for pl in plans:
+            c = pl["call"]
+            codes, scales, ts = pl["outs"][0]
+            run(pl)
+            torch.cuda.synchronize()
+            host = tensors[c.tensor]
+            ref = oracle.quantize(host, c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed)
+            same = (np.array_equal(codes.cpu().numpy(), ref[0]) and
+                    np.array_equal(scales.cpu().numpy(), ref[1]))
+            rep = call_report(host, pl["x"], c, codes, scales, None if c.fmt in MX else ts,
+                              ref)
+            rep["gpu_bytes_equal_oracle"] = bool(same)
+            reports[call_label(c)] = rep
+            if c.rht:  # the same format without the RHT, for the RHT's change in SQNR
+                import dataclasses
+                c2 = dataclasses.replace(c, rht=False)
+                q2 = fp4.quantize(pl["x"], c.fmt, "row", c.rounding, False, 0, c.sr_seed)
+                reports[call_label(c2)] = call_report(host, pl["x"], c2, q2[0], q2[1],
+                                                      None if c.fmt in MX else q2[2])
+                del q2
+            torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, tensors)
@@ -601,6 +833,10 @@ def main():
                    "per_call_us": [round(m * 1e3, 2) for m in per_call],
                    "frac_alg": frac_alg, "frac_moved": frac_moved,
                    "frac_rocprof": frac_rocprof if any(frac_rocprof) else None,
+                   "copy_ceiling_gbs": ceiling,
+                   "frac_alg_of_copy_ceiling": [round(f * HBM_PEAK_GBS / ceiling, 4)
+                                                for f in frac_alg],
+                   "fused_ratio": fused, "reports": reports,
                    "wall_ms_per_step": round(wall_ms, 4),
                    "cold_per_call_us": [round(m * 1e3, 2) for m in cold_per_call] or None,
                    "cold_input_gbs": round(in_bytes / (sum(cold_per_call) * 1e-3) / 1e9, 2)
