@@ -48,8 +48,8 @@ METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
 KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/" + f for f in (
     "fp4_quantize.h", "fp4_quantize_nvfp4.hip", "fp4_quantize_mxfp4.hip", "fp4_quantize_ufp4.hip",
     "fp4_quantize_mxfp4_oas.hip", "fp4_quantize_e2m1_cap2.hip", "fp4_quantize_mxfp4_mbs.hip",
-    "fp4_dequant.hip", "fp4_tiles.h", "fp4_device.h")]
-MX = ("mxfp4", "mxfp4_oas")
+    "fp4_quantize_mxfp4_oas16.hip", "fp4_dequant.hip", "fp4_tiles.h", "fp4_device.h")]
+MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
 
 
 GEMM_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_gemm.hip"]
@@ -325,7 +325,7 @@ def block_scales(scales, ts, fmt, block, shape):
     """Each element's decoded block scale (torch float64): E4M3 byte times the
     tensor scale (two-level formats), 2^(S - 127) (MX formats)."""
     import torch
-    MX_ = ("mxfp4", "mxfp4_oas")
+    MX_ = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
     s = scales.to(torch.int64)
     if fmt in MX_:
         d = torch.ldexp(torch.ones_like(s, dtype=torch.float64), s - 127)

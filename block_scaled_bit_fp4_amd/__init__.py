@@ -14,7 +14,8 @@ scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
 (E2M1 cut at magnitude 2, NVFP4's scaling with the block amax mapped to 2),
 ``"mxfp4_mbs"`` (static macro-block scaling: a macro scale with an 8-bit
 mantissa per 128 elements over 16-element E8M0 blocks; always returns the
-macro-scale array as its third result, as ``outer=True`` does).
+macro-scale array as its third result, as ``outer=True`` does),
+``"mxfp4_oas16"`` (overflow-aware E8M0 scales on 16-element blocks).
 The two-level formats (NVFP4, the uniform grid, the cut E2M1) also take
 double-block scales (``outer=True``): one FP32 outer scale per 128 elements
 of each row of the quantized operand instead of the tensor scale.
@@ -38,11 +39,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4.so")
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5,
+           "mxfp4_oas16": 6}
 BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
-         "mxfp4_mbs": 16}
+         "mxfp4_mbs": 16, "mxfp4_oas16": 16}
 ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that exist only with 128-element macro scales
-MX = ("mxfp4", "mxfp4_oas")
+MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
 OUTER = 128  # elements per outer scale (double-block mode)
 TS_COMPUTE, TS_GIVEN, TS_OUTER128 = 0, 1, 2
 AXES = {"row": 0, "col": 1}

@@ -52,7 +52,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_size(int32_t dt) { return dt == FP4_BF16 ? 2 : 4; }
 
-bool is_mx(int32_t format) { return format == FP4_MXFP4 || format == FP4_MXFP4_OAS; }
+bool is_mx(int32_t format) {
+  return format == FP4_MXFP4 || format == FP4_MXFP4_OAS || format == FP4_MXFP4_OAS16;
+}
+
+// Block size of each format: 16, but 32 for MXFP4 and MXFP4_OAS.
+int32_t block_of(int32_t format) {
+  return (format == FP4_MXFP4 || format == FP4_MXFP4_OAS) ? 32 : 16;
+}
 
 bool two_level(const fp4_params* p) { return !is_mx(p->format); }
 
@@ -63,10 +70,11 @@ bool outer_scales(const fp4_params* p) {
 fp4_status check_params(const fp4_params* p) {
   if (!p) return FP4_ERR_NULL;
   if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4 &&
-      p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2 && p->format != FP4_MXFP4_MBS)
+      p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2 && p->format != FP4_MXFP4_MBS &&
+      p->format != FP4_MXFP4_OAS16)
     return FP4_ERR_FORMAT;
   if (p->format == FP4_MXFP4_MBS && p->ts_mode != FP4_TS_OUTER128) return FP4_ERR_FORMAT;
-  if (p->block != (is_mx(p->format) ? 32 : 16)) return FP4_ERR_FORMAT;
+  if (p->block != block_of(p->format)) return FP4_ERR_FORMAT;
   if (p->axis != FP4_AXIS_ROW && p->axis != FP4_AXIS_COL) return FP4_ERR_FORMAT;
   if (p->rounding != FP4_RTNE && p->rounding != FP4_SR) return FP4_ERR_FORMAT;
   if (p->rht != 0 && p->rht != 1) return FP4_ERR_FORMAT;
@@ -430,6 +438,7 @@ hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
     case FP4_UFP4: return fp4_launch_quantize_ufp4(q, s);
     case FP4_E2M1_CAP2: return fp4_launch_quantize_e2m1_cap2(q, s);
     case FP4_MXFP4_MBS: return fp4_launch_quantize_mxfp4_mbs(q, s);
+    case FP4_MXFP4_OAS16: return fp4_launch_quantize_mxfp4_oas16(q, s);
     default: return fp4_launch_quantize_mxfp4_oas(q, s);
   }
 }

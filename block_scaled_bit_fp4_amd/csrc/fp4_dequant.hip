@@ -528,6 +528,7 @@ hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
     case kUFP4: return dq_outer<kUFP4>(q, s);
     case kCAP2: return dq_outer<kNVFP4>(q, s);  // E2M1 codes, E4M3 scales: decoded as NVFP4
     case kMBS: return dq_outer<kMBS>(q, s);
+    case kMXOAS16: return dq_outer<kMXOAS16>(q, s);
     default: return dq_outer<kMXOAS>(q, s);
   }
 }

@@ -25,16 +25,20 @@ namespace fp4dev {
 // kMBS: MXFP4 with static macro-block scaling ([MXFP4] 2.B): a scale with
 // an 8-bit mantissa per 128-element macro block (carried like the outer
 // scales), 16-element blocks with E8M0 scales relative to it, E2M1 codes.
-enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4, kMBS = 5 };
+// kMXOAS16: overflow-aware MX scaling on 16-element blocks, the granularity
+// at which [MXFP4] 2 applies its techniques (E8M0 per 16 elements).
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4, kMBS = 5, kMXOAS16 = 6 };
 // Tensor-scale modes of the two-level formats: computed from the data,
 // given by the caller, or one outer scale per kOuter elements of an A-row.
 enum : int { kTsCompute = 0, kTsGiven = 1, kTsOuter = 2 };
 constexpr int kOuter = 128;
 
 // E8M0-scaled formats (power-of-two block scales, no tensor scale).
-constexpr bool is_mx(int fmt) { return fmt == kMXFP4 || fmt == kMXOAS; }
+constexpr bool is_mx(int fmt) { return fmt == kMXFP4 || fmt == kMXOAS || fmt == kMXOAS16; }
+// Overflow-aware MX exponents ([MXFP4] 2.A).
+constexpr bool is_oas(int fmt) { return fmt == kMXOAS || fmt == kMXOAS16; }
 template <int FMT>
-constexpr int block_of() { return is_mx(FMT) ? 32 : 16; }
+constexpr int block_of() { return (is_mx(FMT) && FMT != kMXOAS16) ? 32 : 16; }
 
 // ---------------------------------------------------------------- widening
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -315,7 +315,7 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
   const float amax_b = RHT ? amax_t * 0.25f : amax_t;
   float inv;
   if constexpr (is_mx(FMT)) {
-    const int e = FMT == kMXOAS ? e8m0_exponent_oas(amax_b) : e8m0_exponent(amax_b);
+    const int e = is_oas(FMT) ? e8m0_exponent_oas(amax_b) : e8m0_exponent(amax_b);
     sbyte = (uint32_t)(e + 127);
     inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
   } else if constexpr (FMT == kMBS) {

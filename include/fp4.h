@@ -123,6 +123,12 @@ typedef int32_t fp4_status;
  * 2^e_b (binary32); E2M1 elements, saturating at 6.  Requires ts_mode =
  * FP4_TS_OUTER128 and block 16. */
 #define FP4_MXFP4_MBS 5
+/* MXFP4 with overflow-aware scales on 16-element blocks: the granularity at
+ * which the MXFP4 page applies its techniques ("Unveiling the Potential of
+ * Quantization with MXFP4", 2. Methodologie et Analyse; OAS in 2.A): an
+ * E8M0 byte per 16 elements with 3.5 < amax_b / 2^e <= 7, E2M1 elements
+ * saturating at 6, no tensor scale.  Block 16. */
+#define FP4_MXFP4_OAS16 6
 
 #define FP4_AXIS_ROW 0 /* quantize along rows of x */
 #define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
@@ -139,11 +145,13 @@ typedef int32_t fp4_status;
 
 typedef struct {
   int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
-  int32_t block;    /* 16 for NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS; 32 for MXFP4, MXFP4_OAS */
+  int32_t block;    /* 16 for NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16; 32 for MXFP4,
+                       MXFP4_OAS */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for MXFP4 and MXFP4_OAS;
+  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for MXFP4, MXFP4_OAS and
+                       MXFP4_OAS16;
                        MXFP4_MBS requires _OUTER128) */
   uint64_t rht_seed;
   uint64_t sr_seed;

@@ -38,16 +38,17 @@ _SO = os.path.join(_HERE, "libfp4_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5}
+FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5,
+           "mxfp4_oas16": 6}
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 GRIDS = {"e2m1": 0, "uniform": 1, "e2m1_cap2": 2}
 BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
-         "mxfp4_mbs": 16}
+         "mxfp4_mbs": 16, "mxfp4_oas16": 16}
 ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that only exist with 128-element outer scales
 TS_MODES = {"compute": 0, "given": 1, "outer128": 2}
 OUTER = 128  # outer block of the double-block mode
-MX = ("mxfp4", "mxfp4_oas")
+MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
 E2M1_LEVELS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 UNIFORM_LEVELS = (0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0)
 

@@ -300,15 +300,21 @@ static float grid_max(int format) {
 }
 
 static int is_mx(int format) {
-  return format == FP4R_MXFP4 || format == FP4R_MXFP4_OAS;
+  return format == FP4R_MXFP4 || format == FP4R_MXFP4_OAS || format == FP4R_MXFP4_OAS16;
+}
+
+/* Elements per block scale: 32 for MXFP4 and MXFP4-OAS ([MXFP4] 2), 16 for
+ * the rest (NVFP4's groups; [MXFP4] 2: its techniques at a granularity of 16). */
+static int block_of(int format) {
+  return (format == FP4R_MXFP4 || format == FP4R_MXFP4_OAS) ? 32 : 16;
 }
 
 static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
                         int64_t ld) {
   if (!p) return -1;
-  if (p->format < 0 || p->format > 5) return -1;
+  if (p->format < 0 || p->format > 6) return -1;
   if (p->format == FP4R_MXFP4_MBS && p->ts_mode != FP4R_TS_OUTER128) return -1;
-  if (is_mx(p->format) ? p->block != 32 : p->block != 16) return -1;
+  if (p->block != block_of(p->format)) return -1;
   if (!is_mx(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
   if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;
   if (p->rounding != FP4R_RTNE && p->rounding != FP4R_SR) return -1;
@@ -352,7 +358,7 @@ static float block_decode_scale(const fp4r_params* p, uint8_t sbyte, float s_t) 
 
 static uint8_t block_scale_byte(const fp4r_params* p, float amax_b, float s_t) {
   if (p->format == FP4R_MXFP4) return (uint8_t)(fp4r_e8m0_exponent(amax_b) + 127);
-  if (p->format == FP4R_MXFP4_OAS)
+  if (p->format == FP4R_MXFP4_OAS || p->format == FP4R_MXFP4_OAS16)
     return (uint8_t)(fp4r_e8m0_exponent_oas(amax_b) + 127);
   /* MBS: the MX exponent rule applied to amax_b / M, so the block's largest
    * element lands in [4, 8) times d_b = M * 2^e_b (e_b = 0 for the block

@@ -51,8 +51,10 @@ extern "C" {
  * 2.B): one scale with an 8-bit mantissa per 128-element macro block,
  * computed from the macro block's maximum, over 16-element blocks with
  * E8M0 scales relative to it.  Always with 128-element outer scales. */
+/* FP4R_MXFP4_OAS16: overflow-aware MX scaling ([MXFP4] 2.A) on 16-element
+ * blocks, the granularity at which [MXFP4] 2 applies its techniques. */
 enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3, FP4R_E2M1_CAP2 = 4,
-       FP4R_MXFP4_MBS = 5 };
+       FP4R_MXFP4_MBS = 5, FP4R_MXFP4_OAS16 = 6 };
 enum { FP4R_ROW = 0, FP4R_COL = 1 };
 enum { FP4R_RTNE = 0, FP4R_SR = 1 };
 enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
@@ -62,8 +64,10 @@ enum { FP4R_OUTER = 128 };
 enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1, FP4R_GRID_E2M1_CAP2 = 2 };
 
 typedef struct {
-  int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
-  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS) or 32 (MXFP4, MXFP4_OAS) */
+  int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS /
+                       _MXFP4_OAS16 */
+  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16) or 32 (MXFP4,
+                       MXFP4_OAS) */
   int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
   int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */

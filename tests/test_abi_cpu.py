@@ -53,6 +53,7 @@ def test_workspace_bytes(lib):
     assert fp4.workspace_bytes(64, 64, fp4.make_params("nvfp4", ts_given=True)) == 0
     assert fp4.workspace_bytes(64, 128, fp4.make_params("nvfp4", outer=True)) == 0
     assert fp4.workspace_bytes(64, 64, fp4.make_params("mxfp4_oas")) == 0
+    assert fp4.workspace_bytes(64, 64, fp4.make_params("mxfp4_oas16")) == 0
 
 
 # Fake device pointers: validation must reject these calls before touching them.
@@ -83,11 +84,14 @@ def test_quantize_validation(lib):
     assert _q(lib, bad) == -2
     bad = P("mxfp4_oas"); bad.block = 16
     assert _q(lib, bad) == -2
+    bad = P("mxfp4_oas16"); bad.block = 32                        # OAS16 is E8M0 per 16
+    assert _q(lib, bad) == -2
+    assert _q(lib, P("mxfp4_oas16"), cols=40, ld=40) == -3       # W % 16
     bad = P("e2m1_cap2"); bad.block = 32
     assert _q(lib, bad) == -2
     assert _q(lib, P("mxfp4_mbs")) == -2                         # MBS needs its macro scales
     assert _q(lib, P("mxfp4_mbs", ts_given=True)) == -2
-    bad = P("nvfp4"); bad.format = 6
+    bad = P("nvfp4"); bad.format = 42
     assert _q(lib, bad) == -2
     assert _q(lib, P("nvfp4", outer=True), cols=144, ld=144) == -3   # W % 128
     assert _q(lib, P("ufp4", outer=True, axis="col"), rows=96) == -3

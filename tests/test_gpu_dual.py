@@ -53,7 +53,7 @@ def test_dual_fused_parity(fmt, rounding, rht, mode):
         _check(x, fmt, rounding, rht, mode, 11 + i)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "mxfp4_oas", "mxfp4_mbs"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "ufp4", "mxfp4", "mxfp4_oas", "mxfp4_mbs", "mxfp4_oas16"])
 def test_dual_split_parity(fmt):
     mbs = fmt == "mxfp4_mbs"  # macro scales only: both dims multiples of 128
     for (shape, dt), rounding, rht in itertools.product(SPLIT, ["rtne", "sr"], [False, True]):

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(32, 32), (96, 160), (224, 64), (1056, 352), (48, 80)]
 KINDS = workloads.SMALL_KINDS
 
-COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas", "e2m1_cap2"], ["row", "col"],
+COMBOS = list(itertools.product(["nvfp4", "mxfp4", "ufp4", "mxfp4_oas", "e2m1_cap2",
+                                 "mxfp4_oas16"], ["row", "col"],
                                 ["rtne", "sr"], [False, True], ["bf16", "f32"]))
 
 # Double-block (outer scale per 128) shapes: W % 128 == 0 on the axis used.
@@ -125,7 +126,7 @@ def test_poison_and_determinism():
 def test_col_equals_row_of_transpose_on_gpu():
     x = _input("t3", (256, 160), 4, "bf16")
     xt = np.ascontiguousarray(x.T)
-    for fmt in ("nvfp4", "mxfp4", "ufp4", "e2m1_cap2"):
+    for fmt in ("nvfp4", "mxfp4", "ufp4", "e2m1_cap2", "mxfp4_oas16"):
         note("transpose %s" % fmt)
         c1, s1, t1 = fp4.quantize(to_device(x), fmt, "col", "sr", True, 6, 8)
         c2, s2, t2 = fp4.quantize(to_device(xt), fmt, "row", "sr", True, 6, 8)

@@ -146,6 +146,18 @@ def _levels(fmt):
     return E2M1[:5] if fmt == "e2m1_cap2" else E2M1
 
 
+def _oas_exponent(amax: float) -> int:
+    """Overflow-aware MX exponent (MXFP4 page, 2.A), exactly: the integer e
+    with 3.5 < amax / 2^e <= 7, clamped to [-127, 127]; -127 for amax = 0."""
+    if amax == 0:
+        return -127
+    q = Fraction(amax)
+    e = -200
+    while q > 7 * Fraction(2) ** e:
+        e += 1
+    return min(max(e, -127), 127)
+
+
 def _levels_exact(levels):
     return [Fraction(float(v)) for v in levels]
 
@@ -215,6 +227,9 @@ def _brute_quantize(x: np.ndarray, fmt: str, rht: bool = False, signs=None,
             if fmt == "mxfp4":
                 e = -127 if amax == 0 else max(-127, int(np.floor(np.log2(np.float64(amax)))) - 2)
                 S, d = e + 127, np.float32(2.0 ** e)
+            elif fmt == "mxfp4_oas16":
+                e = _oas_exponent(float(amax))
+                S, d = e + 127, np.float32(2.0 ** e)
             else:
                 if s_t == 0 or amax == 0:
                     S = 0
@@ -238,7 +253,7 @@ def _brute_quantize(x: np.ndarray, fmt: str, rht: bool = False, signs=None,
     return codes, scales, s_t
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2", "mxfp4_oas16"])
 @pytest.mark.parametrize("kind", ["normal", "wide_range", "tiny", "zeros_mixed", "grid_ties"])
 def test_brute_force_tiny(fmt, kind):
     x = workloads.small_case(kind, 3, 64, 21)
@@ -246,7 +261,7 @@ def test_brute_force_tiny(fmt, kind):
     bc, bs, bts = _brute_quantize(x, fmt)
     assert np.array_equal(oracle.unpack_codes(codes), bc)
     assert np.array_equal(scales, bs)
-    if fmt != "mxfp4":
+    if fmt not in oracle.MX:
         assert ts == bts
 
 
@@ -268,7 +283,7 @@ def _rht_exact_bf16(rows, cols, seed, spikes=False):
     return workloads.to_bf16_bits(a.astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "ufp4", "e2m1_cap2", "mxfp4_oas16"])
 @pytest.mark.parametrize("rounding", ["rtne", "sr"])
 @pytest.mark.parametrize("spikes", [False, True])
 def test_brute_force_tiny_rht_and_sr(rocrand_kat, fmt, rounding, spikes):
@@ -285,7 +300,7 @@ def test_brute_force_tiny_rht_and_sr(rocrand_kat, fmt, rounding, spikes):
                                   draws)
     assert np.array_equal(scales, bs)
     assert np.array_equal(oracle.unpack_codes(codes), bc)
-    if fmt != "mxfp4":
+    if fmt not in oracle.MX:
         assert ts == bts
 
 

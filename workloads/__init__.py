@@ -190,6 +190,16 @@ def _w_mx_weight_oas() -> Workload:
     return w
 
 
+def _w_mx_weight_oas16() -> Workload:
+    w = _w_mx_weight()
+    w.name = "mxfp4_oas16_weight_8192x8192"
+    w.description = ("8192x8192 BF16 N(0, 0.02^2): MXFP4 with overflow-aware scales on 16-element "
+                     "blocks (E8M0 per 16), RTNE, row and column axis, RHT off and on")
+    for c in w.calls:
+        c.fmt = "mxfp4_oas16"
+    return w
+
+
 def _w_mx_weight_mbs() -> Workload:
     w = _w_mx_weight()
     w.name = "mxfp4_mbs_weight_8192x8192"
@@ -289,6 +299,7 @@ WORKLOADS = {
     "linear_layer_outer": _w_linear_layer_outer,
     "mx_weight_oas": _w_mx_weight_oas,
     "mx_weight_mbs": _w_mx_weight_mbs,
+    "mx_weight_oas16": _w_mx_weight_oas16,
     "linear_layer_dual": _w_linear_layer_dual,
     "training_operands": _w_training_operands,
     "dequant": _w_dequant,
