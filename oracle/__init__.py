@@ -39,16 +39,19 @@ _lock = threading.Lock()
 _lib = None
 
 FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5,
-           "mxfp4_oas16": 6}
+           "mxfp4_oas16": 6, "hif4": 7}
 AXES = {"row": 0, "col": 1}
 ROUNDINGS = {"rtne": 0, "sr": 1}
 GRIDS = {"e2m1": 0, "uniform": 1, "e2m1_cap2": 2}
 BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
-         "mxfp4_mbs": 16, "mxfp4_oas16": 16}
+         "mxfp4_mbs": 16, "mxfp4_oas16": 16, "hif4": 64}
+# scale bytes per block: one, but four for HiF4 (E6M2 byte, 8 + 16 E1M0 bits)
+SCALE_BYTES = {f: (4 if f == "hif4" else 1) for f in BLOCK}
 ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that only exist with 128-element outer scales
 TS_MODES = {"compute": 0, "given": 1, "outer128": 2}
 OUTER = 128  # outer block of the double-block mode
 MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
+NO_TENSOR_SCALE = MX + ("hif4",)  # every scale per block
 E2M1_LEVELS = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 UNIFORM_LEVELS = (0.0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0)
 
@@ -101,6 +104,9 @@ def lib():
         L.fp4r_rht16.argtypes = [f32p, ctypes.c_uint16, ctypes.c_int, f32p]
         L.fp4r_e4m3_encode.argtypes = [ctypes.c_float]
         L.fp4r_e4m3_encode.restype = ctypes.c_uint8
+        L.fp4r_e6m2_encode_n.argtypes = [f32p, i64, u8p]
+        L.fp4r_e6m2_decode.argtypes = [ctypes.c_uint8]
+        L.fp4r_e6m2_decode.restype = ctypes.c_float
         L.fp4r_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.fp4r_e4m3_decode.restype = ctypes.c_float
         L.fp4r_e8m0_exponent.argtypes = [ctypes.c_float]
@@ -194,6 +200,17 @@ def e4m3_encode(r) -> np.ndarray:
     return out
 
 
+def e6m2_encode(r) -> np.ndarray:
+    r = np.ascontiguousarray(np.asarray(r, dtype=np.float32).ravel())
+    out = np.zeros(r.size, dtype=np.uint8)
+    lib().fp4r_e6m2_encode_n(_ptr(r, ctypes.c_float), r.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def e6m2_decode(b: int) -> float:
+    return float(lib().fp4r_e6m2_decode(b))
+
+
 def e4m3_decode(b: int) -> float:
     return float(lib().fp4r_e4m3_decode(b))
 
@@ -247,7 +264,7 @@ def quantize(x: np.ndarray, fmt="nvfp4", axis="row", rounding="rtne", rht=False,
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, mode)
     ra, w = (rows, cols) if axis == "row" else (cols, rows)
     codes = np.zeros((ra, w // 2), dtype=np.uint8)
-    scales = np.zeros((ra, w // BLOCK[fmt]), dtype=np.uint8)
+    scales = np.zeros((ra, w // BLOCK[fmt] * SCALE_BYTES[fmt]), dtype=np.uint8)
     if outer:
         ts = np.zeros((ra, max(w // OUTER, 1)), dtype=np.float32)
     else:
@@ -257,7 +274,7 @@ def quantize(x: np.ndarray, fmt="nvfp4", axis="row", rounding="rtne", rht=False,
                              _ptr(ts, ctypes.c_float))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
-    if fmt in MX:
+    if fmt in NO_TENSOR_SCALE:
         return codes, scales, None
     return codes, scales, (ts[:, : w // OUTER] if outer else float(ts[0]))
 

@@ -146,6 +146,39 @@ __attribute__((constructor)) static void e4m3_table_init(void) {
   for (unsigned b = 0; b < 127u; ++b) kE4M3[b] = e4m3_value_def(b);
 }
 
+/* ------------------------------------------------------------------------
+ * HiF4's E6M2 block scale ([HIF] 2. Metodologia: the shared scale of a
+ * 64-element block; reading: unsigned, exponent bias 2^5 - 1 = 31 as in the
+ * IEEE layouts, subnormals at exponent field 0, every byte finite).  The
+ * 256 values are listed by byte, which orders them by magnitude.
+ * ---------------------------------------------------------------------- */
+static double e6m2_value_def(unsigned b) {
+  unsigned e = (b >> 2) & 63u, m = b & 3u;
+  if (e == 0) return ldexp((double)m / 4.0, 1 - 31);
+  return ldexp(1.0 + (double)m / 4.0, (int)e - 31);
+}
+
+static double kE6M2[256];
+
+__attribute__((constructor)) static void e6m2_table_init(void) {
+  for (unsigned b = 0; b < 256u; ++b) kE6M2[b] = e6m2_value_def(b);
+}
+
+float fp4r_e6m2_decode(uint8_t b) { return (float)kE6M2[b]; }
+
+uint8_t fp4r_e6m2_encode(float r) {
+  double x = (double)r;
+  if (x >= kE6M2[255]) return 0xFF; /* saturating */
+  if (!(x > 0.0)) return 0x00;
+  unsigned c = 0;
+  while (c + 1 <= 0xFFu && kE6M2[c + 1] <= x) ++c;
+  if (kE6M2[c] == x) return (uint8_t)c;
+  double dl = x - kE6M2[c], dh = kE6M2[c + 1] - x; /* exact in binary64 */
+  if (dl < dh) return (uint8_t)c;
+  if (dh < dl) return (uint8_t)(c + 1);
+  return (uint8_t)((c & 1u) ? c + 1 : c);
+}
+
 float fp4r_e4m3_decode(uint8_t b) {
   if ((b & 0x7Fu) == 0x7Fu) return NAN;
   double v = kE4M3[b & 0x7Fu];
@@ -288,7 +321,7 @@ static int64_t a_index(int axis, int64_t i, int64_t j, int64_t ld) {
 }
 
 static int grid_of(int format) {
-  if (format == FP4R_UFP4) return FP4R_GRID_UNIFORM;
+  if (format == FP4R_UFP4 || format == FP4R_HIF4) return FP4R_GRID_UNIFORM;
   return format == FP4R_E2M1_CAP2 ? FP4R_GRID_E2M1_CAP2 : FP4R_GRID_E2M1;
 }
 
@@ -306,23 +339,30 @@ static int is_mx(int format) {
 /* Elements per block scale: 32 for MXFP4 and MXFP4-OAS ([MXFP4] 2), 16 for
  * the rest (NVFP4's groups; [MXFP4] 2: its techniques at a granularity of 16). */
 static int block_of(int format) {
+  if (format == FP4R_HIF4) return 64;
   return (format == FP4R_MXFP4 || format == FP4R_MXFP4_OAS) ? 32 : 16;
 }
+
+/* Formats with a tensor (or outer) scale: the two-level E4M3 formats and
+ * MBS-Static's macro scales.  The MX formats and HiF4 carry all their
+ * scales per block. */
+static int has_tensor_scale(int format) { return !is_mx(format) && format != FP4R_HIF4; }
 
 static int check_params(const fp4r_params* p, int64_t rows, int64_t cols,
                         int64_t ld) {
   if (!p) return -1;
-  if (p->format < 0 || p->format > 6) return -1;
+  if (p->format < 0 || p->format > 7) return -1;
   if (p->format == FP4R_MXFP4_MBS && p->ts_mode != FP4R_TS_OUTER128) return -1;
   if (p->block != block_of(p->format)) return -1;
-  if (!is_mx(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
+  if (has_tensor_scale(p->format) && (p->ts_mode < 0 || p->ts_mode > 2)) return -1;
   if (p->axis != FP4R_ROW && p->axis != FP4R_COL) return -1;
   if (p->rounding != FP4R_RTNE && p->rounding != FP4R_SR) return -1;
   if (rows < 0 || cols < 0 || ld < cols) return -1;
   int64_t W = p->axis == FP4R_ROW ? cols : rows;
   if (W % p->block) return -1;
   if (p->rht && (W % 16)) return -1;
-  if (!is_mx(p->format) && p->ts_mode == FP4R_TS_OUTER128 && (W % FP4R_OUTER)) return -1;
+  if (has_tensor_scale(p->format) && p->ts_mode == FP4R_TS_OUTER128 && (W % FP4R_OUTER))
+    return -1;
   return 0;
 }
 
@@ -398,6 +438,67 @@ void fp4r_quantize_block(const float* y, const fp4r_params* p,
   }
 }
 
+/* ------------------------------------------------------------------------
+ * HiF4 ([HIF] 2. Metodologia): a 64-element block shares an E6M2 scale S;
+ * each of its eight 8-element sub-blocks refines it by an E1M0 factor f8,
+ * each of its sixteen 4-element micro-blocks by another, f4; elements are
+ * E1M2, magnitudes k/4.  The block's largest magnitude is mapped to the top
+ * element level 7/4: S = E6M2(amax / 1.75).  A refinement halves the scale
+ * when the piece's maximum still fits under the top level after halving:
+ * f8 = 1/2 iff amax_8 <= 0.875 * S, f4 = 1/2 iff amax_4 <= 0.875 * S * f8
+ * (products of powers of two and 3-bit significands: exact in binary32).
+ * The element step is d = S * f8 * f4 / 4; v = y * (1 / d) is rounded on
+ * the uniform grid 0..7 (RTNE or SR, saturating at 7), as for UFP4.
+ * ---------------------------------------------------------------------- */
+static float hif4_step(float S, uint32_t word, int e) {
+  const int sub = e / 8, micro = e / 4;
+  const float f8 = ((word >> (8 + sub)) & 1u) ? 1.0f : 0.5f;
+  const float f4 = ((word >> (16 + micro)) & 1u) ? 1.0f : 0.5f;
+  return S * f8 * f4 * 0.25f;
+}
+
+static uint32_t hif4_block(const float* y, const fp4r_params* p, int64_t row_a,
+                           int64_t col_a0, int64_t W, uint8_t* kb) {
+  float amax = 0.0f;
+  for (int e = 0; e < 64; ++e)
+    if (fabsf(y[e]) > amax) amax = fabsf(y[e]);
+  const uint8_t sb = fp4r_e6m2_encode(amax / 1.75f);
+  const float S = fp4r_e6m2_decode(sb);
+  uint32_t word = sb;
+  for (int s = 0; s < 8; ++s) {
+    float a8 = 0.0f;
+    for (int e = 8 * s; e < 8 * s + 8; ++e)
+      if (fabsf(y[e]) > a8) a8 = fabsf(y[e]);
+    const int keep8 = !(a8 <= 0.875f * S);
+    if (keep8) word |= 1u << (8 + s);
+    const float f8 = keep8 ? 1.0f : 0.5f;
+    for (int u = 2 * s; u < 2 * s + 2; ++u) {
+      float a4 = 0.0f;
+      for (int e = 4 * u; e < 4 * u + 4; ++e)
+        if (fabsf(y[e]) > a4) a4 = fabsf(y[e]);
+      if (!(a4 <= 0.875f * S * f8)) word |= 1u << (16 + u);
+    }
+  }
+  for (int e = 0; e < 64; ++e) {
+    const float d = hif4_step(S, word, e);
+    const float yi = y[e];
+    unsigned sgn = signbit(yi) ? 1u : 0u;
+    int k = 0;
+    if (d != 0.0f && yi != 0.0f) {
+      const float inv = 1.0f / d;
+      const float m = fabsf(yi * inv);
+      if (p->rounding == FP4R_SR) {
+        uint64_t n = (uint64_t)row_a * (uint64_t)W + (uint64_t)(col_a0 + e);
+        k = fp4r_round_sr(m, FP4R_GRID_UNIFORM, fp4r_sr_u16(p->sr_seed, n));
+      } else {
+        k = fp4r_round_rtne(m, FP4R_GRID_UNIFORM);
+      }
+    }
+    kb[e] = (uint8_t)((sgn << 3) | (unsigned)k);
+  }
+  return word;
+}
+
 int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
                   int64_t ld, const fp4r_params* p, uint8_t* codes,
                   uint8_t* scales, float* tensor_scale) {
@@ -407,7 +508,7 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
   const int64_t RA = axis == FP4R_ROW ? rows : cols;
   const int64_t W = axis == FP4R_ROW ? cols : rows;
   const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
-  const int two_level = !is_mx(p->format);
+  const int two_level = has_tensor_scale(p->format);
   const int outer = two_level && p->ts_mode == FP4R_TS_OUTER128;
 
   /* tensor scale: amax over the whole (rotated) operand */
@@ -444,10 +545,19 @@ int fp4r_quantize(const void* x, int in_dtype, int64_t rows, int64_t cols,
 #pragma omp parallel
   {
     float* y = (float*)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
-    uint8_t kb[32];
+    uint8_t kb[64];
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < RA; ++i) {
       load_row(x, in_dtype, axis, ld, i, W, p->rht, signs, y);
+      if (p->format == FP4R_HIF4) {
+        for (int64_t b = 0; b < nblk; ++b) {
+          const uint32_t word = hif4_block(y + b * 64, p, i, b * 64, W, kb);
+          for (int j = 0; j < 4; ++j) scales[(i * nblk + b) * 4 + j] = (uint8_t)(word >> (8 * j));
+          for (int e = 0; e < 64; e += 2)
+            codes[i * (W / 2) + (b * 64 + e) / 2] = (uint8_t)(kb[e] | (kb[e + 1] << 4));
+        }
+        continue;
+      }
       if (outer) {
         /* [TJ2] 2.A double block: the outer scale of a 128-element piece
          * takes the place of the tensor scale, from that piece's amax. */
@@ -492,9 +602,10 @@ int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
   const int64_t W = axis == FP4R_ROW ? cols : rows;
   const int64_t nblk = W / B;
   const uint16_t signs = p->rht ? fp4r_rht_signs(p->rht_seed) : 0;
-  const int outer = !is_mx(p->format) && p->ts_mode == FP4R_TS_OUTER128;
+  const int outer = has_tensor_scale(p->format) && p->ts_mode == FP4R_TS_OUTER128;
+  const int hif4 = p->format == FP4R_HIF4;
   float s_t = 0.0f;
-  if (!is_mx(p->format)) {
+  if (has_tensor_scale(p->format)) {
     if (!tensor_scale) return -1;
     if (!outer) s_t = *tensor_scale;
   }
@@ -504,14 +615,24 @@ int fp4r_dequantize(const uint8_t* codes, const uint8_t* scales,
 #pragma omp for schedule(static)
     for (int64_t i = 0; i < RA; ++i) {
       for (int64_t b = 0; b < nblk; ++b) {
-        const float s_b =
-            outer ? tensor_scale[i * (W / FP4R_OUTER) + (b * B) / FP4R_OUTER] : s_t;
-        float d = block_decode_scale(p, scales[i * nblk + b], s_b);
+        uint32_t word = 0;
+        float S = 0.0f, d = 0.0f;
+        if (hif4) {
+          const uint8_t* sw = scales + (i * nblk + b) * 4;
+          word = sw[0] | (sw[1] << 8) | ((uint32_t)sw[2] << 16) | ((uint32_t)sw[3] << 24);
+          S = fp4r_e6m2_decode(sw[0]);
+        } else {
+          const float s_b =
+              outer ? tensor_scale[i * (W / FP4R_OUTER) + (b * B) / FP4R_OUTER] : s_t;
+          d = block_decode_scale(p, scales[i * nblk + b], s_b);
+        }
         for (int e = 0; e < B; ++e) {
           int64_t c = b * B + e;
           uint8_t byte = codes[i * (W / 2) + c / 2];
           unsigned code = (c & 1) ? (byte >> 4) : (byte & 15u);
-          float mag = fp4r_level(grid, (int)(code & 7u)) * d;
+          /* HiF4: k * d with d the element's step, S * f8 * f4 / 4 */
+          float mag = hif4 ? (float)(code & 7u) * hif4_step(S, word, e)
+                           : fp4r_level(grid, (int)(code & 7u)) * d;
           v[c] = (code & 8u) ? -mag : mag;
         }
       }
@@ -561,6 +682,11 @@ void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
   for (int64_t i = 0; i < n; ++i)
     k_out[i] = (uint8_t)(rounding == FP4R_SR ? fp4r_round_sr(m[i], grid, u16[i])
                                              : fp4r_round_rtne(m[i], grid));
+}
+
+void fp4r_e6m2_encode_n(const float* r, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = fp4r_e6m2_encode(r[i]);
 }
 
 void fp4r_f32_to_bf16_n(const float* in, int64_t n, uint16_t* out) {

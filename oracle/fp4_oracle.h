@@ -53,8 +53,19 @@ extern "C" {
  * E8M0 scales relative to it.  Always with 128-element outer scales. */
 /* FP4R_MXFP4_OAS16: overflow-aware MX scaling ([MXFP4] 2.A) on 16-element
  * blocks, the granularity at which [MXFP4] 2 applies its techniques. */
+/* FP4R_HIF4: the three-level HiF4 format ([HIF] 2. Metodologia): per
+ * 64-element block an E6M2 scale, per 8-element sub-block and per 4-element
+ * micro-block a one-bit E1M0 refinement, E1M2 elements.  Reading: element
+ * magnitudes k/4 (k = 0..7); E6M2 unsigned with bias 31 and subnormals,
+ * S = RNE(amax_64 / 1.75) saturating at 1.75 * 2^32; E1M0 with bias 1 is a
+ * factor 1/2 (bit 0) or 1 (bit 1): a sub-block takes 1/2 iff its maximum is
+ * at most 0.875 * S, a micro-block iff its maximum is at most
+ * 0.875 * S * (its sub-block's factor); step d = S * f8 * f4 / 4, v = y *
+ * (1 / d) rounded on the uniform grid 0..7.  Scales: 4 bytes per block
+ * (byte 0 = S, byte 1 = the 8 sub-block bits, bytes 2-3 = the 16
+ * micro-block bits, bit i for the i-th piece, little-endian). */
 enum { FP4R_NVFP4 = 0, FP4R_MXFP4 = 1, FP4R_UFP4 = 2, FP4R_MXFP4_OAS = 3, FP4R_E2M1_CAP2 = 4,
-       FP4R_MXFP4_MBS = 5, FP4R_MXFP4_OAS16 = 6 };
+       FP4R_MXFP4_MBS = 5, FP4R_MXFP4_OAS16 = 6, FP4R_HIF4 = 7 };
 enum { FP4R_ROW = 0, FP4R_COL = 1 };
 enum { FP4R_RTNE = 0, FP4R_SR = 1 };
 enum { FP4R_BF16 = 0, FP4R_F32 = 1 };
@@ -65,9 +76,9 @@ enum { FP4R_GRID_E2M1 = 0, FP4R_GRID_UNIFORM = 1, FP4R_GRID_E2M1_CAP2 = 2 };
 
 typedef struct {
   int32_t format;   /* FP4R_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS /
-                       _MXFP4_OAS16 */
-  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16) or 32 (MXFP4,
-                       MXFP4_OAS) */
+                       _MXFP4_OAS16 / _HIF4 */
+  int32_t block;    /* 16 (NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16), 32 (MXFP4,
+                       MXFP4_OAS) or 64 (HIF4) */
   int32_t axis;     /* FP4R_ROW: quantize along rows of x; FP4R_COL: of x^T */
   int32_t rounding; /* FP4R_RTNE or FP4R_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0: off, 1: 16-point RHT before quantization */
@@ -107,6 +118,12 @@ int fp4r_e8m0_exponent(float amax);
 float fp4r_round8(float x);
 /* MBS-Static macro scale of a 128-element piece: round8(amax / 6). */
 float fp4r_mbs_macro_scale(float amax);
+
+/* HiF4's E6M2 block scale (unsigned, 6 exponent bits with bias 31, 2
+ * mantissa bits, subnormals, all 256 bytes finite): round to nearest even,
+ * saturating at byte 0xFF = 1.75 * 2^32.  r must be >= 0. */
+uint8_t fp4r_e6m2_encode(float r);
+float fp4r_e6m2_decode(uint8_t b);
 
 /* Overflow-aware MX exponent ([MXFP4] 2.A): the e that places amax / 2^e
  * in (3.5, 7], i.e. the smallest e with amax <= 7 * 2^e, clamped to
@@ -152,6 +169,7 @@ void fp4r_quantize_block(const float* y, const fp4r_params* p,
                          uint8_t* codes_out);
 
 /* ---- array forms of the primitives, for the tests' pins ---------------- */
+void fp4r_e6m2_encode_n(const float* r, int64_t n, uint8_t* out);
 void fp4r_e4m3_encode_n(const float* r, int64_t n, uint8_t* out);
 void fp4r_round_n(const float* m, int64_t n, int grid, int rounding,
                   const uint32_t* u16, uint8_t* k_out);
