@@ -48,8 +48,10 @@ METRIC = "fused RHT+FP4 quantize GB/s (BF16 in) at 1 GPU; % of HBM peak"
 KERNEL_SOURCES = ["block_scaled_bit_fp4_amd/csrc/" + f for f in (
     "fp4_quantize.h", "fp4_quantize_nvfp4.hip", "fp4_quantize_mxfp4.hip", "fp4_quantize_ufp4.hip",
     "fp4_quantize_mxfp4_oas.hip", "fp4_quantize_e2m1_cap2.hip", "fp4_quantize_mxfp4_mbs.hip",
-    "fp4_quantize_mxfp4_oas16.hip", "fp4_dequant.hip", "fp4_tiles.h", "fp4_device.h")]
+    "fp4_quantize_mxfp4_oas16.hip", "fp4_quantize_hif4.hip", "fp4_dequant.hip", "fp4_tiles.h",
+    "fp4_device.h")]
 MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
+NO_TS = MX + ("hif4",)  # formats with no tensor or outer scale
 
 
 GEMM_SOURCES = ["block_scaled_bit_fp4_amd/csrc/fp4_gemm.hip"]
@@ -74,7 +76,9 @@ def algorithmic_bytes(rows: int, cols: int, fmt: str, in_bytes: int, outer: bool
     dual-output call reads the input once and writes two sets."""
     n = rows * cols
     if fmt in MX:
-        return n * in_bytes + outputs * (n // 2 + n // 32)
+        return n * in_bytes + outputs * (n // 2 + n // (16 if fmt == "mxfp4_oas16" else 32))
+    if fmt == "hif4":  # a 4-byte scale word per 64 elements, no tensor scale
+        return n * in_bytes + outputs * (n // 2 + n // 16)
     return n * in_bytes + outputs * (n // 2 + n // 16 + (4 * (n // 128) if outer else 4))
 
 
@@ -102,7 +106,7 @@ def moved_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
     """Bytes the chosen algorithm moves: the algorithmic bytes plus, for a
     quantize call with a computed tensor scale (two-level formats without
     outer scales), the tensor-amax pass's second read of the input."""
-    extra = (c.op == "quantize" and c.fmt not in MX and not c.outer)
+    extra = (c.op == "quantize" and c.fmt not in MX + ("hif4",) and not c.outer)
     return op_bytes(c, rows, cols, in_bytes) + (rows * cols * in_bytes if extra else 0)
 
 
@@ -764,7 +768,7 @@ def main():
         "kernel": "call %d (%s): %s" % (
             dom, call_label(c), "fp4_rht" if c.op == "rht" else "fp4_dequantize"
             if c.op == "dequantize" else "fp4_quantize, quantize kernel"
-            if (c.fmt in MX or c.outer) else "fp4_quantize, computed tensor scale: the single-pass "
+            if (c.fmt in MX + ("hif4",) or c.outer) else "fp4_quantize, computed tensor scale: the single-pass "
             "kernel when the operand fits one resident grid, else tensor-amax + quantize kernels"),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
 
@@ -804,7 +808,7 @@ def main():
             ref = oracle.quantize(host, c.fmt, c.axis, c.rounding, c.rht, c.rht_seed, c.sr_seed)
             same = (np.array_equal(codes.cpu().numpy(), ref[0]) and
                     np.array_equal(scales.cpu().numpy(), ref[1]))
-            rep = call_report(host, pl["x"], c, codes, scales, None if c.fmt in MX else ts,
+            rep = call_report(host, pl["x"], c, codes, scales, None if c.fmt in NO_TS else ts,
                               ref)
             rep["gpu_bytes_equal_oracle"] = bool(same)
             reports[call_label(c)] = rep
@@ -813,7 +817,7 @@ def main():
                 c2 = dataclasses.replace(c, rht=False)
                 q2 = fp4.quantize(pl["x"], c.fmt, "row", c.rounding, False, 0, c.sr_seed)
                 reports[call_label(c2)] = call_report(host, pl["x"], c2, q2[0], q2[1],
-                                                      None if c.fmt in MX else q2[2])
+                                                      None if c.fmt in NO_TS else q2[2])
                 del q2
             torch.cuda.empty_cache()
 

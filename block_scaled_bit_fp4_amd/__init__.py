@@ -15,7 +15,9 @@ scale), ``"mxfp4"`` (E2M1, 32-element blocks, E8M0 scale), ``"ufp4"``
 ``"mxfp4_mbs"`` (static macro-block scaling: a macro scale with an 8-bit
 mantissa per 128 elements over 16-element E8M0 blocks; always returns the
 macro-scale array as its third result, as ``outer=True`` does),
-``"mxfp4_oas16"`` (overflow-aware E8M0 scales on 16-element blocks).
+``"mxfp4_oas16"`` (overflow-aware E8M0 scales on 16-element blocks), ``"hif4"``
+(HiF4: an E6M2 scale per 64 elements refined by one-bit E1M0 factors per 8
+and per 4 elements, E1M2 elements; four scale bytes per block).
 The two-level formats (NVFP4, the uniform grid, the cut E2M1) also take
 double-block scales (``outer=True``): one FP32 outer scale per 128 elements
 of each row of the quantized operand instead of the tensor scale.
@@ -40,11 +42,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4.so")
 
 FORMATS = {"nvfp4": 0, "mxfp4": 1, "ufp4": 2, "mxfp4_oas": 3, "e2m1_cap2": 4, "mxfp4_mbs": 5,
-           "mxfp4_oas16": 6}
+           "mxfp4_oas16": 6, "hif4": 7}
 BLOCK = {"nvfp4": 16, "mxfp4": 32, "ufp4": 16, "mxfp4_oas": 32, "e2m1_cap2": 16,
-         "mxfp4_mbs": 16, "mxfp4_oas16": 16}
+         "mxfp4_mbs": 16, "mxfp4_oas16": 16, "hif4": 64}
+# scale bytes per block: one, but four for HiF4 (E6M2 byte and 8 + 16 E1M0 bits)
+SCALE_BYTES = {f: (4 if f == "hif4" else 1) for f in BLOCK}
 ALWAYS_OUTER = ("mxfp4_mbs",)  # formats that exist only with 128-element macro scales
 MX = ("mxfp4", "mxfp4_oas", "mxfp4_oas16")
+NO_TENSOR_SCALE = MX + ("hif4",)  # every scale per block: no tensor or outer scale
 OUTER = 128  # elements per outer scale (double-block mode)
 TS_COMPUTE, TS_GIVEN, TS_OUTER128 = 0, 1, 2
 AXES = {"row": 0, "col": 1}
@@ -202,7 +207,7 @@ def new_workspace(rows: int, cols: int, params: Params, device) -> Optional[torc
 
 def output_shapes(rows: int, cols: int, fmt: str, axis: str):
     ra, w = (rows, cols) if axis == "row" else (cols, rows)
-    return (ra, w // 2), (ra, w // BLOCK[fmt])
+    return (ra, w // 2), (ra, w // BLOCK[fmt] * SCALE_BYTES[fmt])
 
 
 def outer_shape(rows: int, cols: int, axis: str):
@@ -227,7 +232,7 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in NO_TENSOR_SCALE
     given = tensor_scale is not None and not outer
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
     cshape, sshape = output_shapes(rows, cols, fmt, axis)
@@ -241,7 +246,7 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
         if outer:
             ts = ts_out if ts_out is not None else al.empty(
                 outer_shape(rows, cols, axis), torch.float32, dev, "the outer-scale array")
-        elif fmt not in MX:
+        elif fmt not in NO_TENSOR_SCALE:
             if given:
                 ts = tensor_scale if torch.is_tensor(tensor_scale) else al.scalar(
                     tensor_scale, dev, "the given tensor scale")
@@ -274,7 +279,7 @@ def quantize_noalloc(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row",
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in NO_TENSOR_SCALE
     given = tensor_scale is not None and not outer
     p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, given, outer)
     cshape, sshape = output_shapes(rows, cols, fmt, axis)
@@ -288,7 +293,7 @@ def quantize_noalloc(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row",
         if outer:
             ts = ts_out if ts_out is not None else al.empty(
                 outer_shape(rows, cols, axis), torch.float32, dev, "the outer-scale array")
-        elif fmt not in MX:
+        elif fmt not in NO_TENSOR_SCALE:
             if given:
                 ts = tensor_scale if torch.is_tensor(tensor_scale) else al.scalar(
                     tensor_scale, dev, "the given tensor scale")
@@ -316,7 +321,7 @@ def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", r
     if x.dtype not in DTYPES:
         raise TypeError("x must be bfloat16 or float32")
     rows, cols = x.shape
-    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in MX
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in NO_TENSOR_SCALE
     given = tensor_scale is not None and not outer
     p = make_params(fmt, "row", rounding, rht, rht_seed, sr_seed, given, outer)
     dev = x.device
@@ -331,7 +336,7 @@ def quantize_dual(x: torch.Tensor, fmt: str = "nvfp4", rounding: str = "rtne", r
             if outer:
                 ts = al.empty(outer_shape(rows, cols, axis), torch.float32, dev,
                               "the outer-scale array")
-            elif fmt not in MX:
+            elif fmt not in NO_TENSOR_SCALE:
                 if given:
                     v = tensor_scale[0 if axis == "row" else 1]
                     ts = v if torch.is_tensor(v) else al.scalar(v, dev, "the given tensor scale")

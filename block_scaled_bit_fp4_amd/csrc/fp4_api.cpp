@@ -56,12 +56,15 @@ bool is_mx(int32_t format) {
   return format == FP4_MXFP4 || format == FP4_MXFP4_OAS || format == FP4_MXFP4_OAS16;
 }
 
-// Block size of each format: 16, but 32 for MXFP4 and MXFP4_OAS.
+// Block size of each format: 16, but 32 for MXFP4 and MXFP4_OAS, 64 for HiF4.
 int32_t block_of(int32_t format) {
+  if (format == FP4_HIF4) return 64;
   return (format == FP4_MXFP4 || format == FP4_MXFP4_OAS) ? 32 : 16;
 }
 
-bool two_level(const fp4_params* p) { return !is_mx(p->format); }
+// Formats with a tensor scale (computed or given) or outer scales; the MX
+// formats and HiF4 carry every scale per block.
+bool two_level(const fp4_params* p) { return !is_mx(p->format) && p->format != FP4_HIF4; }
 
 bool outer_scales(const fp4_params* p) {
   return two_level(p) && p->ts_mode == FP4_TS_OUTER128;
@@ -71,7 +74,7 @@ fp4_status check_params(const fp4_params* p) {
   if (!p) return FP4_ERR_NULL;
   if (p->format != FP4_NVFP4 && p->format != FP4_MXFP4 && p->format != FP4_UFP4 &&
       p->format != FP4_MXFP4_OAS && p->format != FP4_E2M1_CAP2 && p->format != FP4_MXFP4_MBS &&
-      p->format != FP4_MXFP4_OAS16)
+      p->format != FP4_MXFP4_OAS16 && p->format != FP4_HIF4)
     return FP4_ERR_FORMAT;
   if (p->format == FP4_MXFP4_MBS && p->ts_mode != FP4_TS_OUTER128) return FP4_ERR_FORMAT;
   if (p->block != block_of(p->format)) return FP4_ERR_FORMAT;
@@ -305,7 +308,7 @@ fp4_status fp4_quantize_dual(const void* x, int32_t in_dtype, int64_t rows, int6
     if (!aligned16(workspace)) return FP4_ERR_ALIGN;
   }
   // fused tiles: BF16, whole 128 x 128 tiles, a tile's byte extent below 2^31
-  const bool fused = !empty && in_dtype == FP4_BF16 && !is_mx(p->format) && rows % 128 == 0 &&
+  const bool fused = !empty && in_dtype == FP4_BF16 && two_level(p) && rows % 128 == 0 &&
                      cols % 128 == 0 && ld * 2 * 128 < ((int64_t)1 << 31);
   if (!fused) {
     // the two single-axis calls, one after the other on the stream
@@ -439,6 +442,7 @@ hipError_t fp4_launch_quantize(const QuantLaunch& q, hipStream_t s) {
     case FP4_E2M1_CAP2: return fp4_launch_quantize_e2m1_cap2(q, s);
     case FP4_MXFP4_MBS: return fp4_launch_quantize_mxfp4_mbs(q, s);
     case FP4_MXFP4_OAS16: return fp4_launch_quantize_mxfp4_oas16(q, s);
+    case FP4_HIF4: return fp4_launch_quantize_hif4(q, s);
     default: return fp4_launch_quantize_mxfp4_oas(q, s);
   }
 }

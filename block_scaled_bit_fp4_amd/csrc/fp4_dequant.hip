@@ -114,7 +114,7 @@ __device__ __forceinline__ f2 e2m1_pair(uint32_t w, int sel) {
 // loads fly while the previous block is decoded and stored.
 template <int FMT, bool OUTER>
 struct BlockIn {
-  uint32_t S;
+  uint32_t S;  // scale byte (HiF4: the 4-byte scale word)
   float so;
   uint32_t words[block_of<FMT>() / 8];
 };
@@ -124,7 +124,10 @@ __device__ __forceinline__ BlockIn<FMT, OUTER> load_block(const DequantArgs& a, 
                                                           int64_t b) {
   constexpr int B = block_of<FMT>();
   BlockIn<FMT, OUTER> in;
-  in.S = a.scales[ra * (a.W / B) + b];
+  if constexpr (FMT == kHIF4)
+    in.S = *reinterpret_cast<const uint32_t*>(a.scales + ra * (a.W / B * 4) + b * 4);
+  else
+    in.S = a.scales[ra * (a.W / B) + b];
   // outer scales: the 128-piece of the A-row that holds block b
   in.so = OUTER ? a.ts[ra * (a.W / kOuter) + b * B / kOuter] : 0.0f;
   const uint8_t* cp = a.codes + ra * (a.W / 2) + b * (B / 2);
@@ -132,8 +135,12 @@ __device__ __forceinline__ BlockIn<FMT, OUTER> load_block(const DequantArgs& a, 
     const uint2 v = *reinterpret_cast<const uint2*>(cp);
     in.words[0] = v.x; in.words[1] = v.y;
   } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(cp);
-    in.words[0] = v.x; in.words[1] = v.y; in.words[2] = v.z; in.words[3] = v.w;
+#pragma unroll
+    for (int q = 0; q < B / 32; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(cp + 16 * q);
+      in.words[4 * q] = v.x; in.words[4 * q + 1] = v.y; in.words[4 * q + 2] = v.z;
+      in.words[4 * q + 3] = v.w;
+    }
   }
   return in;
 }
@@ -145,7 +152,9 @@ __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t,
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   const uint32_t S = in.S;
   float d;
-  if constexpr (is_mx(FMT)) {
+  if constexpr (FMT == kHIF4) {
+    d = e6m2_decode(S & 0xFFu);  // the block scale; each micro-block's step below
+  } else if constexpr (is_mx(FMT)) {
     d = S ? __uint_as_float(S << 23) : 5.877471754111438e-39f;
   } else if constexpr (FMT == kMBS) {
     d = __builtin_ldexpf(in.so, (int)S - 127);  // macro scale times 2^e_b
@@ -153,12 +162,30 @@ __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t,
     d = S ? (OUTER ? in.so : s_t) * e4m3_decode(S) : 0.0f;
   }
   const uint32_t (&words)[B / 8] = in.words;
+  // (HiF4: every step d * f8 * f4 / 4 is within [2^-38, 2^31] when d != 0)
   const bool fold = INV && d >= 0x1p-100f && d <= 0x1p100f;
   const float dm = fold ? d * 0.25f : d;
 #pragma unroll
   for (int h = 0; h < B / 16; ++h) {
     float g[16];
-    if constexpr (FMT == kUFP4) {
+    if constexpr (FMT == kHIF4) {
+      // micro-block u = 4h + j/4 of sub-block u/2: step d * f8 * f4 / 4,
+      // value k * step (exact: 3-bit k times a 3-bit significand)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = 4 * h + q;
+        const float f8 = ((S >> (8 + u / 2)) & 1u) ? 1.0f : 0.5f;
+        const float f4 = ((S >> (16 + u)) & 1u) ? 1.0f : 0.5f;
+        const float step = dm * f8 * f4 * 0.25f;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+          const int j = 4 * q + l;
+          const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
+          const float mag = (float)(c & 7u) * step;
+          g[j] = (c & 8u) ? -mag : mag;
+        }
+      }
+    } else if constexpr (FMT == kUFP4) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t c = (words[(h * 16 + j) >> 3] >> (4 * (j & 7))) & 15u;
@@ -199,7 +226,7 @@ __device__ __forceinline__ void dequant_block(const DequantArgs& a, float s_t,
 template <int FMT, bool OUTER, bool INV, int AXIS, typename T>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ out, DequantArgs a) {
   constexpr int B = block_of<FMT>();
-  const float s_t = (is_mx(FMT) || OUTER) ? 0.0f : a.ts[0];
+  const float s_t = (!has_tensor_scale(FMT) || OUTER) ? 0.0f : a.ts[0];
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
   if constexpr (AXIS == 0 && sizeof(T) == 2) {
@@ -299,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_col_tile_kernel(T* __rest
   constexpr int kRowStep = kThreads / LPR;   // A-rows between a lane's units
   constexpr int WORDS = B * (int)sizeof(T) / 4;
   __shared__ __align__(16) uint32_t lds[Tile::kWords];
-  const float s_t = (is_mx(FMT) || OUTER) ? 0.0f : a.ts[0];
+  const float s_t = (!has_tensor_scale(FMT) || OUTER) ? 0.0f : a.ts[0];
   const int64_t ntile = n_rt * n_ct;
   const int lane_ra = threadIdx.x / LPR, j = threadIdx.x % LPR;
   const int seg = threadIdx.x & 7;
@@ -449,16 +476,19 @@ hipError_t launch_dequant_t(const DequantLaunch& q, hipStream_t s) {
   // bottom strips per element
   using Tile = ColTile<T>;
   const int64_t W = q.rows;
-  const bool tiles = (q.ld_out * (int64_t)sizeof(T)) % 16 == 0;
+  // (a HiF4 FP32 tile holds fewer blocks than lanes: strips only)
+  const bool tiles = (q.ld_out * (int64_t)sizeof(T)) % 16 == 0 && !(FMT == kHIF4 && sizeof(T) == 4);
   const int64_t nrt = tiles ? q.rows / Tile::TR : 0, nct = tiles ? q.cols / Tile::TC : 0;
   const int64_t rows_main = nct > 0 ? nrt * Tile::TR : 0;
   const int64_t cols_main = nrt > 0 ? nct * Tile::TC : 0;
   DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, 0, 0, 0, 0, q.signs, 0, 0};
-  if (rows_main > 0 && cols_main > 0) {
-    const int64_t ntile = nrt * nct;
-    hipLaunchKernelGGL((dequantize_col_tile_kernel<FMT, OUTER, INV, T>),
-                       dim3((unsigned)(ntile < kTileGrid ? ntile : kTileGrid)), dim3(kThreads),
-                       0, s, out, a, nrt, nct);
+  if constexpr (!(FMT == kHIF4 && sizeof(T) == 4)) {
+    if (rows_main > 0 && cols_main > 0) {
+      const int64_t ntile = nrt * nct;
+      hipLaunchKernelGGL((dequantize_col_tile_kernel<FMT, OUTER, INV, T>),
+                         dim3((unsigned)(ntile < kTileGrid ? ntile : kTileGrid)),
+                         dim3(kThreads), 0, s, out, a, nrt, nct);
+    }
   }
   auto strip = [&](int64_t blk_begin, int64_t blk_end, int64_t col_begin, int64_t col_end) {
     if (blk_end <= blk_begin || col_end <= col_begin) return;
@@ -492,7 +522,7 @@ hipError_t dq_inv(const DequantLaunch& q, hipStream_t s) {
 }
 template <int FMT>
 hipError_t dq_outer(const DequantLaunch& q, hipStream_t s) {
-  if constexpr (is_mx(FMT)) return dq_inv<FMT, false>(q, s);
+  if constexpr (is_mx(FMT) || FMT == kHIF4) return dq_inv<FMT, false>(q, s);
   else if constexpr (FMT == kMBS) return dq_inv<FMT, true>(q, s);  // macro scales only
   else return q.outer ? dq_inv<FMT, true>(q, s) : dq_inv<FMT, false>(q, s);
 }
@@ -529,6 +559,7 @@ hipError_t fp4_launch_dequantize(const DequantLaunch& q, hipStream_t s) {
     case kCAP2: return dq_outer<kNVFP4>(q, s);  // E2M1 codes, E4M3 scales: decoded as NVFP4
     case kMBS: return dq_outer<kMBS>(q, s);
     case kMXOAS16: return dq_outer<kMXOAS16>(q, s);
+    case kHIF4: return dq_outer<kHIF4>(q, s);
     default: return dq_outer<kMXOAS>(q, s);
   }
 }

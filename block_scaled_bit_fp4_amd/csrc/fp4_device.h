@@ -27,7 +27,11 @@ namespace fp4dev {
 // scales), 16-element blocks with E8M0 scales relative to it, E2M1 codes.
 // kMXOAS16: overflow-aware MX scaling on 16-element blocks, the granularity
 // at which [MXFP4] 2 applies its techniques (E8M0 per 16 elements).
-enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4, kMBS = 5, kMXOAS16 = 6 };
+// kHIF4: HiF4 ([HIF] 2. Metodologia): per 64-element block an E6M2 scale,
+// per 8 and per 4 elements a one-bit E1M0 refinement, E1M2 elements (k/4);
+// its scale word (4 bytes per block) is described at encode_hif4.
+enum : int { kNVFP4 = 0, kMXFP4 = 1, kUFP4 = 2, kMXOAS = 3, kCAP2 = 4, kMBS = 5, kMXOAS16 = 6,
+             kHIF4 = 7 };
 // Tensor-scale modes of the two-level formats: computed from the data,
 // given by the caller, or one outer scale per kOuter elements of an A-row.
 enum : int { kTsCompute = 0, kTsGiven = 1, kTsOuter = 2 };
@@ -37,8 +41,17 @@ constexpr int kOuter = 128;
 constexpr bool is_mx(int fmt) { return fmt == kMXFP4 || fmt == kMXOAS || fmt == kMXOAS16; }
 // Overflow-aware MX exponents ([MXFP4] 2.A).
 constexpr bool is_oas(int fmt) { return fmt == kMXOAS || fmt == kMXOAS16; }
+// A tensor scale (computed or given) or outer scales per 128 elements: the
+// E4M3 two-level formats and MBS-Static.  The MX formats and HiF4 carry
+// every scale per block.
+constexpr bool has_tensor_scale(int fmt) { return !is_mx(fmt) && fmt != kHIF4; }
 template <int FMT>
-constexpr int block_of() { return (is_mx(FMT) && FMT != kMXOAS16) ? 32 : 16; }
+constexpr int block_of() {
+  return FMT == kHIF4 ? 64 : ((is_mx(FMT) && FMT != kMXOAS16) ? 32 : 16);
+}
+// Scale bytes per block: 4 for HiF4's scale word, 1 otherwise.
+template <int FMT>
+constexpr int scale_bytes() { return FMT == kHIF4 ? 4 : 1; }
 
 // ---------------------------------------------------------------- widening
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -193,6 +206,29 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = c >> 3, m = c & 7u;
   const float sub = (float)m * 0.001953125f;  // m * 2^-9
   const float nor = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nor;
+}
+
+// HiF4's E6M2 block scale ([HIF] 2. Metodologia; reading: unsigned, exponent
+// bias 31, subnormal step 2^-32, every byte finite) of r >= 0, round to
+// nearest even, saturating at byte 0xFF = 1.75 * 2^32.  Below 2^-30 the
+// format is subnormal: code rint(r * 2^32) (4 is the smallest normal, so
+// the carry lands right); above, the binary32 significand is rounded to 2
+// bits and the exponent rebiased (127 - 31 = 96, times 4 for the mantissa
+// bits); past the top the code exceeds 255 and clamps.  Branch-free.
+__device__ __forceinline__ uint32_t e6m2_encode(float r) {
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(r, 0x1p-30f) * 0x1p32f);
+  uint32_t b = __float_as_uint(r);
+  b += 0xFFFFFu + ((b >> 21) & 1u);
+  const uint32_t nor = (b >> 21) - (96u << 2);
+  const uint32_t s = r < 0x1p-30f ? sub : nor;
+  return s < 255u ? s : 255u;
+}
+
+__device__ __forceinline__ float e6m2_decode(uint32_t c) {
+  const uint32_t e = c >> 2, m = c & 3u;
+  const float sub = (float)m * 0x1p-32f;
+  const float nor = __uint_as_float(((e + 96u) << 23) | (m << 21));
   return e == 0 ? sub : nor;
 }
 

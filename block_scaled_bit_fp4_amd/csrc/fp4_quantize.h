@@ -137,13 +137,13 @@ __device__ __forceinline__ ScaleFetch scale_fetch(const float* partials, int npa
   ScaleFetch f;
 #pragma unroll
   for (int k = 0; k < kFetch; ++k) f.v[k] = 0.0f;
-  if constexpr (!is_mx(FMT) && TSM == kTsCompute) {
+  if constexpr (has_tensor_scale(FMT) && TSM == kTsCompute) {
 #pragma unroll
     for (int k = 0; k < kFetch; ++k) {
       const int i = threadIdx.x + k * kThreads;
       if (i < npartials) f.v[k] = partials[i];
     }
-  } else if constexpr (!is_mx(FMT) && TSM == kTsGiven) {
+  } else if constexpr (has_tensor_scale(FMT) && TSM == kTsGiven) {
     f.v[0] = ts_in[0];
   }
   return f;
@@ -157,7 +157,7 @@ template <int FMT, int TSM>
 __device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* ts_out,
                                                    float* inv_tab) {
   ScaleCtx c{0.0f, 0.0f};
-  if constexpr (!is_mx(FMT) && TSM != kTsOuter) {
+  if constexpr (has_tensor_scale(FMT) && TSM != kTsOuter) {
     if (TSM == kTsGiven) {
       c.s_t = f.v[0];
     } else {
@@ -293,6 +293,66 @@ __device__ __forceinline__ uint32_t encode8_careful(const float* y, float inv,
   return word;
 }
 
+// One HiF4 block of 64 ([HIF] 2. Metodologia: an E6M2 scale per 64
+// elements, E1M0 scales per 8 and per 4, E1M2 elements).  Reading: the
+// block maximum maps to the top element level 7/4, S = E6M2(amax / 1.75);
+// a sub-block (micro-block) halves its scale when its maximum still fits
+// under the top level after halving: factor 1/2 iff max <= 0.875 * S
+// (times the sub-block's factor); codes k of |y| / d on the uniform grid
+// 0..7 with d = S * f8 * f4 / 4.  Scale word: byte 0 = S, bits 8..15 the
+// sub-block factors, bits 16..31 the micro-block factors (bit set: factor
+// 1; clear: 1/2).  1/d = (1/S) * 4 / (f8 * f4): the binary32 reciprocal
+// scaled by a power of two, exact (nothing leaves the normal range), so one
+// division serves the sixteen micro-blocks.  The maxima compare in the y
+// domain (t / 4 with the RHT, exact).
+template <bool SR, bool RHT, bool BF16IN, bool PRE>
+__device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, uint32_t k0,
+                                            uint32_t k1, uint64_t n0, uint32_t (&packed)[8],
+                                            uint32_t& sword, const uint32_t* pre) {
+  constexpr bool kFold = RHT && BF16IN;
+  const float amax = RHT ? amax_t * 0.25f : amax_t;
+  const uint32_t S = e6m2_encode(amax / 1.75f);
+  const float D = e6m2_decode(S);
+  const float thr = 0.875f * D;
+  const float invD = D != 0.0f ? 1.0f / D : 0.0f;
+  uint32_t word = S;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float a4[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float* tp = t + 8 * s + 4 * m;
+      const float mx = fmaxf(fmaxf(fabsf(tp[0]), fabsf(tp[1])), fmaxf(fabsf(tp[2]), fabsf(tp[3])));
+      a4[m] = RHT ? mx * 0.25f : mx;
+    }
+    const bool keep8 = !(fmaxf(a4[0], a4[1]) <= thr);
+    word |= (uint32_t)keep8 << (8 + s);
+    const float thr4 = keep8 ? thr : thr * 0.5f;
+    float v[8];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bool keep4 = !(a4[m] <= thr4);
+      word |= (uint32_t)keep4 << (16 + 2 * s + m);
+      const float inv = invD * (keep8 ? 4.0f : 8.0f) * (keep4 ? 1.0f : 2.0f);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const float tv = t[8 * s + 4 * m + l];
+        v[4 * m + l] = kFold ? tv * (inv * 0.25f) : (RHT ? tv * 0.25f : tv) * inv;
+      }
+    }
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+    if constexpr (SR && PRE) {
+      r[0] = pre[4 * s]; r[1] = pre[4 * s + 1]; r[2] = pre[4 * s + 2]; r[3] = pre[4 * s + 3];
+    } else if constexpr (SR) {
+      const uint64_t g = (n0 >> 3) + (uint64_t)s;
+      const u32x4 o = philox4x32_10(k0, k1, (uint32_t)g, (uint32_t)(g >> 32), 0u, 0u);
+      r[0] = o.x; r[1] = o.y; r[2] = o.z; r[3] = o.w;
+    }
+    packed[s] = encode8_fast<kUFP4, SR>(v, r);
+  }
+  sword = word;
+}
+
 // Code one block.  t[] holds the rotated values before the 1/4 (RHT) or the
 // plain values, amax_t their largest magnitude, n0 the logical index of the
 // first element (SR draws).
@@ -311,6 +371,10 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
                                              const float* inv_tab, uint32_t k0, uint32_t k1,
                                              uint64_t n0, uint32_t (&packed)[B / 8],
                                              uint32_t& sbyte, const uint32_t* pre = nullptr) {
+  if constexpr (FMT == kHIF4) {
+    encode_hif4<SR, RHT, BF16IN, PRE>(t, amax_t, k0, k1, n0, packed, sbyte, pre);
+    return;
+  }
   constexpr bool kFold = RHT && BF16IN;
   const float amax_b = RHT ? amax_t * 0.25f : amax_t;
   float inv;
@@ -370,8 +434,9 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
 }
 
 // ------------------------------------------------------------- row axis
-// Store the codes and block scales of one unit of U elements of an A-row.
-template <int B, int U>
+// Store the codes and block scales of one unit of U elements of an A-row
+// (SB scale bytes per block: a HiF4 scale word is one 4-byte store).
+template <int B, int U, int SB = 1>
 __device__ __forceinline__ void store_row_unit(const uint32_t (&packed)[U / 8],
                                                const uint32_t (&sb)[U / B], int64_t row,
                                                int64_t minor, const QuantArgs& a) {
@@ -385,8 +450,10 @@ __device__ __forceinline__ void store_row_unit(const uint32_t (&packed)[U / 8],
   } else {
     store8<true>(cp, packed[0], packed[1]);
   }
-  uint8_t* sp = a.scales + row * (a.W / B) + minor * NBU;
-  if constexpr (NBU == 4)
+  uint8_t* sp = a.scales + row * (a.W / B * SB) + minor * NBU * SB;
+  if constexpr (SB == 4)
+    *reinterpret_cast<uint32_t*>(sp) = sb[0];
+  else if constexpr (NBU == 4)
     *reinterpret_cast<uint32_t*>(sp) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
   else if constexpr (NBU == 2)
     *reinterpret_cast<uint16_t*>(sp) = (uint16_t)(sb[0] | (sb[1] << 8));
@@ -453,7 +520,7 @@ __device__ __forceinline__ void code_row_unit(const RowRaw<T, U>& cur, int64_t r
       code(bi, t, amax_t, c);
     }
   }
-  store_row_unit<B, U>(packed, sb, row, minor, a);
+  store_row_unit<B, U, scale_bytes<FMT>()>(packed, sb, row, minor, a);
 }
 
 // Units: major = A-row, minor = piece of U elements within it.
@@ -467,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(const T* __restr
   // After a tensor-amax pass the rows are taken last to first: the end of
   // the input, read last by that pass, is then still in the memory-side
   // cache when this pass starts.
-  constexpr bool kRev = TSM == kTsCompute && !is_mx(FMT);
+  constexpr bool kRev = TSM == kTsCompute && has_tensor_scale(FMT);
   auto row_of = [&](int64_t m) { return kRev ? a.n_major - 1 - m : m; };
   bool have = w.major < a.n_major;
   const ScaleFetch sf = scale_fetch<FMT, TSM>(a.partials, a.npartials, a.ts_in);
@@ -894,8 +961,9 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
     // stores: NB*B/2 contiguous code bytes and NB scale bytes per column
 #pragma unroll
     for (int k = 0; k < C; ++k) {
+      constexpr int SB = scale_bytes<FMT>();
       uint8_t* cp = a.codes + (col + k) * (a.W / 2) + blk0 * (B / 2);
-      uint8_t* sp = a.scales + (col + k) * a.nblk_axis + blk0;
+      uint8_t* sp = a.scales + (col + k) * a.nblk_axis * SB + blk0 * SB;
       if (nb == NB && vec_codes) {
 #pragma unroll
         for (int q = 0; q < NB * WPB; q += 4)
@@ -912,9 +980,14 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
           }
         }
       }
+      if constexpr (SB == 4) {
+        static_assert(NB == 1, "one HiF4 block per run");
+        *reinterpret_cast<uint32_t*>(sp) = sbw[k][0];
+      } else {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        if (j < nb) sp[j] = (uint8_t)(sbw[k][j / 4] >> (8 * (j % 4)));
+        for (int j = 0; j < NB; ++j)
+          if (j < nb) sp[j] = (uint8_t)(sbw[k][j / 4] >> (8 * (j % 4)));
+      }
     }
     w.advance(a.sq, a.sr, a.M);
   }
@@ -930,8 +1003,8 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(const T* __restr
 // with a grid stride and loads its next tile while coding the current one.
 
 template <int FMT, bool SR, bool RHT, int TSM, typename T>
-__global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T* __restrict__ x,
-                                                                     QuantArgs a) {
+__global__ __launch_bounds__(kThreads, block_of<FMT>() == 64 ? 2 : 4) void quantize_col_tile_kernel(
+    const T* __restrict__ x, QuantArgs a) {
   using Tile = ColTile<T>;
   constexpr int B = block_of<FMT>();
   constexpr int TR = Tile::TR, TC = Tile::TC;
@@ -953,7 +1026,7 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
                                        seg * (16 / (int)sizeof(T))) * (uint32_t)sizeof(T);
   // After a tensor-amax pass the row tiles are taken last to first (the end
   // of the input, read last by that pass, is still in the memory-side cache)
-  constexpr bool kRev = TSM == kTsCompute && !is_mx(FMT);
+  constexpr bool kRev = TSM == kTsCompute && has_tensor_scale(FMT);
   auto rt = [&](int64_t t) { return kRev ? a.n_major - 1 - t : t; };
   auto load_tile = [&](int64_t tr, int64_t tc, uint4 (&buf)[kLoads]) {
     const char* base = reinterpret_cast<const char*>(x + rt(tr) * TR * a.ld + tc * TC);
@@ -1015,8 +1088,9 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
     // units one at a time for 32-element blocks (register pressure)
     const int64_t ra0 = c0 + lane_ra;  // A-row = column of x
     const int64_t rb = r0 / B + j;     // block index along the A-row
+    constexpr int SB = scale_bytes<FMT>();
     uint8_t* cp0 = a.codes + ra0 * (a.W / 2) + rb * (B / 2);
-    uint8_t* sp0 = a.scales + ra0 * a.nblk_axis + rb;
+    uint8_t* sp0 = a.scales + ra0 * a.nblk_axis * SB + rb * SB;
     const uint64_t n00 = (uint64_t)ra0 * (uint64_t)a.W + (uint64_t)(rb * B);
     constexpr int kUnroll = B == 32 ? 1 : kUnits;
 #pragma unroll kUnroll
@@ -1062,9 +1136,17 @@ __global__ __launch_bounds__(kThreads, 4) void quantize_col_tile_kernel(const T*
       encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
                                                          a.sr_k1, n0, pk, sbyte);
       uint8_t* cp = cp0 + di * (a.W / 2);
-      if constexpr (B == 16) store8<true>(cp, pk[0], pk[1]);
-      else store16<true>(cp, pk[0], pk[1], pk[2], pk[3]);
-      sp0[di * a.nblk_axis] = (uint8_t)sbyte;
+      if constexpr (B == 16) {
+        store8<true>(cp, pk[0], pk[1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < B / 32; ++q)
+          store16<true>(cp + 16 * q, pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+      }
+      if constexpr (SB == 4)
+        *reinterpret_cast<uint32_t*>(sp0 + di * a.nblk_axis * 4) = sbyte;
+      else
+        sp0[di * a.nblk_axis] = (uint8_t)sbyte;
     }
     tile = next;
     tr = ntr;
@@ -1509,7 +1591,7 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   a.signs = q.signs;
   a.sr_k0 = q.sr_k0;
   a.sr_k1 = q.sr_k1;
-  if constexpr (!is_mx(FMT) && FMT != kMBS && TSM == kTsCompute) {
+  if constexpr (has_tensor_scale(FMT) && FMT != kMBS && TSM == kTsCompute) {
     if (FP4_SINGLE_PASS && q.axis == 0 && q.cols % 32 == 0 && q.call_tag != 0 &&
         q.ws_bytes >= kSinglePassWsBytes &&
         (try_single_pass<FMT, SR, RHT, T, 1, 1024>(q, a, s) ||
@@ -1517,11 +1599,12 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
          try_single_pass<FMT, SR, RHT, T, 4, 256>(q, a, s)))
       return hipGetLastError();
   }
-  if (!is_mx(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
+  if constexpr (has_tensor_scale(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
   if (q.axis == 0) {
     a.W = q.cols;
     const bool wide = q.cols % 32 == 0;
-    const bool wider = FP4_ROW_UNIT >= 64 && q.cols % 64 == 0;
+    // a HiF4 block (64) is one lane's unit
+    const bool wider = (FP4_ROW_UNIT >= 64 || FMT == kHIF4) && q.cols % 64 == 0;
     const int U = wider ? 64 : (wide ? 32 : 16);
     a.n_major = q.rows;
     a.M = q.cols / U;
@@ -1532,12 +1615,14 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       a.sr = wp.sr;
       hipLaunchKernelGGL(kernel, dim3(wp.grid), dim3(kThreads), 0, s, x, a);
     };
-    if (wider)
+    if (wider) {
       launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 64>);
-    else if (wide)
-      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 32>);
-    else if constexpr (B == 16)
-      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 16>);
+    } else if constexpr (B <= 32) {
+      if (wide)
+        launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 32>);
+      else if constexpr (B == 16)
+        launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 16>);
+    }
   } else {
     a.W = q.rows;
     a.nblk_axis = q.rows / B;
@@ -1545,24 +1630,30 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
     // interior: whole tiles; edges (bottom rows, right columns): run kernel
     const int64_t nrt = q.rows / Tile::TR, nct = q.cols / Tile::TC;
     // (a tile's byte extent below 2^31 keeps its per-lane load offsets in 32 bits)
+    // (a HiF4 FP32 tile holds fewer blocks than lanes: runs only)
     const bool tiles = nrt > 0 && nct > 0 && (q.ld * (int64_t)sizeof(T)) % 16 == 0 &&
-                       q.ld * (int64_t)sizeof(T) * Tile::TR < ((int64_t)1 << 31);
+                       q.ld * (int64_t)sizeof(T) * Tile::TR < ((int64_t)1 << 31) &&
+                       !(FMT == kHIF4 && sizeof(T) == 4);
     const int64_t rows_main = tiles ? nrt * Tile::TR : 0;
     const int64_t cols_main = tiles ? nct * Tile::TC : 0;
-    if (tiles) {
-      QuantArgs t = a;
-      t.n_major = nrt;
-      t.M = nct;
-      const int64_t ntile = nrt * nct;
-      // more workgroups than fit at once measured faster here than one
-      // resident wave
-      const unsigned grid = (unsigned)(ntile < kColGrid ? ntile : kColGrid);
-      hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, TSM, T>), dim3(grid),
-                         dim3(kThreads), 0, s, x, t);
+    if constexpr (!(FMT == kHIF4 && sizeof(T) == 4)) {
+      if (tiles) {
+        QuantArgs t = a;
+        t.n_major = nrt;
+        t.M = nct;
+        const int64_t ntile = nrt * nct;
+        // more workgroups than fit at once measured faster here than one
+        // resident wave
+        const unsigned grid = (unsigned)(ntile < kColGrid ? ntile : kColGrid);
+        hipLaunchKernelGGL((quantize_col_tile_kernel<FMT, SR, RHT, TSM, T>), dim3(grid),
+                           dim3(kThreads), 0, s, x, t);
+      }
     }
     // runs of 128 rows (64 with SR, whose Philox state needs the registers)
     // (one 128-piece per run with outer scales)
+    // (one 64-element block per run for HiF4: its registers)
     constexpr int NB = TSM == kTsOuter ? kOuter / B
+                       : B == 64       ? 1
                                        : (B == 16 ? kColBlocks : kColBlocks / 2) / (SR ? 2 : 1);
     auto run = [&](int64_t blk_begin, int64_t blk_end, int64_t col_begin, int64_t col_end) {
       if (blk_end <= blk_begin || col_end <= col_begin) return;
@@ -1571,17 +1662,20 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       r.blk_end = blk_end;
       r.col_begin = col_begin;
       r.n_major = (blk_end - blk_begin + NB - 1) / NB;
-      const int C = (FP4_COL_PAIR && (col_end - col_begin) % 2 == 0) ? 2 : 1;
+      const int C = (FP4_COL_PAIR && B < 64 && (col_end - col_begin) % 2 == 0) ? 2 : 1;
       r.M = (col_end - col_begin) / C;
       const WalkPlan wp = plan_walk(r.n_major, r.M, kColGrid);
       r.sq = wp.sq;
       r.sr = wp.sr;
-      if (C == 2)
-        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 2, NB>), dim3(wp.grid),
-                           dim3(kThreads), 0, s, x, r);
-      else
-        hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 1, NB>), dim3(wp.grid),
-                           dim3(kThreads), 0, s, x, r);
+      if constexpr (B < 64) {
+        if (C == 2) {
+          hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 2, NB>), dim3(wp.grid),
+                             dim3(kThreads), 0, s, x, r);
+          return;
+        }
+      }
+      hipLaunchKernelGGL((quantize_col_kernel<FMT, SR, RHT, TSM, T, 1, NB>), dim3(wp.grid),
+                         dim3(kThreads), 0, s, x, r);
     };
     // right strip over the tiled rows, then the bottom strip over all columns
     run(0, rows_main / B, cols_main, q.cols);
@@ -1597,7 +1691,7 @@ hipError_t pick_dtype(const QuantLaunch& q, hipStream_t s) {
 }
 template <int FMT, bool SR, bool RHT>
 hipError_t pick_tsm(const QuantLaunch& q, hipStream_t s) {
-  if constexpr (is_mx(FMT)) {
+  if constexpr (is_mx(FMT) || FMT == kHIF4) {
     return pick_dtype<FMT, SR, RHT, kTsCompute>(q, s);  // no tensor scale
   } else if constexpr (FMT == kMBS) {
     return pick_dtype<FMT, SR, RHT, kTsOuter>(q, s);  // macro scales only

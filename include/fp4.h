@@ -67,7 +67,7 @@
  *  - x: rows x cols, leading dimension ld (elements), BF16 or FP32.
  *  - codes: rows_A x (W / 2) bytes; byte (i, j/2) holds A[i][j], even j in
  *    the low nibble.  rows_A = rows (ROW) or cols (COL); W = cols or rows.
- *  - scales: rows_A x (W / B) bytes.
+ *  - scales: rows_A x (W / B) bytes (HiF4: 4 bytes per block).
  *  - tensor_scale (two-level formats only): one float; with FP4_TS_OUTER128,
  *    rows_A x (W / 128) floats, row-major (requires W % 128 == 0).
  *
@@ -129,6 +129,21 @@ typedef int32_t fp4_status;
  * E8M0 byte per 16 elements with 3.5 < amax_b / 2^e <= 7, E2M1 elements
  * saturating at 6, no tensor scale.  Block 16. */
 #define FP4_MXFP4_OAS16 6
+/* HiF4 ("Unleashing Low-Bit Inference on Ascend NPUs: A Comprehensive
+ * Evaluation of HiFloat Formats", 2. Metodologia: an E6M2 scale per 64
+ * elements, E1M0 scales per 8 and per 4 elements, E1M2 elements).  The page
+ * gives no selection or rounding rule; reading: element magnitudes k/4
+ * (k = 0..7, the E1M2 values with bias 1); S = E6M2 (unsigned, bias 31,
+ * subnormal step 2^-32, saturating at 1.75 * 2^32) of amax_64 / 1.75,
+ * rounded to nearest even; an 8-element sub-block takes factor 1/2 iff its
+ * maximum <= 0.875 * S, else 1; a 4-element micro-block takes 1/2 iff its
+ * maximum <= 0.875 * S * (its sub-block's factor), else 1; step d = S *
+ * f8 * f4 / 4; codes k = the uniform-grid rounding (RTNE or SR, saturating
+ * at 7) of |y| * (1/d), sign in bit 3.  No tensor scale.  Block 64 (W %
+ * 64 == 0).  Scales: 4 bytes per block, rows_A x (W / 16) bytes: byte 0 =
+ * S, byte 1 = the 8 sub-block bits, bytes 2-3 = the 16 micro-block bits
+ * (bit i for the i-th piece of the block, little-endian; set: factor 1). */
+#define FP4_HIF4 7
 
 #define FP4_AXIS_ROW 0 /* quantize along rows of x */
 #define FP4_AXIS_COL 1 /* quantize along columns of x (output is x^T-major) */
@@ -146,12 +161,12 @@ typedef int32_t fp4_status;
 typedef struct {
   int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
   int32_t block;    /* 16 for NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16; 32 for MXFP4,
-                       MXFP4_OAS */
+                       MXFP4_OAS; 64 for HIF4 */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
   int32_t rounding; /* FP4_RTNE / FP4_SR (elements only; scales are RTNE) */
   int32_t rht;      /* 0 = off, 1 = 16-point RHT before quantization */
-  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for MXFP4, MXFP4_OAS and
-                       MXFP4_OAS16;
+  int32_t ts_mode;  /* FP4_TS_COMPUTE / _GIVEN / _OUTER128 (ignored for MXFP4, MXFP4_OAS,
+                       MXFP4_OAS16 and HIF4;
                        MXFP4_MBS requires _OUTER128) */
   uint64_t rht_seed;
   uint64_t sr_seed;

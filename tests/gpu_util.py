@@ -69,7 +69,7 @@ def quantize_both(x: np.ndarray, fmt, axis="row", rounding="rtne", rht=False, rh
     assert_bytes_equal(to_host(c), oc, "codes " + tag)
     if outer:
         assert_bytes_equal(to_host(ts).view(np.uint32), ots.view(np.uint32), "outer scales " + tag)
-    elif fmt not in fp4.MX:
+    elif fmt not in fp4.NO_TENSOR_SCALE:
         assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots), "tensor scale " + tag
     return c, s, ts, (oc, osc, ots)
 

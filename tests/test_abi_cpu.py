@@ -84,6 +84,11 @@ def test_quantize_validation(lib):
     assert _q(lib, bad) == -2
     bad = P("mxfp4_oas"); bad.block = 16
     assert _q(lib, bad) == -2
+    bad = P("hif4"); bad.block = 16                               # HiF4 blocks are 64
+    assert _q(lib, bad) == -2
+    assert _q(lib, P("hif4"), cols=96, ld=96) == -3               # W % 64
+    assert fp4.workspace_bytes(64, 64, P("hif4")) == 0
+    assert fp4.output_shapes(64, 128, "hif4", "row") == ((64, 64), (64, 8))
     bad = P("mxfp4_oas16"); bad.block = 32                        # OAS16 is E8M0 per 16
     assert _q(lib, bad) == -2
     assert _q(lib, P("mxfp4_oas16"), cols=40, ld=40) == -3       # W % 16

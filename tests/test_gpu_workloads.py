@@ -27,7 +27,7 @@ def _dual_full(x, call):
         assert_bytes_equal(to_host(c), oc, "dual codes " + axis)
         if call.outer:
             assert_bytes_equal(to_host(t).view(np.uint32), ots.view(np.uint32), "dual outer")
-        elif call.fmt not in fp4.MX:
+        elif call.fmt not in fp4.NO_TENSOR_SCALE:
             assert to_host(t).view(np.uint32)[0] == np.float32(ots).view(np.uint32)
 
 

@@ -200,6 +200,16 @@ def _w_mx_weight_oas16() -> Workload:
     return w
 
 
+def _w_hif4_weight() -> Workload:
+    w = _w_mx_weight()
+    w.name = "hif4_weight_8192x8192"
+    w.description = ("8192x8192 BF16 N(0, 0.02^2): HiF4 (E6M2 per 64, E1M0 per 8 and per 4, E1M2 "
+                     "elements), RTNE, row and column axis, RHT off and on")
+    for c in w.calls:
+        c.fmt = "hif4"
+    return w
+
+
 def _w_mx_weight_mbs() -> Workload:
     w = _w_mx_weight()
     w.name = "mxfp4_mbs_weight_8192x8192"
@@ -300,6 +310,7 @@ WORKLOADS = {
     "mx_weight_oas": _w_mx_weight_oas,
     "mx_weight_mbs": _w_mx_weight_mbs,
     "mx_weight_oas16": _w_mx_weight_oas16,
+    "hif4_weight": _w_hif4_weight,
     "linear_layer_dual": _w_linear_layer_dual,
     "training_operands": _w_training_operands,
     "dequant": _w_dequant,
