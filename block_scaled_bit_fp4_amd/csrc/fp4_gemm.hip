@@ -38,8 +38,31 @@ struct GemmArgs {
   const uint8_t* bs;  // [N][K/32]
   void* c;
   int64_t M, N, K, ldc;
-  int64_t n_tn;       // column tiles
+  int64_t n_tm, n_tn;  // row and column tiles
+  int xcd;             // place tiles by XCD (see tile_of)
+  int group_m;         // tile rows per raster group
 };
+
+// The C tile of workgroup b.  Workgroups are dealt to the eight XCDs in
+// turn (b mod 8), and each XCD has its own L2.  With xcd set, XCD x takes
+// a contiguous eighth of the tiles (in dispatch order) instead of every
+// eighth tile; within that range tiles run in groups of group_m tile rows,
+// column by column, so that the workgroups an XCD runs together share A
+// rows and B rows in its L2.  A bijection of [0, tiles).
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int64_t b, int64_t& tm, int64_t& tn) {
+  const int64_t tiles = g.n_tm * g.n_tn;
+  int64_t l = b;
+  if (g.xcd) {
+    const int64_t full = tiles - tiles % 8;
+    if (b < full) l = (b % 8) * (full / 8) + b / 8;
+  }
+  const int64_t gsize = (int64_t)g.group_m * g.n_tn;
+  const int64_t grp = l / gsize, first = grp * g.group_m;
+  const int64_t rows = g.n_tm - first < g.group_m ? g.n_tm - first : g.group_m;
+  const int64_t in = l - grp * gsize;
+  tm = first + in % rows;
+  tn = in / rows;
+}
 
 // LDS: two stages of codes (A tile then B tile, 256 rows x 64 bytes each)
 // and two buffers of scales, each holding a group of 16 K steps: the step's
@@ -289,7 +312,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tm = blockIdx.x / g.n_tn, tn = blockIdx.x - tm * g.n_tn;
+  int64_t tm, tn;
+  tile_of(g, blockIdx.x, tm, tn);
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
   const int nk = (int)(g.K / kBK);
   const int64_t rb = g.K / 2, sb = g.K / 32;
@@ -390,7 +414,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
 
 hipError_t fp4_launch_gemm_mx(const GemmLaunch& q, hipStream_t s) {
   const int64_t n_tm = (q.M + kBM - 1) / kBM, n_tn = (q.N + kBN - 1) / kBN;
-  GemmArgs g{q.a_codes, q.a_scales, q.b_codes, q.b_scales, q.c, q.M, q.N, q.K, q.ldc, n_tn};
+  // Tiles by XCD in groups of 8 tile rows: L2 fetches of the linear-layer
+  // GEMMs measured 25-35% lower than in row-major dispatch order, at the
+  // same speed (the kernel is bound by MFMA issue and LDS, not by L2).
+  GemmArgs g{q.a_codes, q.a_scales, q.b_codes, q.b_scales, q.c, q.M, q.N, q.K, q.ldc, n_tm, n_tn,
+             1, 8};
   const int64_t tiles = n_tm * n_tn;
   if (q.c_dtype == 0)
     hipLaunchKernelGGL(gemm_mx_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
