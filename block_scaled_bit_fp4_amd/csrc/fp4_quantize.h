@@ -305,10 +305,16 @@ __device__ __forceinline__ uint32_t encode8_careful(const float* y, float inv,
 // scaled by a power of two, exact (nothing leaves the normal range), so one
 // division serves the sixteen micro-blocks.  The maxima compare in the y
 // domain (t / 4 with the RHT, exact).
-template <bool SR, bool RHT, bool BF16IN, bool PRE>
-__device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, uint32_t k0,
-                                            uint32_t k1, uint64_t n0, uint32_t (&packed)[8],
-                                            uint32_t& sword, const uint32_t* pre) {
+// NS sub-blocks (8 elements each) of a HiF4 block, the block's largest
+// magnitude (before the 1/4 with the RHT) given: the whole block (NS = 8)
+// or one half (NS = 4, sub-blocks s0 .. s0 + 3, when two lanes share a
+// block).  Writes the lane's code words and its part of the scale word:
+// byte 0 and the bits of its own sub-blocks and micro-blocks.
+template <int NS, bool SR, bool RHT, bool BF16IN, bool PRE>
+__device__ __forceinline__ void encode_hif4_part(const float* t, float amax_t, int s0,
+                                                 uint32_t k0, uint32_t k1, uint64_t n0,
+                                                 uint32_t* packed, uint32_t& sword,
+                                                 const uint32_t* pre) {
   constexpr bool kFold = RHT && BF16IN;
   const float amax = RHT ? amax_t * 0.25f : amax_t;
   const uint32_t S = e6m2_encode(amax / 1.75f);
@@ -317,7 +323,7 @@ __device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, 
   const float invD = D != 0.0f ? 1.0f / D : 0.0f;
   uint32_t word = S;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < NS; ++s) {
     float a4[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -326,13 +332,13 @@ __device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, 
       a4[m] = RHT ? mx * 0.25f : mx;
     }
     const bool keep8 = !(fmaxf(a4[0], a4[1]) <= thr);
-    word |= (uint32_t)keep8 << (8 + s);
+    word |= (uint32_t)keep8 << (8 + s0 + s);
     const float thr4 = keep8 ? thr : thr * 0.5f;
     float v[8];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bool keep4 = !(a4[m] <= thr4);
-      word |= (uint32_t)keep4 << (16 + 2 * s + m);
+      word |= (uint32_t)keep4 << (16 + 2 * (s0 + s) + m);
       const float inv = invD * (keep8 ? 4.0f : 8.0f) * (keep4 ? 1.0f : 2.0f);
 #pragma unroll
       for (int l = 0; l < 4; ++l) {
@@ -351,6 +357,25 @@ __device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, 
     packed[s] = encode8_fast<kUFP4, SR>(v, r);
   }
   sword = word;
+}
+
+// One HiF4 block of 64 ([HIF] 2. Metodologia: an E6M2 scale per 64
+// elements, E1M0 scales per 8 and per 4, E1M2 elements).  Reading: the
+// block maximum maps to the top element level 7/4, S = E6M2(amax / 1.75);
+// a sub-block (micro-block) halves its scale when its maximum still fits
+// under the top level after halving: factor 1/2 iff max <= 0.875 * S
+// (times the sub-block's factor); codes k of |y| / d on the uniform grid
+// 0..7 with d = S * f8 * f4 / 4.  Scale word: byte 0 = S, bits 8..15 the
+// sub-block factors, bits 16..31 the micro-block factors (bit set: factor
+// 1; clear: 1/2).  1/d = (1/S) * 4 / (f8 * f4): the binary32 reciprocal
+// scaled by a power of two, exact (nothing leaves the normal range), so one
+// division serves the sixteen micro-blocks.  The maxima compare in the y
+// domain (t / 4 with the RHT, exact).
+template <bool SR, bool RHT, bool BF16IN, bool PRE>
+__device__ __forceinline__ void encode_hif4(const float (&t)[64], float amax_t, uint32_t k0,
+                                            uint32_t k1, uint64_t n0, uint32_t (&packed)[8],
+                                            uint32_t& sword, const uint32_t* pre) {
+  encode_hif4_part<8, SR, RHT, BF16IN, PRE>(t, amax_t, 0, k0, k1, n0, packed, sword, pre);
 }
 
 // Code one block.  t[] holds the rotated values before the 1/4 (RHT) or the
@@ -467,60 +492,88 @@ template <int FMT, bool SR, bool RHT, int TSM, typename T, int U>
 __device__ __forceinline__ void code_row_unit(const RowRaw<T, U>& cur, int64_t row, int64_t minor,
                                               const QuantArgs& a, const ScaleCtx& c,
                                               const float* inv_tab) {
-  constexpr int B = block_of<FMT>();
-  constexpr int NBU = U / B;  // blocks per unit
-  uint32_t packed[U / 8];
-  uint32_t sb[NBU];
-  // widened (and rotated) block bi of the unit, with its largest magnitude
-  auto block_values = [&](int bi, float (&t)[B], float& amax_t) {
-    amax_t = 0.0f;
+  if constexpr (FMT == kHIF4 && U == 32) {
+    // two lanes per HiF4 block (units 2i and 2i + 1 of an A-row sit in
+    // lanes 2j and 2j + 1): the block maximum and the scale word combine by
+    // a lane-pair exchange; the even lane stores the word
+    float t[32], am = 0.0f;
 #pragma unroll
-    for (int h = 0; h < B / 16; ++h) {
+    for (int h = 0; h < 2; ++h) {
       float g[16];
-      cur.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+      cur.template group<RHT>(h, g, a.signs);
       if (RHT) fwht16(g);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         t[16 * h + j] = g[j];
-        amax_t = fmaxf(amax_t, fabsf(g[j]));
+        am = fmaxf(am, fabsf(g[j]));
       }
     }
-  };
-  auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
-    const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * U + bi * B);
-    uint32_t pk[B / 8];
-    encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
-                                                       a.sr_k1, n0, pk, sb[bi]);
-#pragma unroll
-    for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
-  };
-  if constexpr (TSM == kTsOuter) {
-    // kOuter / U consecutive lanes hold one 128-piece of an A-row (the
-    // walk keeps them in step): their maxima combine by lane exchange.
-    constexpr int LPO = kOuter / U;
-    float t[NBU][B], am[NBU];
-    float ao = 0.0f;
-#pragma unroll
-    for (int bi = 0; bi < NBU; ++bi) {
-      block_values(bi, t[bi], am[bi]);
-      ao = fmaxf(ao, am[bi]);
-    }
-    ao = group_max<LPO>(ao);
-    ScaleCtx co;
-    co.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
-    co.den = co.s_t * grid_max<FMT>();
-    if (minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + minor / LPO] = co.s_t;
-#pragma unroll
-    for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
+    am = group_max<2>(am);
+    const int half = (int)(minor & 1);
+    const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * 32);
+    uint32_t pk[4], part;
+    encode_hif4_part<4, SR, RHT, sizeof(T) == 2, false>(t, am, 4 * half, a.sr_k0, a.sr_k1, n0,
+                                                        pk, part, nullptr);
+    const uint32_t word = part | swap_lane_pair(part);
+    store16<true>(a.codes + row * (a.W / 2) + minor * 16, pk[0], pk[1], pk[2], pk[3]);
+    if (!half)
+      *reinterpret_cast<uint32_t*>(a.scales + row * (a.W / 16) + (minor >> 1) * 4) = word;
   } else {
+    constexpr int B = block_of<FMT>();
+    constexpr int NBU = U / B;  // blocks per unit
+    uint32_t packed[U / 8];
+    uint32_t sb[NBU];
+    // widened (and rotated) block bi of the unit, with its largest magnitude
+    auto block_values = [&](int bi, float (&t)[B], float& amax_t) {
+      amax_t = 0.0f;
 #pragma unroll
-    for (int bi = 0; bi < NBU; ++bi) {
-      float t[B], amax_t;
-      block_values(bi, t, amax_t);
-      code(bi, t, amax_t, c);
+      for (int h = 0; h < B / 16; ++h) {
+        float g[16];
+        cur.template group<RHT>(bi * (B / 16) + h, g, a.signs);
+        if (RHT) fwht16(g);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          t[16 * h + j] = g[j];
+          amax_t = fmaxf(amax_t, fabsf(g[j]));
+        }
+      }
+    };
+    auto code = [&](int bi, const float (&t)[B], float amax_t, const ScaleCtx& cc) {
+      const uint64_t n0 = (uint64_t)row * (uint64_t)a.W + (uint64_t)(minor * U + bi * B);
+      uint32_t pk[B / 8];
+      encode_block<FMT, SR, RHT, sizeof(T) == 2, B, TSM>(t, amax_t, cc, inv_tab, a.sr_k0,
+                                                         a.sr_k1, n0, pk, sb[bi]);
+#pragma unroll
+      for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
+    };
+    if constexpr (TSM == kTsOuter) {
+      // kOuter / U consecutive lanes hold one 128-piece of an A-row (the
+      // walk keeps them in step): their maxima combine by lane exchange.
+      constexpr int LPO = kOuter / U;
+      float t[NBU][B], am[NBU];
+      float ao = 0.0f;
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) {
+        block_values(bi, t[bi], am[bi]);
+        ao = fmaxf(ao, am[bi]);
+      }
+      ao = group_max<LPO>(ao);
+      ScaleCtx co;
+      co.s_t = outer_scale<FMT>(RHT ? ao * 0.25f : ao);
+      co.den = co.s_t * grid_max<FMT>();
+      if (minor % LPO == 0) a.ts_out[row * (a.W / kOuter) + minor / LPO] = co.s_t;
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) code(bi, t[bi], am[bi], co);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < NBU; ++bi) {
+        float t[B], amax_t;
+        block_values(bi, t, amax_t);
+        code(bi, t, amax_t, c);
+      }
     }
+    store_row_unit<B, U, scale_bytes<FMT>()>(packed, sb, row, minor, a);
   }
-  store_row_unit<B, U, scale_bytes<FMT>()>(packed, sb, row, minor, a);
 }
 
 // Units: major = A-row, minor = piece of U elements within it.
@@ -1603,8 +1656,8 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   if (q.axis == 0) {
     a.W = q.cols;
     const bool wide = q.cols % 32 == 0;
-    // a HiF4 block (64) is one lane's unit
-    const bool wider = (FP4_ROW_UNIT >= 64 || FMT == kHIF4) && q.cols % 64 == 0;
+    // (HiF4: two lanes of 32 elements per 64-element block)
+    const bool wider = FP4_ROW_UNIT >= 64 && FMT != kHIF4 && q.cols % 64 == 0;
     const int U = wider ? 64 : (wide ? 32 : 16);
     a.n_major = q.rows;
     a.M = q.cols / U;
@@ -1615,7 +1668,9 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
       a.sr = wp.sr;
       hipLaunchKernelGGL(kernel, dim3(wp.grid), dim3(kThreads), 0, s, x, a);
     };
-    if (wider) {
+    if constexpr (FMT == kHIF4) {
+      launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 32>);  // W % 64 == 0
+    } else if (wider) {
       launch(quantize_row_kernel<FMT, SR, RHT, TSM, T, 64>);
     } else if constexpr (B <= 32) {
       if (wide)
