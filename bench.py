@@ -610,7 +610,8 @@ def main():
     args = ap.parse_args()
     if args.traffic_from:
         cmd = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <dir> -o run -- python3 "
-               "bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline --copy-mib %d"
+               "bench.py --workload %s --steps 2 --warmup 1 --no-cpu-baseline --no-cold "
+               "--no-reports --copy-mib %d"
                % (args.workload, args.copy_mib or 256))
         t = traffic_from_counters(args.workload, args.traffic_from[0], args.traffic_from[1],
                                   args.copy_mib or 256,
