@@ -681,14 +681,14 @@ __device__ __forceinline__ float unit_absmax(const RowRaw<T, U>& r, uint32_t sig
 }
 
 // Partial maximum of workgroup j, recomputed from the input by the whole
-// calling workgroup (the value workgroup j posts).
-template <bool RHT, typename T, int U, int NU, int NT>
+// calling workgroup (the value workgroup j posts); nu units per lane.
+template <bool RHT, typename T, int U, int NT>
 __device__ float partial_of(const T* __restrict__ x, const QuantArgs& a, int64_t j,
-                            int64_t stride) {
+                            int64_t stride, int nu) {
   const int64_t units = a.n_major * a.M;
   float m = 0.0f;
-#pragma unroll
-  for (int k = 0; k < NU; ++k) {
+#pragma unroll 1
+  for (int k = 0; k < nu; ++k) {
     const int64_t u = j * NT + threadIdx.x + k * stride;
     if (u < units) {
       const int64_t row = u / a.M, minor = u - row * a.M;
@@ -702,11 +702,12 @@ __device__ float partial_of(const T* __restrict__ x, const QuantArgs& a, int64_t
 }
 
 // Tensor maximum from the posted slots [0, n), waiting up to wait_ticks of
-// the constant-rate clock; slots still missing then are computed here.
-// Block-uniform control flow (partial_of synchronises the workgroup).
-template <bool RHT, typename T, int U, int NU, int NT>
+// the constant-rate clock; slots still missing then are computed here (nu
+// units per lane).  Block-uniform control flow (partial_of synchronises the
+// workgroup).
+template <bool RHT, typename T, int U, int NT>
 __device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxSlot* slots, int n,
-                              uint64_t tag, uint64_t wait_ticks, int64_t stride) {
+                              uint64_t tag, uint64_t wait_ticks, int64_t stride, int nu) {
   constexpr int kPer = (kAmaxPartials + NT - 1) / NT;
   __shared__ int missing[kAmaxPartials];
   __shared__ int nmissing;
@@ -737,8 +738,67 @@ __device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxS
   __syncthreads();
   const int nm = nmissing;
   for (int i = 0; i < nm; ++i)
-    m = fmaxf(m, partial_of<RHT, T, U, NU, NT>(x, a, missing[i], stride));
+    m = fmaxf(m, partial_of<RHT, T, U, NT>(x, a, missing[i], stride, nu));
   return block_max<NT>(m);
+}
+
+// The exchange: this workgroup's partial maximum m (before the 1/4 with the
+// RHT) is posted in its slot; workgroup 0 gathers the slots and posts the
+// tensor maximum in the result slot, and the others wait for it.  nu units
+// per lane, for the recomputation of partial maxima that never arrive.
+//
+// Waits: workgroup 0 waits wait_ticks for every slot, then computes the
+// missing partial maxima itself and posts the tensor maximum; the other
+// workgroups wait up to long_ticks (longer) for that result, so that in the
+// normal course only workgroup 0 recomputes anything, and compute what they
+// miss themselves only if it never comes (workgroup 0 not resident).
+template <bool RHT, typename T, int U, int NT>
+__device__ float exchange_amax(const T* __restrict__ x, const QuantArgs& a, AmaxSlot* slots,
+                               uint64_t tag, float m, uint64_t wait_ticks, uint64_t long_ticks,
+                               int64_t stride, int nu) {
+  __shared__ float shared_amax;
+  __shared__ int shared_have;
+  m = block_max<NT>(m);
+  if (threadIdx.x == 0) post_slot(slots + blockIdx.x, RHT ? m * 0.25f : m, tag);
+  AmaxSlot* result = slots + kAmaxPartials;
+  float amax;
+  if (blockIdx.x == 0) {
+    amax = gather_slots<RHT, T, U, NT>(x, a, slots, gridDim.x, tag, wait_ticks, stride, nu);
+    if (threadIdx.x == 0) post_slot(result, amax, tag);
+  } else {
+    if (threadIdx.x == 0) {
+      const uint64_t t0 = wall_clock64();
+      float v = 0.0f;
+      bool ok;
+      while (!(ok = read_slot(result, tag, v)) && wall_clock64() - t0 < long_ticks)
+        __builtin_amdgcn_s_sleep(2);
+      shared_amax = v;
+      shared_have = ok;
+    }
+    __syncthreads();
+    amax = shared_amax;
+    if (!shared_have)  // workgroup 0 never posted: take what is posted, compute the rest
+      amax = gather_slots<RHT, T, U, NT>(x, a, slots, gridDim.x, tag, 0, stride, nu);
+  }
+  return amax;
+}
+
+// The two-level scale from the tensor maximum, as in scale_prologue: s_t,
+// written once by the grid's first lane, and the reciprocal step table.
+template <int FMT>
+__device__ __forceinline__ ScaleCtx scale_from_amax(float amax, const QuantArgs& a,
+                                                    float* inv_tab) {
+  ScaleCtx c;
+  c.s_t = amax / (grid_max<FMT>() * 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
+  c.den = c.s_t * grid_max<FMT>();
+  if (threadIdx.x < 128) {
+    const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
+    const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
+    inv_tab[threadIdx.x] = d != 0.0f ? 1.0f / d : 0.0f;
+  }
+  __syncthreads();
+  return c;
 }
 
 // NT lanes per workgroup, NU units of U elements per lane.  With stochastic
@@ -747,12 +807,7 @@ __device__ float gather_slots(const T* __restrict__ x, const QuantArgs& a, AmaxS
 // work then runs while the loads are in flight instead of after the
 // exchange.  Layout [group of 8 elements][lane], 16 bytes per entry, so the
 // writes and reads of a wave are contiguous.
-//
-// Waits: workgroup 0 waits wait_ticks for every slot, then computes the
-// missing partial maxima itself and posts the tensor maximum; the other
-// workgroups wait up to long_ticks (longer) for that result, so that in the
-// normal course only workgroup 0 recomputes anything, and compute what they
-// miss themselves only if it never comes (workgroup 0 not resident).
+// The exchange and its waits: exchange_amax.
 template <int FMT, bool SR, bool RHT, typename T, int U, int NU, int NT>
 __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
     const T* __restrict__ x, QuantArgs a, AmaxSlot* slots, uint64_t tag, uint64_t wait_ticks,
@@ -762,8 +817,6 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
   constexpr int GPU = U / 8;  // Philox groups (8 elements each) per unit
   extern __shared__ uint4 draws[];
   __shared__ float inv_tab[128];
-  __shared__ float shared_amax;
-  __shared__ int shared_have;
   const int64_t units = a.n_major * a.M;
   const int64_t stride = (int64_t)gridDim.x * NT;
   const int64_t u0 = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -824,29 +877,8 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
   for (int k = 0; k < NU; ++k)
 #pragma unroll
     for (int bi = 0; bi < NBU; ++bi) m = fmaxf(m, bam[k][bi]);  // 0 past the last unit
-  m = block_max<NT>(m);
-  if (threadIdx.x == 0) post_slot(slots + blockIdx.x, RHT ? m * 0.25f : m, tag);
-
-  AmaxSlot* result = slots + kAmaxPartials;
-  float amax;
-  if (blockIdx.x == 0) {
-    amax = gather_slots<RHT, T, U, NU, NT>(x, a, slots, gridDim.x, tag, wait_ticks, stride);
-    if (threadIdx.x == 0) post_slot(result, amax, tag);
-  } else {
-    if (threadIdx.x == 0) {
-      const uint64_t t0 = wall_clock64();
-      float v = 0.0f;
-      bool ok;
-      while (!(ok = read_slot(result, tag, v)) && wall_clock64() - t0 < long_ticks)
-        __builtin_amdgcn_s_sleep(2);
-      shared_amax = v;
-      shared_have = ok;
-    }
-    __syncthreads();
-    amax = shared_amax;
-    if (!shared_have)  // workgroup 0 never posted: take what is posted, compute the rest
-      amax = gather_slots<RHT, T, U, NU, NT>(x, a, slots, gridDim.x, tag, 0, stride);
-  }
+  const float amax = exchange_amax<RHT, T, U, NT>(x, a, slots, tag, m, wait_ticks, long_ticks,
+                                                   stride, NU);
 
   if constexpr (!RHT) {
     // opaque to the compiler, so that it widens the raw words again below
@@ -859,17 +891,7 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
                      "+v"(raw[k].q[i].w));
   }
 
-  // the two-level scale from the tensor maximum, as in scale_prologue
-  ScaleCtx c;
-  c.s_t = amax / (grid_max<FMT>() * 448.0f);
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
-  c.den = c.s_t * grid_max<FMT>();
-  if (threadIdx.x < 128) {
-    const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
-    const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
-    inv_tab[threadIdx.x] = d != 0.0f ? 1.0f / d : 0.0f;
-  }
-  __syncthreads();
+  const ScaleCtx c = scale_from_amax<FMT>(amax, a, inv_tab);
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
     const int64_t u = u0 + k * stride;
@@ -908,6 +930,119 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
         for (int q = 0; q < B / 8; ++q) packed[bi * (B / 8) + q] = pk[q];
       }
       store_row_unit<B, U>(packed, sb, row, minor, a);
+    }
+  }
+}
+
+
+// ----------------------------------------- row axis, wide single pass
+// Two-level formats with a computed tensor scale, contiguous BF16 operands
+// too large for the registers of one resident grid: one workgroup of NT
+// lanes per compute unit.  Units of a lane: u0 + k * stride, k = 0 .. nu - 1
+// (unit u: elements [32u, 32u + 32) of the operand, rows back to back);
+// the first NR stay raw in registers, the next NL raw in LDS, the rest are
+// streamed.  Pass 1 reads every unit once and rotates it for the partial
+// maximum, keeping the held units; after the exchange the lanes code the
+// held units (rotated again from the raw words) and read the streamed ones
+// a second time.  Only the streamed share of the input is read twice,
+// where the two-pass path reads all of it twice; the second rotation is
+// vector work that overlaps the streamed reads and the stores.
+// LDS layout [slot][16-byte piece][lane]: the writes and reads of one piece
+// by a wave are contiguous.
+template <int FMT, bool SR, bool RHT, typename T, int U, int NR, int NL, int NT>
+__global__ __launch_bounds__(NT) void quantize_row_wide_kernel(
+    const T* __restrict__ x, QuantArgs a, AmaxSlot* slots, uint64_t tag, uint64_t wait_ticks,
+    uint64_t long_ticks, int nu) {
+  using Raw = RowRaw<T, U>;
+  constexpr int KV = Raw::kVec;
+  extern __shared__ uint4 held[];
+  __shared__ float inv_tab[128];
+  const int64_t units = a.n_major * a.M;
+  const int64_t stride = (int64_t)gridDim.x * NT;
+  const int64_t u0 = (int64_t)blockIdx.x * NT + threadIdx.x;
+  auto unit = [&](int k) { return u0 + (int64_t)k * stride; };
+  auto load = [&](int k, Raw& r) {
+    if (unit(k) < units) {
+      r.load(x + unit(k) * U);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KV; ++i) r.q[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto lds_at = [&](int slot, int i) -> uint4& { return held[(slot * KV + i) * NT + threadIdx.x]; };
+
+  // ---- pass 1: every unit read once.  The held units' loads are issued
+  // first; each of the next NR loads is in flight while a held unit is
+  // rotated, and the rest stream one at a time.
+  Raw raw[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) load(k, raw[k]);
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int k = NR + j;
+    Raw cur;
+    if (k < nu) load(k, cur);
+    m = fmaxf(m, unit_absmax<RHT, T, U>(raw[j], a.signs));  // 0 past the last unit
+    if (k < nu) {
+      m = fmaxf(m, unit_absmax<RHT, T, U>(cur, a.signs));
+      if (j < NL) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) lds_at(j, i) = cur.q[i];
+      }
+    }
+  }
+#pragma unroll 1
+  for (int k = 2 * NR; k < nu; ++k) {
+    Raw cur;
+    load(k, cur);
+    m = fmaxf(m, unit_absmax<RHT, T, U>(cur, a.signs));
+  }
+
+  const float amax = exchange_amax<RHT, T, U, NT>(x, a, slots, tag, m, wait_ticks, long_ticks,
+                                                   stride, nu);
+  // opaque to the compiler, so that the held words are rotated again below
+  // instead of the first rotation being kept alive across the exchange
+#pragma unroll
+  for (int k = 0; k < NR; ++k)
+#pragma unroll
+    for (int i = 0; i < KV; ++i)
+      asm volatile("" : "+v"(raw[k].q[i].x), "+v"(raw[k].q[i].y), "+v"(raw[k].q[i].z),
+                   "+v"(raw[k].q[i].w));
+  const ScaleCtx c = scale_from_amax<FMT>(amax, a, inv_tab);
+
+  // ---- pass 2: held units, then the streamed ones read again (the first
+  // two streamed loads are issued as soon as registers free up).  With
+  // the rows back to back, (row 0, piece u) addresses unit u.
+  const int ns = nu - NR - NL;
+  auto code = [&](int k, const Raw& r) {
+    if (unit(k) < units)
+      code_row_unit<FMT, SR, RHT, kTsCompute, T, U>(r, 0, unit(k), a, c, inv_tab);
+  };
+  Raw sa, sb;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    code(k, raw[k]);
+    if (k == NR - 1 && ns > 0) load(NR + NL, sa);
+  }
+#pragma unroll
+  for (int l = 0; l < NL; ++l) {
+    if (NR + l < nu) {
+      Raw r;
+#pragma unroll
+      for (int i = 0; i < KV; ++i) r.q[i] = lds_at(l, i);
+      code(NR + l, r);
+    }
+    if (l == 0 && ns > 1) load(NR + NL + 1, sb);
+  }
+#pragma unroll 1
+  for (int j = 0; j < ns; j += 2) {
+    const int k = NR + NL + j;
+    code(k, sa);
+    if (j + 2 < ns) load(k + 2, sa);
+    if (j + 1 < ns) {
+      code(k + 1, sb);
+      if (j + 3 < ns) load(k + 3, sb);
     }
   }
 }
@@ -1570,6 +1705,9 @@ uint64_t wall_ticks_per_us() {
 #ifndef FP4_SINGLE_PASS
 #define FP4_SINGLE_PASS 1
 #endif
+#ifndef FP4_WIDE_PASS
+#define FP4_WIDE_PASS 1
+#endif
 
 // Dynamic LDS of the single-pass kernel: the SR draws of every lane.
 template <bool SR, int U, int NU, int NT>
@@ -1629,6 +1767,39 @@ bool try_single_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   return true;
 }
 
+// The wide single pass (contiguous BF16 row operands past the single
+// pass's reach): one workgroup of 1024 lanes per compute unit, NR units
+// held in registers and NL in LDS per lane.  False when one such workgroup per
+// compute unit is not resident at once; nothing is launched then.
+template <int FMT, bool SR, bool RHT, typename T>
+bool try_wide_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return false;
+  } else {
+  constexpr int U = 32, NR = RHT ? 3 : 4, NL = 2, NT = 1024;
+  static_assert(NL <= NR, "LDS units are taken with the held ones");
+  auto kernel = quantize_row_wide_kernel<FMT, SR, RHT, T, U, NR, NL, NT>;
+  constexpr size_t lds = (size_t)NL * RowRaw<T, U>::kVec * 16 * NT;
+  const int64_t units = q.rows * (q.cols / U);
+  if (q.ld != q.cols) return false;
+  const int64_t grid = resident_wgs_nt(reinterpret_cast<const void*>(kernel), NT, lds);
+  if (grid < 1 || grid > kAmaxPartials) return false;
+  const int64_t stride = grid * NT;
+  const int64_t nu = (units + stride - 1) / stride;
+  if (nu > (int64_t)1 << 30) return false;
+  a.W = q.cols;
+  a.n_major = q.rows;
+  a.M = q.cols / U;
+  AmaxSlot* slots = reinterpret_cast<AmaxSlot*>(q.workspace);
+  const uint64_t per_us = wall_ticks_per_us();
+  const uint64_t ticks = (uint64_t)q.wait_us * per_us;
+  const uint64_t long_ticks = 4 * ticks + 64 * per_us;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), lds, s, static_cast<const T*>(q.x), a,
+                     slots, q.call_tag, ticks, long_ticks, (int)nu);
+  return true;
+  }
+}
+
 template <int FMT, bool SR, bool RHT, int TSM, typename T>
 hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
   constexpr int B = block_of<FMT>();
@@ -1649,7 +1820,8 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
         q.ws_bytes >= kSinglePassWsBytes &&
         (try_single_pass<FMT, SR, RHT, T, 1, 1024>(q, a, s) ||
          (sizeof(T) == 2 && try_single_pass<FMT, SR, RHT, T, 2, 1024>(q, a, s)) ||
-         try_single_pass<FMT, SR, RHT, T, 4, 256>(q, a, s)))
+         try_single_pass<FMT, SR, RHT, T, 4, 256>(q, a, s) ||
+         (FP4_WIDE_PASS && try_wide_pass<FMT, SR, RHT, T>(q, a, s))))
       return hipGetLastError();
   }
   if constexpr (has_tensor_scale(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
