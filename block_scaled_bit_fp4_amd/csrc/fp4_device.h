@@ -202,6 +202,26 @@ __device__ __forceinline__ uint32_t e4m3_encode(float r) {
   return r < 448.0f ? s : 0x7Eu;
 }
 
+// e4m3_encode(r) of the binary32 quotient r = a / den, given rden, the
+// binary32 reciprocal of den (0 when it is not a normal number).  The
+// product q = a * rden is within 2.5 units in the last place of r (two
+// roundings of relative size 2^-24 each, against r's half unit), so where
+// no rounding midpoint of the E4M3 grid lies within 4 binary32 patterns of
+// q, and q is in the normal E4M3 range, q and r round to the same code
+// (r is then no midpoint either, so no tie is decided differently); the
+// midpoints there are the patterns with low 20 bits 0x80000.  Elsewhere
+// (rare: near a midpoint, subnormal E4M3 codes, saturation, non-finite
+// values) the quotient is divided out.  The result is e4m3_encode(a / den)
+// in every case; one multiply replaces a correctly rounded division.
+__device__ __forceinline__ uint32_t e4m3_encode_quotient(float a, float den, float rden) {
+  const float q = a * rden;
+  const uint32_t b = __float_as_uint(q);
+  const bool near = ((b & 0xFFFFFu) - 0x7FFFCu) <= 8u;
+  if (q >= 0x1.0001p-6f && q < 448.0f && !near)
+    return ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  return e4m3_encode(a / den);
+}
+
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = c >> 3, m = c & 7u;
   const float sub = (float)m * 0.001953125f;  // m * 2^-9

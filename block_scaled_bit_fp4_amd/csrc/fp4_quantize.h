@@ -108,10 +108,17 @@ struct QuantArgs {
   uint32_t sr_k0, sr_k1;
 };
 
-// Per-workgroup constants of the two-level scale.
+// Per-workgroup constants of the two-level scale: s_t, den = s_t * G, and
+// rden, den's binary32 reciprocal for the block-scale selection (0: not
+// set, or den's reciprocal not a normal number; the quotient is then
+// always divided out).  Outer scales (one per 128-piece) leave rden unused.
 struct ScaleCtx {
-  float s_t, den;
+  float s_t, den, rden;
 };
+
+__device__ __forceinline__ float recip_of_den(float den) {
+  return (den >= 0x1p-125f && den <= 0x1p125f) ? 1.0f / den : 0.0f;
+}
 
 // Tensor-scale inputs of a workgroup: the amax partial maxima (4 per lane)
 // or the given scale.  Fetched before the lane's first data loads: loads
@@ -156,7 +163,7 @@ __device__ __forceinline__ ScaleFetch scale_fetch(const float* partials, int npa
 template <int FMT, int TSM>
 __device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* ts_out,
                                                    float* inv_tab) {
-  ScaleCtx c{0.0f, 0.0f};
+  ScaleCtx c{0.0f, 0.0f, 0.0f};
   if constexpr (has_tensor_scale(FMT) && TSM != kTsOuter) {
     if (TSM == kTsGiven) {
       c.s_t = f.v[0];
@@ -169,6 +176,7 @@ __device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* t
       if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[0] = c.s_t;
     }
     c.den = c.s_t * grid_max<FMT>();
+    c.rden = recip_of_den(c.den);
     if (threadIdx.x < 128) {
       const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
       const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
@@ -415,7 +423,11 @@ __device__ __forceinline__ void encode_block(const float (&t)[B], float amax_t, 
     const float d = __builtin_ldexpf(c.s_t, e);
     inv = d != 0.0f ? 1.0f / d : 0.0f;
   } else {
-    sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
+    if constexpr (TSM == kTsOuter)
+      sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode(amax_b / c.den) : 0u;
+    else
+      sbyte = (c.s_t != 0.0f && amax_b != 0.0f) ? e4m3_encode_quotient(amax_b, c.den, c.rden)
+                                                : 0u;
     if constexpr (TSM == kTsOuter) {
       const float d = sbyte ? c.s_t * e4m3_decode(sbyte) : 0.0f;
       inv = d != 0.0f ? 1.0f / d : 0.0f;
@@ -792,6 +804,7 @@ __device__ __forceinline__ ScaleCtx scale_from_amax(float amax, const QuantArgs&
   c.s_t = amax / (grid_max<FMT>() * 448.0f);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.ts_out[0] = c.s_t;
   c.den = c.s_t * grid_max<FMT>();
+  c.rden = recip_of_den(c.den);
   if (threadIdx.x < 128) {
     const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
     const float d = S ? c.s_t * e4m3_decode(S) : 0.0f;
@@ -1408,6 +1421,8 @@ __device__ __forceinline__ void dual_prologue(const DualArgs& a, const ScaleFetc
     }
     cr.den = cr.s_t * grid_max<FMT>();
     cc.den = cc.s_t * grid_max<FMT>();
+    cr.rden = recip_of_den(cr.den);
+    cc.rden = recip_of_den(cc.den);
     if (threadIdx.x < 128) {
       const uint32_t S = threadIdx.x < 127 ? threadIdx.x : 126u;
       const float dr = S ? cr.s_t * e4m3_decode(S) : 0.0f;
