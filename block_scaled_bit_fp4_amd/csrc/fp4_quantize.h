@@ -187,16 +187,39 @@ __device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* t
   return c;
 }
 
-// Elements 2j and 2j + 1 of v, stochastically rounded in hardware with the
-// draws of Philox word w (element 2j its low half, 2j + 1 its high half).
-// Both converts take the pair (odd element first); the first uses the odd
-// element's draw and keeps its code in the low nibble, the second the even
-// element's draw and keeps its code in the high nibble.  Only byte 0 of each
-// result is defined (the compiler does not carry the convert's other
-// destination bytes through); the caller gathers and swaps the nibbles.
+// Stochastic E2M1 conversion of one pair into byte J of `word`, the other
+// bytes kept.  The convert writes only the byte its selector names; the
+// compiler's builtin does not carry the other bytes of its first operand
+// through to the result, so the instruction is written out with `word` as
+// an input-output operand (byte 0, converted first, starts the word: its
+// other bytes are written by the next three).  Pair order (odd element,
+// even element); scale operand 1.0 (no rescaling).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int J>
+__device__ __forceinline__ void cvt_sr_pk_fp4_byte(uint32_t& word, f32x2 p, uint32_t rnd) {
+  if constexpr (J == 0)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(word) : "v"(p), "v"(rnd));
+  else if constexpr (J == 1)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]"
+        : "+v"(word) : "v"(p), "v"(rnd));
+  else if constexpr (J == 2)
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]"
+        : "+v"(word) : "v"(p), "v"(rnd));
+  else
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]"
+        : "+v"(word) : "v"(p), "v"(rnd));
+}
+
+// Elements 2J and 2J + 1 of a group of 8, stochastically rounded in
+// hardware with the draws of Philox word w (element 2J its low half, 2J + 1
+// its high half), into byte J of `odd` and of `even`.  Both converts take
+// the pair (odd element first); the first uses the odd element's draw and
+// keeps its code in the low nibble of its byte, the second the even
+// element's draw and keeps its code in the high nibble; the caller swaps
+// the nibbles into place.
+template <int J>
 __device__ __forceinline__ void sr_pair_e2m1(float ve, float vo, uint32_t w, uint32_t& odd,
                                              uint32_t& even) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
   // first slot, bits 31..10: ~(high half) then six ones = ~w | 0xFFFF
   // (three-input op, truth table 0xCF = ~a | b)
   const uint32_t r0 = __builtin_amdgcn_bitop3_b32(w, 0xFFFFu, 0u, 0xCF);
@@ -206,17 +229,11 @@ __device__ __forceinline__ void sr_pair_e2m1(float ve, float vo, uint32_t w, uin
   // shift and a not
   uint32_t r1;
   asm("v_mad_i32_i24 %0, %1, %2, -1" : "=v"(r1) : "v"(w), "s"(-32768));
-  f2 p;
+  f32x2 p;
   p.x = vo;
   p.y = ve;
-  odd = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r0, 1.0f, 0);
-  even = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r1, 1.0f, 0);
-}
-
-// Bytes 0 of a, b, c, d as one word (selector 0x0C gives a zero byte).
-__device__ __forceinline__ uint32_t gather_low_bytes(uint32_t a, uint32_t b, uint32_t c,
-                                                     uint32_t d) {
-  return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+  cvt_sr_pk_fp4_byte<J>(odd, p, r0);
+  cvt_sr_pk_fp4_byte<J>(even, p, r1);
 }
 
 // Encode 8 scaled values (all finite) into one word of 4-bit codes.
@@ -261,11 +278,11 @@ __device__ __forceinline__ uint32_t encode8_fast(const float* v_in, const uint32
     // element's draw, and each element's nibble is taken from its convert.
     // The pair enters odd element first: each slot then takes its draw from
     // w in one instruction (above), and the nibbles swap back in the merge.
-    uint32_t od[4], ev[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sr_pair_e2m1(v[2 * j], v[2 * j + 1], r[j], od[j], ev[j]);
-    const uint32_t wo = gather_low_bytes(od[0], od[1], od[2], od[3]);  // odd codes, low nibbles
-    const uint32_t we = gather_low_bytes(ev[0], ev[1], ev[2], ev[3]);  // even codes, high nibbles
+    uint32_t wo, we;  // odd codes in low nibbles, even codes in high nibbles
+    sr_pair_e2m1<0>(v[0], v[1], r[0], wo, we);
+    sr_pair_e2m1<1>(v[2], v[3], r[1], wo, we);
+    sr_pair_e2m1<2>(v[4], v[5], r[2], wo, we);
+    sr_pair_e2m1<3>(v[6], v[7], r[3], wo, we);
     word = ((we >> 4) & 0x0F0F0F0Fu) | ((wo << 4) & 0xF0F0F0F0u);
   } else {
 #pragma unroll
@@ -836,24 +853,30 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
   // Everything that does not depend on the tensor scale is done before the
   // exchange: the units' widened (and rotated) values and their block
   // maxima stay in registers for the coding after it.
+  // A lane's units past the last one load a copy of the last unit (its
+  // values are in the operand, so the partial maximum is unchanged, and
+  // nothing is stored for them): every load is unconditional, so none
+  // waits for the one before (a zero fill on the other side of a branch
+  // would rewrite the load's registers, and the load would be waited for
+  // first).  Rows back to back (ld = W): unit u starts at element 32u, no
+  // division.
   RowRaw<T, U> raw[NU];
-  int64_t rowk[NU], minork[NU];
+  const bool dense = a.ld == a.W;
 #pragma unroll
   for (int k = 0; k < NU; ++k) {
     const int64_t u = u0 + k * stride;
-    rowk[k] = u / a.M;
-    minork[k] = u - rowk[k] * a.M;
-    if (u < units) {
-      raw[k].load(x + rowk[k] * a.ld + minork[k] * U);
+    const int64_t uc = u < units ? u : units - 1;
+    if (dense) {
+      raw[k].load(x + uc * U);
     } else {
-#pragma unroll
-      for (int i = 0; i < RowRaw<T, U>::kVec; ++i) raw[k].q[i] = make_uint4(0u, 0u, 0u, 0u);
+      const int64_t row = uc / a.M;
+      raw[k].load(x + row * a.ld + (uc - row * a.M) * U);
     }
   }
   if constexpr (SR) {
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
-      const uint64_t g0 = ((uint64_t)rowk[k] * (uint64_t)a.W + (uint64_t)(minork[k] * U)) >> 3;
+      const uint64_t g0 = ((uint64_t)(u0 + k * stride) * (uint64_t)U) >> 3;
 #pragma unroll
       for (int q = 0; q < GPU; ++q) {
         const uint64_t g = g0 + (uint64_t)q;
@@ -889,7 +912,7 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
 #pragma unroll
   for (int k = 0; k < NU; ++k)
 #pragma unroll
-    for (int bi = 0; bi < NBU; ++bi) m = fmaxf(m, bam[k][bi]);  // 0 past the last unit
+    for (int bi = 0; bi < NBU; ++bi) m = fmaxf(m, bam[k][bi]);
   const float amax = exchange_amax<RHT, T, U, NT>(x, a, slots, tag, m, wait_ticks, long_ticks,
                                                    stride, NU);
 
@@ -909,7 +932,8 @@ __global__ __launch_bounds__(NT) void quantize_row_single_kernel(
   for (int k = 0; k < NU; ++k) {
     const int64_t u = u0 + k * stride;
     if (u < units) {
-      const int64_t row = rowk[k], minor = minork[k];
+      // rows back to back in the outputs: (row 0, piece u) is unit u
+      const int64_t row = 0, minor = u;
       uint32_t packed[U / 8];
       uint32_t sb[NBU];
 #pragma unroll
@@ -974,14 +998,12 @@ __global__ __launch_bounds__(NT) void quantize_row_wide_kernel(
   const int64_t stride = (int64_t)gridDim.x * NT;
   const int64_t u0 = (int64_t)blockIdx.x * NT + threadIdx.x;
   auto unit = [&](int k) { return u0 + (int64_t)k * stride; };
-  auto load = [&](int k, Raw& r) {
-    if (unit(k) < units) {
-      r.load(x + unit(k) * U);
-    } else {
-#pragma unroll
-      for (int i = 0; i < KV; ++i) r.q[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
+  // Past the last unit a lane loads a copy of the last unit: the partial
+  // maximum is unchanged and nothing is stored for it.  The loads are
+  // unconditional, so none is waited for before the next is issued (a
+  // zero fill on the other side of a branch would rewrite the registers of
+  // a load in flight and force a wait on it).
+  auto load = [&](int k, Raw& r) { r.load(x + (unit(k) < units ? unit(k) : units - 1) * U); };
   auto lds_at = [&](int slot, int i) -> uint4& { return held[(slot * KV + i) * NT + threadIdx.x]; };
 
   // ---- pass 1: every unit read once.  The held units' loads are issued
@@ -996,7 +1018,7 @@ __global__ __launch_bounds__(NT) void quantize_row_wide_kernel(
     const int k = NR + j;
     Raw cur;
     if (k < nu) load(k, cur);
-    m = fmaxf(m, unit_absmax<RHT, T, U>(raw[j], a.signs));  // 0 past the last unit
+    m = fmaxf(m, unit_absmax<RHT, T, U>(raw[j], a.signs));
     if (k < nu) {
       m = fmaxf(m, unit_absmax<RHT, T, U>(cur, a.signs));
       if (j < NL) {
@@ -1785,7 +1807,8 @@ bool try_single_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
 // The wide single pass (contiguous BF16 row operands past the single
 // pass's reach): one workgroup of 1024 lanes per compute unit, NR units
 // held in registers and NL in LDS per lane.  False when one such workgroup per
-// compute unit is not resident at once; nothing is launched then.
+// compute unit is not resident at once, or when fewer than half of a lane's
+// units would be held; nothing is launched then.
 template <int FMT, bool SR, bool RHT, typename T>
 bool try_wide_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   if constexpr (sizeof(T) != 2) {
@@ -1801,7 +1824,12 @@ bool try_wide_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   if (grid < 1 || grid > kAmaxPartials) return false;
   const int64_t stride = grid * NT;
   const int64_t nu = (units + stride - 1) / stride;
-  if (nu > (int64_t)1 << 30) return false;
+  // Only while at least half of a lane's units are held: past that the
+  // second pass reads nearly all of the operand again anyway, and the two
+  // kernels of the two-pass path, each with its loads spread over four
+  // workgroups per compute unit, stream it faster (measured on an
+  // 8192 x 28672 operand, 28 units per lane: 190 us wide, 173 us two-pass).
+  if (nu > 2 * (NR + NL)) return false;
   a.W = q.cols;
   a.n_major = q.rows;
   a.M = q.cols / U;

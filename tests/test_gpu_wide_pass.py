@@ -34,12 +34,15 @@ def _bf16(shape, seed, kind="normal"):
 
 
 # With 256 workgroups of 1024 lanes (one per compute unit) a lane takes
-# ceil(units / 262144) units of 32 elements:
-#   (4104, 4128): 3 units per lane (the held ones only, LDS slots unused
-#     with the RHT, partly used without);
-#   (4096, 8192): 4 per lane; (8192, 8192): 8 per lane (3 streamed with the
+# ceil(units / 262144) units of 32 elements; with the RHT it holds 3 in
+# registers and 2 in LDS, without it 4 and 2:
+#   (4104, 4128): 3 units per lane (the held ones only, LDS slots unused);
+#   (4096, 8192): 4 per lane; (6144, 8192): 6 per lane (with the RHT one
+#     unit streamed, read in the held-unit loop of the first pass);
+#   (7168, 8192): 7 per lane; (8192, 8192): 8 per lane (3 streamed with the
 #     RHT, 2 without); (8256, 8224): 9 per lane, the last round ragged.
-WIDE_SHAPES = [(4104, 4128), (4096, 8192), (8192, 8192), (8256, 8224)]
+WIDE_SHAPES = [(4104, 4128), (4096, 8192), (6144, 8192), (7168, 8192), (8192, 8192),
+               (8256, 8224)]
 
 
 @pytest.mark.parametrize("shape", WIDE_SHAPES)
@@ -66,7 +69,7 @@ def test_wide_pass_max_in_every_share():
     shape = (8192, 8192)
     base = _bf16(shape, 901)
     stride_units = 256 * 1024
-    for k in (0, 2, 3, 4, 7):  # held (k < 3), LDS (3, 4), streamed (k >= 5), with the RHT
+    for k in (0, 2, 3, 4, 5, 6, 7):  # held (k < 3), LDS (3, 4), streamed (k >= 5), RHT
         x = base.copy()
         u = k * stride_units + 5
         x.reshape(-1)[32 * u + 17] = workloads.to_bf16_bits(np.array([[2.0 ** 20]],
