@@ -193,20 +193,25 @@ __device__ __forceinline__ ScaleCtx scale_prologue(const ScaleFetch& f, float* t
 // through to the result, so the instruction is written out with `word` as
 // an input-output operand (byte 0, converted first, starts the word: its
 // other bytes are written by the next three).  Pair order (odd element,
-// even element); scale operand 1.0 (no rescaling).
+// even element); scale operand 1.0 (no rescaling).  Wait states, which the
+// compiler does not add around inline assembly: one before each convert,
+// which reads the word (or the draw register it may share) the previous
+// instruction may have just written (the compiler puts one between two such
+// converts of its own), and two after the last one, before other
+// instructions read the word.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int J>
 __device__ __forceinline__ void cvt_sr_pk_fp4_byte(uint32_t& word, f32x2 p, uint32_t rnd) {
   if constexpr (J == 0)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(word) : "v"(p), "v"(rnd));
+    asm("s_nop 0\n\tv_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "=v"(word) : "v"(p), "v"(rnd));
   else if constexpr (J == 1)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]"
+    asm("s_nop 0\n\tv_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]"
         : "+v"(word) : "v"(p), "v"(rnd));
   else if constexpr (J == 2)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]"
+    asm("s_nop 0\n\tv_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]"
         : "+v"(word) : "v"(p), "v"(rnd));
   else
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]"
+    asm("s_nop 0\n\tv_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]\n\ts_nop 1"
         : "+v"(word) : "v"(p), "v"(rnd));
 }
 
