@@ -136,3 +136,25 @@ def test_single_pass_beside_a_busy_stream(monkeypatch, rounding, wait_us):
     assert_bytes_equal(to_host(s), osc, "scales beside a busy stream")
     assert_bytes_equal(to_host(c), oc, "codes beside a busy stream")
     assert call_ms < busy_ms + 20.0
+
+
+# Strided views (row pitch above the width): unit u is then not element 32u
+# of the buffer, and the kernel divides by the units per row; one and two
+# units per lane, and a ragged last workgroup.
+@pytest.mark.parametrize("shape,pitch", [((1056, 352), 384), ((2048, 4096), 4160),
+                                         ((4096, 4096), 4128)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_single_pass_strided_rows(shape, pitch, rounding):
+    full = _bf16((shape[0], pitch), 500 + shape[0] % 89, "outlier_cols")
+    x = np.ascontiguousarray(full[:, :shape[1]])
+    note("single pass strided %s pitch %d %s" % (shape, pitch, rounding))
+    xd = to_device(full)[:, :shape[1]]
+    two = torch.empty(TWO_PASS_WS, dtype=torch.uint8, device=DEV)
+    a = _run(xd, "nvfp4", rounding, True, None)
+    b = _run(xd, "nvfp4", rounding, True, two)
+    oc, osc, ots = oracle.quantize(x, "nvfp4", "row", rounding, True, 7, 11)
+    assert a[2] == f32_bits(ots)
+    assert_bytes_equal(a[1], osc, "scales strided single pass")
+    assert_bytes_equal(a[0], oc, "codes strided single pass")
+    assert_bytes_equal(a[0], b[0], "codes single vs two-pass")
+    assert a[2] == b[2]
