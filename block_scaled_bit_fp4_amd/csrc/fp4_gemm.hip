@@ -414,11 +414,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
 
 hipError_t fp4_launch_gemm_mx(const GemmLaunch& q, hipStream_t s) {
   const int64_t n_tm = (q.M + kBM - 1) / kBM, n_tn = (q.N + kBN - 1) / kBN;
-  // Tiles by XCD in groups of 8 tile rows: L2 fetches of the linear-layer
-  // GEMMs measured 25-35% lower than in row-major dispatch order, at the
-  // same speed (the kernel is bound by MFMA issue and LDS, not by L2).
+  // Tiles by XCD in groups of 4 tile rows: L2 fetches of the linear-layer
+  // GEMMs measured 25-35% lower than in row-major dispatch order.  Groups of
+  // 1, 2, 4, 8, 16 and 32 tile rows, and no XCD placement, measured side by
+  // side: 4 is fastest (forward GEMM 561 us against 585 with 8, 627 with
+  // 32, 588 without placement).
   GemmArgs g{q.a_codes, q.a_scales, q.b_codes, q.b_scales, q.c, q.M, q.N, q.K, q.ldc, n_tm, n_tn,
-             1, 8};
+             1, 4};
   const int64_t tiles = n_tm * n_tn;
   if (q.c_dtype == 0)
     hipLaunchKernelGGL(gemm_mx_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
