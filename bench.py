@@ -779,7 +779,8 @@ def main():
             dom, call_label(c), "fp4_rht" if c.op == "rht" else "fp4_dequantize"
             if c.op == "dequantize" else "fp4_quantize, quantize kernel"
             if (c.fmt in MX + ("hif4",) or c.outer) else "fp4_quantize, computed tensor scale: the single-pass "
-            "kernel when the operand fits one resident grid, else tensor-amax + quantize kernels"),
+            "kernel when the operand fits one resident grid, the wide single pass for BF16 rows while "
+            "a lane holds half its units, else tensor-amax + quantize kernels"),
         "algorithmic_bytes": pl["alg"], "mean_us": round(per_call[dom] * 1e3, 2)}
 
     if args.copy_mib:
