@@ -622,8 +622,8 @@ def main():
         print(json.dumps(t))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: the hot path is single-GPU in this build "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the library quantizes on one device and has no "
+              "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
