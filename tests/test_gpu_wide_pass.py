@@ -136,3 +136,12 @@ def test_strided_large_operand_takes_two_pass():
     assert f32_bits(float(to_host(ts)[0])) == f32_bits(ots)
     assert_bytes_equal(to_host(s), osc, "scales strided")
     assert_bytes_equal(to_host(c), oc, "codes strided")
+
+
+@pytest.mark.parametrize("shape", [(10240, 8192), (11264, 8192)])
+def test_wide_pass_threshold(shape):
+    """Either side of the wide pass's reach with the RHT (5 of 10 units per
+    lane held: wide; 5 of 11: two-pass): the oracle's bytes both times."""
+    x = _bf16(shape, 905, "outlier_cols")
+    note("wide pass threshold %s" % (shape,))
+    quantize_both(x, "nvfp4", "row", "rtne", True, 7, 11)
