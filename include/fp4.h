@@ -180,13 +180,18 @@ typedef struct {
  * resident grid (about 16M elements with the RHT on MI355X), one kernel
  * reads x once: its workgroups exchange partial maxima through 16-byte
  * records in the workspace, tagged per call so that earlier contents are
- * never taken for this call's.  Otherwise, when ws_bytes is below the
- * returned size but at least 4096 (1024 floats), or when the stream is
- * being captured into a HIP graph (a replayed launch would carry the tag it
- * was captured with), a tensor-maximum pass precedes the quantize pass.  Both give the same bytes.  A workgroup that
- * waits longer than FP4_AMAX_WAIT_US microseconds (environment, default
- * 500) for the others computes what it misses from x itself, so a call
- * whose workgroups are not all resident at once still finishes. */
+ * never taken for this call's.  A larger BF16 row operand whose rows are
+ * back to back (ld == cols), up to about 84M elements with the RHT, also
+ * takes one kernel with the same exchange: it holds part of x in
+ * registers and LDS and reads only the rest a second time.  Otherwise, when
+ * ws_bytes is below the returned size but at least 4096 (1024 floats), or
+ * when the stream is being captured into a HIP graph (a replayed launch
+ * would carry the tag it was captured with), a tensor-maximum pass precedes
+ * the quantize pass.  All give the same bytes.  A workgroup that waits
+ * longer than FP4_AMAX_WAIT_US microseconds (environment; by default 10 plus
+ * the time to read x at 2.5 TB/s) for the others computes what it misses
+ * from x itself, so a call whose workgroups are not all resident at once
+ * still finishes. */
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
 
 /* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
