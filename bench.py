@@ -22,8 +22,8 @@ dominant call: its algorithmic bytes (input + codes + scale bytes + 4-byte
 tensor scale) over its mean duration, against the 8 TB/s HBM peak.
 `cpu_baseline` times the scalar oracle on the host on a bounded sample of
 the same workload.  Beside the per-call fractions of the 8 TB/s peak
-(single-read algorithmic bytes, bytes as moved with the tensor-amax pass's
-second read, counter-measured bytes) the line carries the rate of a plain
+(single-read algorithmic bytes, bytes as moved with the input counted as
+often as the chosen path reads it, counter-measured bytes) the line carries the rate of a plain
 device copy (`copy_ceiling_gbs`, the practical ceiling) and, for the
 workloads with a fused RHT, the plain / fused / unfused quantize times of
 the first operand (the ratio the shrinkage-bias page reports in
@@ -102,12 +102,18 @@ def op_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
     return algorithmic_bytes(rows, cols, c.fmt, in_bytes, c.outer, 2 if c.axis == "both" else 1)
 
 
-def moved_bytes(c, rows: int, cols: int, in_bytes: int) -> int:
-    """Bytes the chosen algorithm moves: the algorithmic bytes plus, for a
-    quantize call with a computed tensor scale (two-level formats without
-    outer scales), the tensor-amax pass's second read of the input."""
+def moved_bytes(c, rows: int, cols: int, in_bytes: int, reads=None) -> int:
+    """Bytes the chosen algorithm moves: the algorithmic bytes with the input
+    counted as often as the path reads it.  `reads` = the library's own
+    account of the input bytes a single-axis quantize call reads (once for
+    the single pass, in between for the wide single pass, twice after a
+    tensor-amax pass); a dual call with a computed tensor scale always takes
+    its amax pass."""
+    alg = op_bytes(c, rows, cols, in_bytes)
+    if reads is not None:
+        return alg + reads - rows * cols * in_bytes
     extra = (c.op == "quantize" and c.fmt not in MX + ("hif4",) and not c.outer)
-    return op_bytes(c, rows, cols, in_bytes) + (rows * cols * in_bytes if extra else 0)
+    return alg + (rows * cols * in_bytes if extra else 0)
 
 
 def traffic_for(workload: str, call_index: int):
@@ -666,10 +672,12 @@ def main():
                          torch.empty(ss, dtype=torch.uint8, device=dev),
                          torch.empty(ts_shape, dtype=torch.float32, device=dev)))
         nws = (fp4.workspace_bytes_dual if dual else fp4.workspace_bytes)(rows, cols, p)
+        reads = (fp4.input_bytes(rows, cols, x.stride(0), x.dtype, p, nws)
+                 if call.op == "quantize" and not dual else None)
         pl = dict(call=call, x=x, outs=outs,
                   ws=torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None,
                   alg=op_bytes(call, rows, cols, x.element_size()),
-                  moved=moved_bytes(call, rows, cols, x.element_size()),
+                  moved=moved_bytes(call, rows, cols, x.element_size(), reads),
                   in_bytes=x.numel() * x.element_size())
         if call.op == "dequantize":   # this call's codes, made once outside the timed region
             codes, scales, ts = outs[0]

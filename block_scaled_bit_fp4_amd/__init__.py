@@ -64,7 +64,7 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_NULL", -2: "FP4_ERR_FORMAT", -3: "FP4_ERR_SH
 # every symbol include/fp4.h declares
 EXPORTS = ("fp4_workspace_bytes", "fp4_quantize", "fp4_dequantize", "fp4_rht",
            "fp4_rht_signs", "fp4_status_str", "fp4_workspace_bytes_dual", "fp4_quantize_dual",
-           "fp4_gemm_mx", "fp4_quantize_noalloc")
+           "fp4_gemm_mx", "fp4_quantize_noalloc", "fp4_quantize_input_bytes")
 
 
 class FP4Error(RuntimeError):
@@ -105,6 +105,9 @@ def load():
         L.fp4_quantize.restype = i32
         L.fp4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp]
         L.fp4_quantize_noalloc.restype = i32
+        L.fp4_quantize_input_bytes.argtypes = [i32, i64, i64, i64, P, sz,
+                                               ctypes.POINTER(ctypes.c_int64)]
+        L.fp4_quantize_input_bytes.restype = i32
         L.fp4_workspace_bytes_dual.argtypes = [i64, i64, P]
         L.fp4_workspace_bytes_dual.restype = sz
         L.fp4_quantize_dual.argtypes = [vp, i32, i64, i64, i64, P, vp, vp, vp, vp, vp, vp, vp,
@@ -262,6 +265,21 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     if st != FP4_OK:
         raise FP4Error(st, "fp4_quantize")
     return codes, scales, ts
+
+
+def input_bytes(rows: int, cols: int, ld: int, dtype: torch.dtype, params: Params,
+                ws_bytes: int) -> int:
+    """Bytes of x that fp4_quantize reads with these arguments on the current
+    device, outside graph capture (once, or twice with a tensor-maximum pass,
+    or in between for the wide single pass); no launch."""
+    if dtype not in DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    out = ctypes.c_int64(0)
+    st = load().fp4_quantize_input_bytes(DTYPES[dtype], rows, cols, ld, ctypes.byref(params),
+                                         ws_bytes, ctypes.byref(out))
+    if st != FP4_OK:
+        raise FP4Error(st, "fp4_quantize_input_bytes")
+    return int(out.value)
 
 
 def quantize_noalloc(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row",

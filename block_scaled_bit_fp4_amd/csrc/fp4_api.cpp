@@ -254,6 +254,36 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
   return finish(fp4_launch_quantize(q, s), s);
 }
 
+fp4_status fp4_quantize_input_bytes(int32_t in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                    const fp4_params* p, size_t ws_bytes, int64_t* bytes) {
+  if (!bytes) return FP4_ERR_NULL;
+  fp4_status st = check_params(p);
+  if (st != FP4_OK) return st;
+  if (in_dtype != FP4_BF16 && in_dtype != FP4_F32) return FP4_ERR_DTYPE;
+  if ((st = check_shape(p, rows, cols, ld)) != FP4_OK) return st;
+  if (needs_workspace(p) && ws_bytes < sizeof(float) * (size_t)kAmaxPartials)
+    return FP4_ERR_WORKSPACE;
+  *bytes = 0;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  int64_t elems = 0;
+  QuantLaunch q{};
+  q.in_dtype = in_dtype;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld = ld;
+  q.format = p->format;
+  q.axis = p->axis;
+  q.sr = p->rounding == FP4_SR;
+  q.rht = p->rht;
+  q.ts_mode = two_level(p) ? p->ts_mode : FP4_TS_COMPUTE;
+  q.ws_bytes = ws_bytes;
+  q.call_tag = 1;  // as a call outside graph capture
+  q.plan_reads = &elems;
+  if (fp4_launch_quantize(q, nullptr) != hipSuccess) return FP4_ERR_DEVICE;
+  *bytes = elems * (int64_t)elem_size(in_dtype);
+  return FP4_OK;
+}
+
 fp4_status fp4_quantize_noalloc(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
                                 int64_t ld, const fp4_params* p, uint8_t* codes,
                                 uint8_t* scales, float* tensor_scale, void* stream) {

@@ -30,6 +30,7 @@ struct QuantLaunch {
   size_t ws_bytes;
   uint64_t call_tag;  // unique per call (single-pass exchange); 0: two-pass only
   uint32_t wait_us;   // single-pass: workgroup 0's wait before it computes what is missing
+  int64_t* plan_reads;  // non-null: launch nothing, store the input elements the path reads
 };
 
 // Row-axis and column-axis quantization of one BF16 x in one pass

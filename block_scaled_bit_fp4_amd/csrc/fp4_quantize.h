@@ -1795,6 +1795,10 @@ bool try_single_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   const int64_t grid = (units + (int64_t)NT * NU - 1) / ((int64_t)NT * NU);
   const int64_t cap = resident_wgs_nt(reinterpret_cast<const void*>(kernel), NT, lds);
   if (grid < 1 || grid > kAmaxPartials || grid > cap) return false;
+  if (q.plan_reads) {  // every element read once
+    *q.plan_reads = q.rows * q.cols;
+    return true;
+  }
   a.W = q.cols;
   a.n_major = q.rows;
   a.M = q.cols / U;
@@ -1835,6 +1839,11 @@ bool try_wide_pass(const QuantLaunch& q, QuantArgs a, hipStream_t s) {
   // workgroups per compute unit, stream it faster (measured on an
   // 8192 x 28672 operand, 28 units per lane: 190 us wide, 173 us two-pass).
   if (nu > 2 * (NR + NL)) return false;
+  if (q.plan_reads) {  // units past the first NR + NL of every lane are read twice
+    const int64_t held = units < stride * (NR + NL) ? units : stride * (NR + NL);
+    *q.plan_reads = (2 * units - held) * U;
+    return true;
+  }
   a.W = q.cols;
   a.n_major = q.rows;
   a.M = q.cols / U;
@@ -1871,6 +1880,10 @@ hipError_t launch_quantize_t(const QuantLaunch& q, hipStream_t s) {
          try_single_pass<FMT, SR, RHT, T, 4, 256>(q, a, s) ||
          (FP4_WIDE_PASS && try_wide_pass<FMT, SR, RHT, T>(q, a, s))))
       return hipGetLastError();
+  }
+  if (q.plan_reads) {  // a tensor-amax pass reads x once more
+    *q.plan_reads = (has_tensor_scale(FMT) && TSM == kTsCompute ? 2 : 1) * q.rows * q.cols;
+    return hipSuccess;
   }
   if constexpr (has_tensor_scale(FMT) && TSM == kTsCompute) launch_amax<RHT, T>(q, s);
   if (q.axis == 0) {

@@ -209,6 +209,22 @@ fp4_status fp4_quantize(const void* x, int32_t in_dtype, int64_t rows, int64_t c
                         float* tensor_scale, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* Host-side query, no launch: the bytes of x that fp4_quantize with these
+ * arguments reads on the current device, outside graph capture, stored in
+ * *bytes.  A computed tensor scale needs the maximum of the whole operand
+ * before any block is coded (per-tensor scaling: "Le Architetture
+ * Normalizzate ...", "Enunciato del Problema"): the single pass reads x
+ * once (rows * cols elements), the wide single pass
+ * reads the units it does not hold twice, and the two-pass path (a
+ * tensor-maximum pass, then the quantize pass) reads x twice.  Every other
+ * mode reads x once.  Same argument checks as fp4_quantize apart from the
+ * pointers; FP4_ERR_NULL if bytes is NULL, FP4_ERR_WORKSPACE if a computed
+ * tensor scale's ws_bytes is below 4096.  Without a device (or when the
+ * occupancy query fails) it reports the two-pass path, which fp4_quantize
+ * then takes too. */
+fp4_status fp4_quantize_input_bytes(int32_t in_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                    const fp4_params* p, size_t ws_bytes, int64_t* bytes);
+
 /* Allocation-free fp4_quantize, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, checks and results as fp4_quantize

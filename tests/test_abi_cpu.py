@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_scaled_bit_fp4_amd as fp4
 import oracle
@@ -199,3 +200,31 @@ def test_noalloc_validation(lib):
     for shape in ((64, 64), (16384, 14336)):
         for fmt in ("nvfp4", "ufp4", "e2m1_cap2"):
             assert fp4.workspace_bytes(*shape, P(fmt)) <= 16640
+
+
+def test_input_bytes_query(lib):
+    """fp4_quantize_input_bytes: host checks, and the modes that read x once
+    on any device (no tensor maximum to find first)."""
+    P = fp4.make_params
+    out = ctypes.c_int64(-1)
+    q = lambda p, dt=0, rows=64, cols=64, ld=64, nws=4096, o=ctypes.byref(out): \
+        lib.fp4_quantize_input_bytes(dt, rows, cols, ld,
+                                     ctypes.byref(p) if p is not None else None, nws, o)
+    assert q(None) == -1
+    assert q(P("nvfp4"), o=None) == -1
+    bad = P("nvfp4"); bad.block = 32
+    assert q(bad) == -2
+    assert q(P("nvfp4"), dt=4) == -5
+    assert q(P("nvfp4"), cols=24, ld=24) == -3
+    assert q(P("nvfp4"), ld=32) == -3
+    assert q(P("nvfp4"), nws=16) == -6
+    assert q(P("nvfp4"), rows=0) == 0 and out.value == 0
+    # a workspace too small for the slot exchange: amax pass + quantize pass
+    assert q(P("nvfp4", rht=True)) == 0 and out.value == 2 * 64 * 64 * 2
+    assert q(P("nvfp4", axis="col"), dt=1) == 0 and out.value == 2 * 64 * 64 * 4
+    for p in (P("mxfp4"), P("mxfp4_oas"), P("hif4"), P("nvfp4", ts_given=True)):
+        cols = 128
+        assert q(p, cols=cols, ld=cols, nws=0) == 0 and out.value == 64 * cols * 2, p.format
+    assert q(P("nvfp4", outer=True), cols=128, ld=128, nws=0) == 0 and out.value == 64 * 128 * 2
+    assert fp4.input_bytes(64, 128, 128, torch.bfloat16, P("mxfp4_mbs", outer=True), 0) == \
+        64 * 128 * 2

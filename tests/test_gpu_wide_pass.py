@@ -145,3 +145,30 @@ def test_wide_pass_threshold(shape):
     x = _bf16(shape, 905, "outlier_cols")
     note("wide pass threshold %s" % (shape,))
     quantize_both(x, "nvfp4", "row", "rtne", True, 7, 11)
+
+
+def test_input_bytes_follow_the_path():
+    """fp4_quantize_input_bytes reports the input bytes of the path the call
+    takes: once for the single pass, in between for the wide pass (the units
+    it does not hold are read twice), twice for the two-pass path."""
+    P = fp4.make_params
+    p = P("nvfp4", "row", "rtne", True)
+    ws = fp4.workspace_bytes(1, 1, p)
+    bf = torch.bfloat16
+    n = 4096 * 4096 * 2
+    assert fp4.input_bytes(4096, 4096, 4096, bf, p, ws) == n            # single pass
+    assert fp4.input_bytes(4096, 4096, 4096, bf, p, TWO_PASS_WS) == 2 * n
+    # FP32 rows take the single pass while they fit one resident grid
+    assert fp4.input_bytes(4096, 4096, 4096, torch.float32, p, ws) in (2 * n, 4 * n)
+    for rows in (8192, 10240):                                         # wide
+        n = rows * 8192 * 2
+        r = fp4.input_bytes(rows, 8192, 8192, bf, p, ws)
+        assert n < r < 2 * n and (r - n) % 64 == 0, (rows, r)
+    n = 11264 * 8192 * 2
+    assert fp4.input_bytes(11264, 8192, 8192, bf, p, ws) == 2 * n        # past the wide reach
+    n = 8192 * 8192 * 2
+    assert fp4.input_bytes(8192, 8192, 8320, bf, p, ws) == 2 * n         # strided: two-pass
+    assert fp4.input_bytes(8192, 8192, 8192, bf, P("nvfp4", "col", "rtne", True), ws) == 2 * n
+    assert fp4.input_bytes(8192, 8192, 8192, bf, P("mxfp4", "row", "rtne", True), 0) == n
+    assert fp4.input_bytes(8192, 8192, 8192, bf, P("nvfp4", outer=True), 0) == n
+    assert fp4.input_bytes(8192, 8192, 8192, bf, P("nvfp4", ts_given=True), 0) == n
