@@ -12,6 +12,10 @@
 
 using namespace fp4dev;
 
+#ifndef FP4_DEQ_WAVE_ROWS
+#define FP4_DEQ_WAVE_ROWS 1
+#endif
+
 namespace {
 
 // Group g (16 elements) of A-row ra: row axis reads 16 contiguous elements,
@@ -229,7 +233,37 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(T* __restrict__ ou
   const float s_t = (!has_tensor_scale(FMT) || OUTER) ? 0.0f : a.ts[0];
   Walk w;
   w.init((int64_t)blockIdx.x * kThreads + threadIdx.x, a.M);
-  if constexpr (AXIS == 0 && sizeof(T) == 2) {
+  if constexpr (AXIS == 2) {
+    // BF16 rows with a multiple of 64 blocks per A-row: the 64 lanes of a
+    // wave decode 64 consecutive blocks of one A-row (2 KB of output), then
+    // trade halves across lanes (ds_bpermute, no LDS memory) so that each of
+    // the two 16-byte store instructions writes one contiguous 1 KB: lane l
+    // stores half l % 2 of block l / 2, then of block 32 + l / 2.  Every lane
+    // of a wave takes the same A-row, so a wave is active or done as a whole.
+    static_assert(B == 16 && sizeof(T) == 2, "16-element blocks, BF16 rows");
+    const int l = threadIdx.x & 63;
+    const int src1 = 4 * (l >> 1), src2 = 4 * (32 + (l >> 1));
+    const bool odd = l & 1;
+    while (w.major < a.n_major) {
+      uint32_t v[8];
+      dequant_block<FMT, OUTER, INV, T>(a, s_t, load_block<FMT, OUTER>(a, w.major, w.minor), v);
+      uint32_t p[4], q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)v[k]);
+        const uint32_t b1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)v[4 + k]);
+        const uint32_t a2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src2, (int)v[k]);
+        const uint32_t b2 = (uint32_t)__builtin_amdgcn_ds_bpermute(src2, (int)v[4 + k]);
+        p[k] = odd ? b1 : a1;
+        q[k] = odd ? b2 : a2;
+      }
+      // the wave's first block is this lane's block minus l
+      uint32_t* to = reinterpret_cast<uint32_t*>(out + w.major * a.ld_out + (w.minor - l) * B);
+      store16<false>(to + 4 * l, p[0], p[1], p[2], p[3]);
+      store16<false>(to + 256 + 4 * l, q[0], q[1], q[2], q[3]);
+      w.advance(a.sq, a.sr, a.M);
+    }
+  } else if constexpr (AXIS == 0 && sizeof(T) == 2) {
     // BF16 rows: 2 bytes per value, a lane's 16-value group is two 16-byte
     // stores (staging measured slower here)
     // (loading the next block ahead measured slower here)
@@ -468,6 +502,15 @@ hipError_t launch_dequant_t(const DequantLaunch& q, hipStream_t s) {
     const WalkPlan wp = plan_walk(nmaj, M, kMaxGrid);
     DequantArgs a{q.codes, q.scales, q.tensor_scale, q.ld_out, W, nmaj, M, wp.sq, wp.sr,
                   q.signs, 0, 0};
+    if constexpr (B == 16 && sizeof(T) == 2) {
+      // whole waves on one A-row: 64 | blocks per row (the walk's stride is
+      // a multiple of 64 lanes, so every wave starts on a multiple of 64)
+      if (FP4_DEQ_WAVE_ROWS && M % 64 == 0) {
+        hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, 2, T>), dim3(wp.grid),
+                           dim3(kThreads), 0, s, out, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((dequantize_kernel<FMT, OUTER, INV, 0, T>), dim3(wp.grid),
                        dim3(kThreads), 0, s, out, a);
     return hipGetLastError();
