@@ -88,6 +88,39 @@ def test_outer_scale_parity(fmt, axis, rounding, rht, dtype):
                                "outer dequant inv=%s %s" % (inv, shape))
 
 
+# Row dequantize to BF16 with 64 or more 16-element blocks per row (the
+# path whose waves trade block halves so that each store instruction writes
+# one contiguous 1 KB): 64 and 128 blocks per row, every 16-element format,
+# outer scales, the inverse RHT on and off, and an output pitch above the
+# width.
+WAVE_ROW_CASES = list(itertools.product(["nvfp4", "ufp4", "e2m1_cap2", "mxfp4_oas16",
+                                         "mxfp4_mbs"], [False, True]))
+
+
+@pytest.mark.parametrize("fmt,rht", WAVE_ROW_CASES,
+                         ids=["%s-rht%d" % (f, r) for f, r in WAVE_ROW_CASES])
+def test_dequant_bf16_whole_wave_rows(fmt, rht):
+    for i, (shape, pitch) in enumerate([((64, 1024), 1024), ((40, 2048), 2048),
+                                        ((24, 1024), 1152)]):
+        kind = KINDS[(i + len(fmt)) % len(KINDS)]
+        x = _input(kind, shape, 300 + i, "bf16")
+        rows, cols = shape
+        outer = fmt == "mxfp4_mbs" or (fmt != "mxfp4_oas16" and i == 1)
+        note("wave rows %s rht=%s %s outer=%s %s" % (fmt, rht, shape, outer, kind))
+        c, s, ts, (oc, osc, ots) = quantize_both(x, fmt, "row", "rtne", rht, 6, 1,
+                                                 outer=outer)
+        for inv in ([False, True] if rht else [False]):
+            full = torch.zeros((rows, pitch), dtype=torch.bfloat16, device=DEV)
+            out = full[:, :cols]
+            fp4.dequantize(c, s, ts, rows, cols, fmt, "row", rht, 6, inv, torch.bfloat16,
+                           out=out)
+            torch.cuda.synchronize()
+            want = oracle.dequantize(oc, osc, ots, rows, cols, fmt, "row", rht, 6, inv, "bf16")
+            assert_bytes_equal(to_host(out), want, "wave rows inv=%s %s" % (inv, shape))
+            if pitch > cols:  # the padding is left alone
+                assert not to_host(full[:, cols:]).any()
+
+
 def test_outer_scale_rejects_ragged_width():
     x = to_device(np.zeros((64, 144), dtype=np.float32))
     with pytest.raises(fp4.FP4Error):
