@@ -159,7 +159,8 @@ typedef int32_t fp4_status;
 #define FP4_TS_OUTER128 2 /* double block (MBS: macro scale): one FP32 per 128 elements */
 
 typedef struct {
-  int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS */
+  int32_t format;   /* FP4_NVFP4 / _MXFP4 / _UFP4 / _MXFP4_OAS / _E2M1_CAP2 / _MXFP4_MBS /
+                       _MXFP4_OAS16 / _HIF4 */
   int32_t block;    /* 16 for NVFP4, UFP4, E2M1_CAP2, MXFP4_MBS, MXFP4_OAS16; 32 for MXFP4,
                        MXFP4_OAS; 64 for HIF4 */
   int32_t axis;     /* FP4_AXIS_ROW / FP4_AXIS_COL */
@@ -196,8 +197,9 @@ size_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_params* p);
 
 /* Quantize x (rows x cols, leading dimension ld, in_dtype) into codes and
  * scales (layouts above).  tensor_scale is written (COMPUTE, OUTER128) or
- * read (GIVEN) for the two-level formats (NVFP4, UFP4, E2M1_CAP2) and may
- * be NULL for the MX formats.
+ * read (GIVEN) for the two-level formats (NVFP4, UFP4, E2M1_CAP2; MXFP4_MBS
+ * writes its macro scales there, as OUTER128) and may be NULL for the MX
+ * formats and HiF4.
  * workspace holds ws_bytes bytes: at least 4096 for a computed tensor scale,
  * fp4_workspace_bytes() for the single-pass kernel.  Requirements: block
  * matches the format; W divisible by the block (and by 16 when rht, by 128
@@ -298,7 +300,7 @@ fp4_status fp4_rht(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, 
  * Experimentaux").  An RHT applied to both operands along K cancels in the
  * product (the 16-point transform is orthogonal).  Each product of two
  * codes is exact; accumulation is in binary32 inside gfx950's scaled
- * matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4), in its order, so
+ * matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4), in its order, so
  * results match an exact reference within a binary32 accumulation bound,
  * not bit for bit.  C is M x N, FP32 or BF16 (round to nearest even), row
  * leading dimension ldc >= N.  M, N and K must be multiples of 128, K > 0,
