@@ -31,6 +31,10 @@
 #include "fp4_launch.h"
 #include "fp4_tiles.h"
 
+#ifndef FP4_UNIFORM_PACK
+#define FP4_UNIFORM_PACK 1
+#endif
+
 using namespace fp4dev;
 
 namespace {
@@ -255,7 +259,30 @@ __device__ __forceinline__ uint32_t encode8_fast(const float* v_in, const uint32
     for (int l = 0; l < 8; ++l) vc[l] = fminf(fmaxf(v_in[l], -2.0f), 2.0f);
     v = vc;
   }
-  if constexpr (FMT == kUFP4 && !SR) {
+  if constexpr (FMT == kUFP4 && !SR && FP4_UNIFORM_PACK) {
+    // Uniform grid, round to nearest even: k = rint(min(|v|, 7)), an exact
+    // integer 0..7, written into a byte by the float -> u8 pack convert
+    // (exact for integers): element 2j into byte j of lo, element 2j + 1
+    // into byte j of hi, so that lo | hi << 4 holds element l in nibble l.
+    // Signs: byte selectors 9 and 11 of the byte permute give 0xFF where bit
+    // 31 of its second or first source is set; the even elements' sign
+    // bytes masked to bit 3 of each byte, the odd ones' to bit 7.
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo = __builtin_amdgcn_cvt_pk_u8_f32(rintf(fminf(fabsf(v[2 * j]), 7.0f)), j, lo);
+      hi = __builtin_amdgcn_cvt_pk_u8_f32(rintf(fminf(fabsf(v[2 * j + 1]), 7.0f)), j, hi);
+    }
+    const uint32_t b[8] = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                           __float_as_uint(v[3]), __float_as_uint(v[4]), __float_as_uint(v[5]),
+                           __float_as_uint(v[6]), __float_as_uint(v[7])};
+    // bytes 0, 1 = signs of (b[p], b[p + 2]); bytes 2, 3 = signs of (b[p + 4], b[p + 6])
+    const uint32_t se0 = __builtin_amdgcn_perm(b[2], b[0], 0x0C0C0B09u);
+    const uint32_t se1 = __builtin_amdgcn_perm(b[6], b[4], 0x0B090C0Cu);
+    const uint32_t so0 = __builtin_amdgcn_perm(b[3], b[1], 0x0C0C0B09u);
+    const uint32_t so1 = __builtin_amdgcn_perm(b[7], b[5], 0x0B090C0Cu);
+    word = (lo | (hi << 4)) | ((se0 | se1) & 0x08080808u) | ((so0 | so1) & 0x80808080u);
+  } else if constexpr (FMT == kUFP4 && !SR) {
     // Uniform grid, round to nearest even: adding 2^23 to min(m, 7) rounds
     // it to an integer (binary32 addition, ties to even) held in the low
     // mantissa bits; the sign bit of v becomes bit 3.
